@@ -1,0 +1,79 @@
+"""Top-k KV-block selection for sparse verification (float32, order pinned).
+
+The sparse-verification page ("Methodology", attention sparsity) keeps only
+the top-k key/value blocks per query, chosen by a cheap relevance score.
+Reading of the score: the mean-pooled key of each block, dotted with the
+query (signed, unscaled).  Candidates are the blocks holding committed
+context, n < ceil(ctx_b / bs); tree slots are never candidates (they are
+always attended).  Selection is per query (b, node, query head).
+
+Because the indices must match exactly, the float32 arithmetic is fixed:
+
+* mean  = (sequential float32 sum over the block's valid tokens, in
+          position order) / n_valid, one IEEE division;
+* score = products q[d] * mean[d] in float32, then a halving tree:
+          add element d + D/2 into d, then d + D/4, ..., then d + 1;
+* order = score descending, then block index ascending; keep the first k,
+          emit them in ascending block order, pad with -1.
+"""
+import numpy as np
+
+from .codec import decode_f32
+
+
+def block_means(k_pages, block_table, ctx_lens, bs, dtype):
+    """float32 [B, nmax, Hkv, D]; entries past a sequence's context blocks are NaN."""
+    B = len(ctx_lens)
+    Hkv, D = k_pages.shape[1], k_pages.shape[3]
+    nb = [(int(c) + bs - 1) // bs for c in ctx_lens]
+    nmax = max(nb + [0])
+    out = np.full((B, nmax, Hkv, D), np.nan, dtype=np.float32)
+    for b in range(B):
+        ctx = int(ctx_lens[b])
+        for n in range(nb[b]):
+            blk = int(block_table[b, n])
+            valid = min(bs, ctx - n * bs)
+            s = np.zeros((Hkv, D), dtype=np.float32)
+            for t in range(valid):
+                s = s + decode_f32(k_pages[blk, :, t, :], dtype)
+            out[b, n] = s / np.float32(valid)
+    return out
+
+
+def block_scores(qv, means):
+    """qv: float32 [D]; means: float32 [n, D] -> float32 [n] via the halving tree."""
+    p = np.asarray(qv, dtype=np.float32)[None, :] * np.asarray(means, dtype=np.float32)
+    w = p.shape[1] // 2
+    while w >= 1:
+        p = p[:, :w] + p[:, w:2 * w]
+        w //= 2
+    return p[:, 0]
+
+
+def select(scores, k):
+    """Indices of the k best (score desc, index asc), ascending, padded with -1."""
+    n = len(scores)
+    order = np.lexsort((np.arange(n), -scores))
+    keep = np.sort(order[:k])
+    out = np.full(k, -1, dtype=np.int32)
+    out[:len(keep)] = keep
+    return out
+
+
+def topk_blocks(q, k_pages, block_table, ctx_lens, bs, k, dtype, means=None):
+    """sel [B, T, Hq, k] int32."""
+    B, T, Hq, D = q.shape
+    Hkv = k_pages.shape[1]
+    G = Hq // Hkv
+    if means is None:
+        means = block_means(k_pages, block_table, ctx_lens, bs, dtype)
+    sel = np.full((B, T, Hq, k), -1, dtype=np.int32)
+    for b in range(B):
+        nb = (int(ctx_lens[b]) + bs - 1) // bs
+        for i in range(T):
+            for h in range(Hq):
+                if nb == 0:
+                    continue
+                sc = block_scores(decode_f32(q[b, i, h], dtype), means[b, :nb, h // G])
+                sel[b, i, h] = select(sc, k)
+    return sel

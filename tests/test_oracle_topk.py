@@ -1,0 +1,110 @@
+"""Pins for the block-selection oracle: integer-valued inputs where every
+float32 operation is exact (so the score must equal the exact dot product),
+error bounds against float64, a full sort by brute force on tiny inputs,
+ties, partial blocks and planted high-norm blocks."""
+import numpy as np
+import pytest
+
+import oracle
+from synth.inputs import f32_to_bf16_bits
+from tests.helpers import paged_from_dense
+
+
+def _int_case(rng, B=2, Hkv=2, D=16, ctx=(20, 13), bs=4, T=3, Hq=4):
+    """Small-integer keys and queries: every product and partial sum is an
+    exact float32 integer, and block sums are multiples of the valid count."""
+    n = max(ctx) + T
+    Kd = rng.integers(-3, 4, size=(B, Hkv, n, D)).astype(np.float32)
+    for b in range(B):
+        for blk in range((ctx[b] + bs - 1) // bs):
+            lo, hi = blk * bs, min(ctx[b], (blk + 1) * bs)
+            # make each block's sum divisible by its valid count: mean is exact
+            tot = Kd[b, :, lo:hi, :].sum(axis=1)
+            Kd[b, :, hi - 1, :] -= np.mod(tot, hi - lo)
+    Vd = np.zeros_like(Kd)
+    q = rng.integers(-2, 3, size=(B, T, Hq, D)).astype(np.float32)
+    kp, vp, table = paged_from_dense(Kd, Vd, bs, rng)
+    return q, kp, table, np.array(ctx, np.int32), Kd
+
+
+def test_exact_integer_scores_and_brute_force_sort():
+    """Check (e): selection equals a brute-force full sort, with scores equal
+    to the exact integer dot product of the query and the block-mean key."""
+    rng = np.random.default_rng(0)
+    bs = 4
+    q, kp, table, ctx, Kd = _int_case(rng, bs=bs)
+    means = oracle.block_means(kp, table, ctx, bs, "f32")
+    for k in (1, 3, 5, 8, 9):
+        sel = oracle.topk_blocks(q, kp, table, ctx, bs, k, "f32")
+        for b in range(2):
+            nb = (ctx[b] + bs - 1) // bs
+            for i in range(3):
+                for h in range(4):
+                    g = h // 2
+                    exact = []
+                    for n in range(nb):
+                        lo, hi = n * bs, min(ctx[b], (n + 1) * bs)
+                        mean = [sum(int(Kd[b, g, t, d]) for t in range(lo, hi)) // (hi - lo)
+                                for d in range(16)]
+                        assert np.array_equal(means[b, n, g], np.array(mean, np.float32))
+                        exact.append((-sum(int(q[b, i, h, d]) * mean[d] for d in range(16)), n))
+                    best = sorted(n for _, n in sorted(exact)[:k])
+                    want = best + [-1] * (k - len(best))
+                    assert list(sel[b, i, h]) == want
+
+
+def test_scores_within_float32_error_bound():
+    rng = np.random.default_rng(1)
+    D = 128
+    qv = rng.standard_normal(D).astype(np.float32)
+    m = rng.standard_normal((50, D)).astype(np.float32)
+    s = oracle.block_scores(qv, m)
+    exact = m.astype(np.float64) @ qv.astype(np.float64)
+    bound = (np.abs(m.astype(np.float64)) @ np.abs(qv.astype(np.float64))) * 8 * 2.0 ** -24
+    assert np.all(np.abs(s - exact) <= bound)
+
+
+def test_block_mean_is_sequential_float32_sum():
+    """The mean of a 64-token bf16 block equals the float64 mean within the
+    float32 accumulation bound, and a partial block divides by its valid count."""
+    rng = np.random.default_rng(2)
+    bs, D = 64, 128
+    Kf = rng.standard_normal((1, 1, 100, D)).astype(np.float32)
+    Kb = f32_to_bf16_bits(Kf)
+    kp, _, table = paged_from_dense(Kb, np.zeros_like(Kb), bs)
+    means = oracle.block_means(kp, table, np.array([100], np.int32), bs, "bf16")
+    Kx = (Kb.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    for n, (lo, hi) in enumerate([(0, 64), (64, 100)]):
+        ref = Kx[0, 0, lo:hi].mean(axis=0)
+        bound = np.abs(Kx[0, 0, lo:hi]).sum(axis=0) / (hi - lo) * (hi - lo + 1) * 2.0 ** -24
+        assert np.all(np.abs(means[0, n, 0] - ref) <= bound)
+
+
+def test_ties_go_to_lower_block_and_padding():
+    """Duplicated blocks give exactly equal scores; the lower index wins."""
+    rng = np.random.default_rng(3)
+    bs, D = 2, 8
+    base = rng.standard_normal((1, 1, 2, D)).astype(np.float32)
+    Kd = np.concatenate([base] * 5, axis=2)           # 5 identical blocks
+    kp, _, table = paged_from_dense(Kd, np.zeros_like(Kd), bs)
+    q = rng.standard_normal((1, 1, 1, D)).astype(np.float32)
+    sel = oracle.topk_blocks(q, kp, table, np.array([10], np.int32), bs, 3, "f32")
+    assert list(sel[0, 0, 0]) == [0, 1, 2]
+    sel = oracle.topk_blocks(q, kp, table, np.array([10], np.int32), bs, 7, "f32")
+    assert list(sel[0, 0, 0]) == [0, 1, 2, 3, 4, -1, -1]
+    sel = oracle.topk_blocks(q, kp, table, np.array([0], np.int32), bs, 2, "f32")
+    assert list(sel[0, 0, 0]) == [-1, -1]
+
+
+def test_planted_aligned_blocks_are_selected():
+    rng = np.random.default_rng(4)
+    bs, D, nblk = 16, 32, 20
+    Kd = rng.standard_normal((1, 1, nblk * bs, D)).astype(np.float32)
+    qv = rng.standard_normal(D).astype(np.float32)
+    planted = [3, 11, 17]
+    for n in planted:
+        Kd[0, 0, n * bs:(n + 1) * bs] += 5.0 * qv / np.linalg.norm(qv)
+    kp, _, table = paged_from_dense(Kd, np.zeros_like(Kd), bs, rng)
+    sel = oracle.topk_blocks(qv[None, None, None], kp, table, np.array([nblk * bs], np.int32),
+                             bs, 3, "f32")
+    assert list(sel[0, 0, 0]) == planted
