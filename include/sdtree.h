@@ -1,0 +1,183 @@
+/*
+ * sdtree.h -- tree verification for speculative decoding on MI355X (gfx950).
+ *
+ * The verification pass of speculative decoding (SpecExec page, "Approach":
+ * the whole draft tree is verified in one target pass; EasySpec page, "+tree"
+ * baseline; sparse-verification page, "Methodology") as four calls:
+ *
+ *   sd_tree_verify_attn  every draft-tree node attends to the committed context
+ *                        plus its own ancestors, grouped-query heads, paged KV;
+ *   sd_accept            the acceptance walk (greedy, rejection sampling, or
+ *                        sampling from the target at each node);
+ *   sd_kv_commit         the accepted root path becomes committed context;
+ *   sd_topk_blocks       top-k KV blocks per query for sparse verification.
+ *
+ * Conventions shared by every call
+ *   - Tensor arguments are DEVICE pointers owned by the caller.  The library
+ *     never allocates or frees device memory.  Scratch comes from a caller
+ *     workspace `ws` of at least sd_workspace_bytes(...) bytes, zero-filled
+ *     once by the caller before its first use (the library leaves it reusable).
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = default stream)
+ *     and return an sd_status.  Argument and shape errors are detected on the
+ *     host before anything is launched; then nothing is launched.
+ *   - Data-dependent errors (a bad parent index, a block id out of range, a
+ *     context that does not fit the block table) set a sticky bit in the
+ *     workspace status word and the affected unit is skipped;
+ *     sd_device_status reads (and clears) it.
+ *   - No exceptions, aborts or printing.  One workspace must not be used by two
+ *     calls that may run concurrently.
+ *
+ * Layouts (row-major, innermost last)
+ *   q, out        [B, T, Hq, D]                 element type `dtype`
+ *   k_pages       [num_blocks, Hkv, bs, D]      element type `dtype`
+ *   v_pages       [num_blocks, Hkv, D, bs]      V is stored transposed in each page
+ *   block_table   int32 [B, max_blocks]         logical block -> physical block
+ *   ctx_lens      int32 [B]                     committed context length
+ *   tree_parent   int32 [B or 1, T]             parent[0] = -1, 0 <= parent[i] < i
+ *   tree_token    int32 [B or 1, T]
+ *   Logical position p of sequence b lives in block block_table[b][p / bs] at
+ *   offset p % bs.  Tree node i's K/V must already sit at position ctx_b + i
+ *   (the caller writes it there), so the table must cover ctx_b + T positions.
+ *   Query head h reads KV head h / (Hq / Hkv).
+ */
+#ifndef SDTREE_H
+#define SDTREE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum sd_status {
+  SD_OK = 0,
+  SD_INVALID_ARG = 1,        /* null pointer, bad scalar (k <= 0, temperature < 0, ...) */
+  SD_BAD_SHAPE = 2,          /* inconsistent sizes (Hq % Hkv != 0, T < 1, ...) */
+  SD_BAD_DTYPE = 3,          /* element type code not supported by the call */
+  SD_UNSUPPORTED = 4,        /* valid but outside what the kernels handle (D not 64/128, T > 4096) */
+  SD_CAPACITY = 5,           /* workspace smaller than sd_workspace_bytes() */
+  SD_HIP_ERROR = 6,          /* a HIP runtime call failed */
+  SD_DEVICE_DATA_ERROR = 7   /* returned by sd_device_status when a sticky bit is set */
+} sd_status;
+
+typedef enum sd_dtype { SD_F32 = 0, SD_BF16 = 1 } sd_dtype;
+
+/* Sticky bits of the workspace status word. */
+#define SD_ERR_PARENT     0x1u   /* parent[i] not in [-1, i) (attention) or not in [0, i) (accept) */
+#define SD_ERR_BLOCK      0x2u   /* block_table entry outside [0, num_blocks) */
+#define SD_ERR_CAPACITY   0x4u   /* ctx_b + T exceeds max_blocks * bs, or ctx_b < 0 */
+#define SD_ERR_TOKEN      0x8u   /* tree token outside [0, V) */
+#define SD_ERR_SELECTION  0x10u  /* sel_blocks entry not a context block / not ascending */
+
+typedef struct sd_shape {
+  int32_t B;            /* sequences */
+  int32_t T;            /* tree nodes including the root (node 0) */
+  int32_t Hq;           /* query heads */
+  int32_t Hkv;          /* KV heads; Hq % Hkv == 0 */
+  int32_t D;            /* head dim: 64 or 128 */
+  int32_t bs;           /* tokens per KV block; a multiple of 8 */
+  int32_t max_blocks;   /* columns of block_table */
+  int32_t num_blocks;   /* blocks in k_pages / v_pages */
+  int32_t dtype;        /* sd_dtype of q, k_pages, v_pages, out */
+  int32_t tree_stride;  /* 0: one tree shared by all sequences, T: one tree per sequence */
+  float scale;          /* softmax scale; 0 means 1/sqrt(D) */
+} sd_shape;
+
+typedef struct sd_accept_shape {
+  int32_t B;            /* sequences */
+  int32_t T;            /* tree nodes including the root */
+  int32_t V;            /* vocabulary */
+  int32_t logit_dtype;  /* sd_dtype of target_logits */
+  int32_t tree_stride;  /* 0 or T, as in sd_shape */
+} sd_accept_shape;
+
+enum { SD_CALL_ATTN = 1, SD_CALL_ACCEPT = 2, SD_CALL_TOPK = 3, SD_CALL_COMMIT = 4 };
+
+/*
+ * Tree-masked grouped-query attention over the paged cache.
+ * For every (b, i, h): out = softmax(scale * q . K^T) V over the keys at
+ * positions {p < ctx_b} U {ctx_b + j : j is i or an ancestor of i}
+ * (SpecExec page, "Approach"; EasySpec page, "+tree").
+ *   sel_blocks  NULL for dense attention, else int32 [B, T, Hq, k_sel]: the
+ *               context blocks each query keeps, ascending, -1 padded at the
+ *               end (sparse-verification page, "Methodology": top-k blocks per
+ *               query); tree ancestors are always attended.
+ *   out         written in `dtype`.
+ *   ws          >= sd_workspace_bytes(SD_CALL_ATTN, shape, k_sel).
+ */
+sd_status sd_tree_verify_attn(const sd_shape* shape, const void* q, const void* k_pages,
+                              const void* v_pages, const int32_t* block_table,
+                              const int32_t* ctx_lens, const int32_t* tree_parent,
+                              const int32_t* sel_blocks, int32_t k_sel, void* out, void* ws,
+                              size_t ws_bytes, void* stream);
+
+/*
+ * Acceptance walk from the root (SpecExec page, "Approach" and "Builds on";
+ * EasySpec page, "Approach").  The rule follows the arguments:
+ *   temperature == 0                    greedy: follow the target argmax
+ *                                       (lowest id on ties) while a child
+ *                                       carries it (lowest node index first);
+ *   temperature > 0, draft_probs given  rejection sampling: siblings in
+ *                                       ascending index, child c with token x
+ *                                       accepted when u[c][0]*q(x) < r(x); on
+ *                                       rejection r <- normalise(max(r-q, 0));
+ *   temperature > 0, draft_probs NULL   sample x from softmax(l / temperature)
+ *                                       with u[cur][1]; descend into the child
+ *                                       carrying x, else stop.
+ *   target_logits  [B, T, V] in logit_dtype; draft_probs float32 [B, T, V].
+ *   uniforms       float32 [B, T, 2] in [0, 1); may be NULL when temperature == 0.
+ *   path           int32 [B, T]: accepted nodes from the root, -1 padded.
+ *   path_len       int32 [B]: accepted drafts + 1.   bonus  int32 [B]: next root token.
+ *   ws             >= sd_workspace_bytes(SD_CALL_ACCEPT, shape, 0).
+ */
+sd_status sd_accept(const sd_accept_shape* shape, const void* target_logits,
+                    const float* draft_probs, const int32_t* tree_parent,
+                    const int32_t* tree_token, const float* uniforms, float temperature,
+                    int32_t* path, int32_t* path_len, int32_t* bonus, void* ws, size_t ws_bytes,
+                    void* stream);
+
+/*
+ * Commit the accepted path: for j < path_len[b], position ctx_b + j takes the
+ * K/V of position ctx_b + path[b][j] (every KV head), then ctx_lens[b] +=
+ * path_len[b].  In place; path must be increasing with path[b][0] == 0 (as
+ * sd_accept produces), which makes the in-place copy safe.  k_pages, v_pages
+ * and ctx_lens are modified.  A sequence whose path or table fails validation
+ * is left untouched and a sticky bit is set in ws (>= sd_workspace_bytes(
+ * SD_CALL_COMMIT, shape, 0) bytes; only its status word is used).
+ *   path      int32 [B, T] as produced by sd_accept; path_len int32 [B].
+ */
+sd_status sd_kv_commit(const sd_shape* shape, void* k_pages, void* v_pages,
+                       const int32_t* block_table, int32_t* ctx_lens, const int32_t* path,
+                       const int32_t* path_len, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Top-k context blocks per query (sparse-verification page, "Methodology":
+ * keep the top-k key/value blocks per query by a cheap relevance score).
+ * Score of block n for query (b, i, h) = q . mean of the block's valid keys,
+ * computed in float32 in a fixed order (sequential token sum, one division,
+ * products, halving-tree sum over D).  Candidates: n < ceil(ctx_b / bs).
+ * Keeps the k best (score descending, lower index first on ties).
+ *   sel_blocks  int32 [B, T, Hq, k]: ascending, -1 padded.
+ *   ws          >= sd_workspace_bytes(SD_CALL_TOPK, shape, k).
+ */
+sd_status sd_topk_blocks(const sd_shape* shape, const void* q, const void* k_pages,
+                         const int32_t* block_table, const int32_t* ctx_lens, int32_t k,
+                         int32_t* sel_blocks, void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes a call needs; `shape` points to an sd_shape (ATTN, TOPK,
+ * COMMIT) or an sd_accept_shape (ACCEPT); `extra` is k_sel (ATTN, 0 = dense) or
+ * k (TOPK).  0 on bad input. */
+size_t sd_workspace_bytes(int32_t call_id, const void* shape, int32_t extra);
+
+/* Synchronises `stream`, reads the sticky bits into *bits (may be NULL), clears
+ * them, and returns SD_DEVICE_DATA_ERROR if any was set. */
+sd_status sd_device_status(void* ws, void* stream, uint32_t* bits);
+
+/* Static description of a status code. */
+const char* sd_status_str(sd_status s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SDTREE_H */

@@ -99,10 +99,10 @@ def accept(target_logits, logit_dtype, draft_probs, tree_parent, tree_token, uni
                     if ok:
                         nxt = k
                         break
-                    r = np.maximum(r - qd, 0.0)
-                    z = r.sum()
+                    rn = np.maximum(r - qd, 0.0)
+                    z = rn.sum()
                     if z > 0:
-                        r = r / z
+                        r = rn / z
                 if nxt is None:
                     x, c, thr = invcdf(r, float(uniforms[b, cur, 1]))
                     ev.append(("sample", cur, x, c, thr))

@@ -1,0 +1,103 @@
+"""The C ABI on the CPU: the library loads, exports every function the header
+declares, sizes workspaces, and rejects bad arguments on the host before any
+HIP call (so these run without a GPU)."""
+import ctypes
+
+import pytest
+
+from tree_verification_amd import _lib
+
+L = None
+
+
+def setup_module():
+    global L
+    L = _lib.lib()
+
+
+def test_exports_every_declared_function():
+    names = _lib.declared_functions()
+    assert len(names) == 7
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings():
+    for code in range(8):
+        assert L.sd_status_str(code)
+    assert L.sd_status_str(99) == b"unknown status"
+
+
+def _shape(**kw):
+    base = dict(B=16, T=64, Hq=32, Hkv=8, D=128, bs=16, max_blocks=260, num_blocks=4160,
+                dtype=1, tree_stride=64, scale=0.0)
+    base.update(kw)
+    return _lib.SdShape(*[base[f] for f, _ in _lib.SdShape._fields_])
+
+
+FAKE = ctypes.c_void_p(0x1000)
+
+
+def _attn(shape, ws_bytes=1 << 40, sel=None, ksel=0, null_q=False):
+    return L.sd_tree_verify_attn(ctypes.byref(shape), None if null_q else FAKE, FAKE, FAKE, FAKE,
+                                 FAKE, FAKE, sel, ksel, FAKE, FAKE, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Hq=30), 2), (dict(T=0), 2), (dict(B=0), 2), (dict(tree_stride=5), 2),
+    (dict(dtype=7), 3), (dict(D=96), 4), (dict(bs=12), 4), (dict(T=5000, tree_stride=5000), 4),
+    (dict(scale=-1.0), 1), (dict(scale=float("inf")), 1),
+])
+def test_attention_rejects_bad_shapes(kw, code):
+    assert _attn(_shape(**kw)) == code
+
+
+def test_attention_rejects_null_small_ws_and_bad_ksel():
+    s = _shape()
+    assert _attn(s, null_q=True) == 1
+    need = L.sd_workspace_bytes(1, ctypes.byref(s), 0)
+    assert need > 0
+    assert _attn(s, ws_bytes=need - 1) == 5
+    assert _attn(s, sel=FAKE, ksel=0) == 1
+    assert _attn(s, sel=FAKE, ksel=65) == 1
+    assert _attn(s, sel=None, ksel=3) == 1
+
+
+def test_workspace_sizes():
+    s = _shape()
+    dense = L.sd_workspace_bytes(1, ctypes.byref(s), 0)
+    assert dense >= 256 + 16 * 64 * 8   # header + one ancestor word per node
+    assert L.sd_workspace_bytes(1, ctypes.byref(s), 65) == 0
+    assert L.sd_workspace_bytes(3, ctypes.byref(s), 32) >= 16 * 260 * 8 * 128 * 4
+    assert L.sd_workspace_bytes(3, ctypes.byref(s), 0) == 0
+    assert L.sd_workspace_bytes(4, ctypes.byref(s), 0) == 256
+    a = _lib.SdAcceptShape(16, 64, 128256, 1, 64)
+    assert L.sd_workspace_bytes(2, ctypes.byref(a), 0) == 256
+    assert L.sd_workspace_bytes(9, ctypes.byref(s), 0) == 0
+    assert L.sd_workspace_bytes(1, None, 0) == 0
+
+
+def test_accept_rejects_bad_arguments():
+    def call(shape, tau=0.8, unif=FAKE, ws=256):
+        return L.sd_accept(ctypes.byref(shape), FAKE, FAKE, FAKE, FAKE, unif, tau, FAKE, FAKE, FAKE,
+                           FAKE, ws, None)
+    ok = _lib.SdAcceptShape(2, 8, 100, 1, 8)
+    assert call(_lib.SdAcceptShape(0, 8, 100, 1, 8)) == 2
+    assert call(_lib.SdAcceptShape(2, 8, 100, 1, 3)) == 2
+    assert call(_lib.SdAcceptShape(2, 8, 100, 5, 8)) == 3
+    assert call(_lib.SdAcceptShape(2, 5000, 100, 1, 5000)) == 4
+    assert call(ok, tau=-0.5) == 1
+    assert call(ok, tau=float("nan")) == 1
+    assert call(ok, unif=None) == 1
+    assert call(ok, ws=100) == 5
+
+
+def test_commit_and_topk_reject_bad_arguments():
+    s = _shape()
+    assert L.sd_kv_commit(ctypes.byref(_shape(Hq=7)), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 256,
+                          None) == 2
+    assert L.sd_kv_commit(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 256, None) == 1
+    assert L.sd_kv_commit(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 8, None) == 5
+    assert L.sd_topk_blocks(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, 0, FAKE, FAKE, 1 << 40, None) == 1
+    assert L.sd_topk_blocks(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, 4, FAKE, FAKE, 10, None) == 5
+    assert L.sd_device_status(None, None, None) == 1

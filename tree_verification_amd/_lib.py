@@ -1,0 +1,207 @@
+"""ctypes binding of libsdtree.so: argument marshalling only.
+
+Every step of the verification pass runs in the library's HIP kernels; this
+module turns torch tensors (device memory, the current HIP stream) into the
+C ABI's plain pointers and sizes.  There is no CPU fallback: if the library
+is not built, or a tensor is not on the GPU, calls raise.
+"""
+import ctypes
+import os
+import re
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsdtree.so")
+HEADER = os.path.join(os.path.dirname(_HERE), "include", "sdtree.h")
+
+SD_F32, SD_BF16 = 0, 1
+SD_CALL_ATTN, SD_CALL_ACCEPT, SD_CALL_TOPK, SD_CALL_COMMIT = 1, 2, 3, 4
+STATUS = {0: "SD_OK", 1: "SD_INVALID_ARG", 2: "SD_BAD_SHAPE", 3: "SD_BAD_DTYPE",
+          4: "SD_UNSUPPORTED", 5: "SD_CAPACITY", 6: "SD_HIP_ERROR", 7: "SD_DEVICE_DATA_ERROR"}
+ERR_BITS = {0x1: "parent", 0x2: "block", 0x4: "capacity", 0x8: "token", 0x10: "selection"}
+
+
+class SdShape(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("T", ctypes.c_int32), ("Hq", ctypes.c_int32),
+                ("Hkv", ctypes.c_int32), ("D", ctypes.c_int32), ("bs", ctypes.c_int32),
+                ("max_blocks", ctypes.c_int32), ("num_blocks", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("tree_stride", ctypes.c_int32),
+                ("scale", ctypes.c_float)]
+
+
+class SdAcceptShape(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("T", ctypes.c_int32), ("V", ctypes.c_int32),
+                ("logit_dtype", ctypes.c_int32), ("tree_stride", ctypes.c_int32)]
+
+
+class SdError(RuntimeError):
+    def __init__(self, call, code):
+        super().__init__("%s returned %s" % (call, STATUS.get(code, code)))
+        self.code = code
+
+
+_P = ctypes.c_void_p
+_LIB = None
+
+
+def declared_functions():
+    """Names of the functions include/sdtree.h declares."""
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w]+\*?\s+\*?(sd_\w+)\s*\(", text, re.M)))
+
+
+def lib():
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("libsdtree.so is not built; run `python -m tree_verification_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    i32, sz = ctypes.c_int32, ctypes.c_size_t
+    sig = {
+        "sd_tree_verify_attn": [ctypes.POINTER(SdShape), _P, _P, _P, _P, _P, _P, _P, i32, _P, _P, sz, _P],
+        "sd_accept": [ctypes.POINTER(SdAcceptShape), _P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P,
+                      _P, sz, _P],
+        "sd_kv_commit": [ctypes.POINTER(SdShape), _P, _P, _P, _P, _P, _P, _P, sz, _P],
+        "sd_topk_blocks": [ctypes.POINTER(SdShape), _P, _P, _P, _P, i32, _P, _P, sz, _P],
+        "sd_device_status": [_P, _P, ctypes.POINTER(ctypes.c_uint32)],
+        "sd_workspace_bytes": [i32, _P, i32],
+        "sd_status_str": [i32],
+    }
+    for name, args in sig.items():
+        f = getattr(L, name)
+        f.argtypes = args
+        f.restype = ctypes.c_int
+    L.sd_workspace_bytes.restype = ctypes.c_size_t
+    L.sd_status_str.restype = ctypes.c_char_p
+    _LIB = L
+    return L
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensor must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check(name, code):
+    if code != 0:
+        raise SdError(name, code)
+
+
+_dtype_code = {torch.float32: SD_F32, torch.bfloat16: SD_BF16}
+
+
+def make_shape(q, k_pages, block_table, tree_parent, scale=0.0):
+    B, T, Hq, D = q.shape
+    nb, Hkv, bs, D2 = k_pages.shape
+    if D2 != D:
+        raise ValueError("head dim mismatch")
+    stride = 0 if tree_parent.shape[0] == 1 else T
+    return SdShape(B, T, Hq, Hkv, D, bs, block_table.shape[1], nb, _dtype_code[q.dtype], stride,
+                   float(scale))
+
+
+class Workspace:
+    """A zero-filled device scratch buffer, grown on demand (one per device)."""
+
+    def __init__(self):
+        self._buf = {}
+
+    def get(self, device, nbytes):
+        key = torch.device(device).index
+        buf = self._buf.get(key)
+        if buf is None or buf.numel() < nbytes:
+            buf = torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+            self._buf[key] = buf
+        return buf
+
+
+_WS = Workspace()
+
+
+def workspace_bytes(call, shape, extra=0):
+    return lib().sd_workspace_bytes(call, ctypes.byref(shape), extra)
+
+
+def tree_verify_attn(q, k_pages, v_pages, block_table, ctx_lens, tree_parent, out=None,
+                     sel_blocks=None, scale=0.0, ws=None):
+    shape = make_shape(q, k_pages, block_table, tree_parent, scale)
+    if out is None:
+        out = torch.empty_like(q)
+    k_sel = 0 if sel_blocks is None else sel_blocks.shape[-1]
+    need = workspace_bytes(SD_CALL_ATTN, shape, k_sel)
+    if need == 0:
+        raise SdError("sd_workspace_bytes", 2)
+    ws = _WS.get(q.device, need) if ws is None else ws
+    _check("sd_tree_verify_attn", lib().sd_tree_verify_attn(
+        ctypes.byref(shape), _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table),
+        _ptr(ctx_lens), _ptr(tree_parent), _ptr(sel_blocks), k_sel, _ptr(out), _ptr(ws),
+        ws.numel(), _stream(q.device)))
+    return out
+
+
+def accept(target_logits, draft_probs, tree_parent, tree_token, uniforms, temperature,
+           path=None, path_len=None, bonus=None, ws=None):
+    B, T, V = target_logits.shape
+    shape = SdAcceptShape(B, T, V, _dtype_code[target_logits.dtype],
+                          0 if tree_parent.shape[0] == 1 else T)
+    dev = target_logits.device
+    if path is None:
+        path = torch.empty((B, T), dtype=torch.int32, device=dev)
+    if path_len is None:
+        path_len = torch.empty(B, dtype=torch.int32, device=dev)
+    if bonus is None:
+        bonus = torch.empty(B, dtype=torch.int32, device=dev)
+    need = workspace_bytes(SD_CALL_ACCEPT, shape)
+    ws = _WS.get(dev, need) if ws is None else ws
+    _check("sd_accept", lib().sd_accept(
+        ctypes.byref(shape), _ptr(target_logits), _ptr(draft_probs), _ptr(tree_parent),
+        _ptr(tree_token), _ptr(uniforms), float(temperature), _ptr(path), _ptr(path_len),
+        _ptr(bonus), _ptr(ws), ws.numel(), _stream(dev)))
+    return path, path_len, bonus
+
+
+def kv_commit(k_pages, v_pages, block_table, ctx_lens, path, path_len, ws=None):
+    B, T = path.shape
+    nb, Hkv, bs, D = k_pages.shape
+    shape = SdShape(B, T, Hkv, Hkv, D, bs, block_table.shape[1], nb, _dtype_code[k_pages.dtype],
+                    T, 0.0)
+    need = workspace_bytes(SD_CALL_COMMIT, shape)
+    ws = _WS.get(k_pages.device, need) if ws is None else ws
+    _check("sd_kv_commit", lib().sd_kv_commit(
+        ctypes.byref(shape), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(ctx_lens),
+        _ptr(path), _ptr(path_len), _ptr(ws), ws.numel(), _stream(k_pages.device)))
+
+
+def topk_blocks(q, k_pages, block_table, ctx_lens, k, sel=None, ws=None):
+    B, T, Hq, D = q.shape
+    parent_like = torch.empty((1, T))
+    shape = make_shape(q, k_pages, block_table, parent_like)
+    if sel is None:
+        sel = torch.empty((B, T, Hq, k), dtype=torch.int32, device=q.device)
+    need = workspace_bytes(SD_CALL_TOPK, shape, k)
+    ws = _WS.get(q.device, need) if ws is None else ws
+    _check("sd_topk_blocks", lib().sd_topk_blocks(
+        ctypes.byref(shape), _ptr(q), _ptr(k_pages), _ptr(block_table), _ptr(ctx_lens), int(k),
+        _ptr(sel), _ptr(ws), ws.numel(), _stream(q.device)))
+    return sel
+
+
+def device_status(ws=None, device="cuda"):
+    """Reads and clears the sticky device error bits of a workspace."""
+    ws = _WS.get(device, 256) if ws is None else ws
+    bits = ctypes.c_uint32(0)
+    code = lib().sd_device_status(_ptr(ws), _stream(ws.device), ctypes.byref(bits))
+    if code not in (0, 7):
+        raise SdError("sd_device_status", code)
+    return bits.value

@@ -1,0 +1,133 @@
+// Internal definitions shared by the sdtree kernels and the host layer.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "sdtree.h"
+
+namespace sdtree {
+
+typedef uint16_t bf16_bits;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Workspace header: the sticky status word and small counters live in the
+// first 256 bytes; call-specific regions follow.
+constexpr size_t kWsHeader = 256;
+
+__device__ __forceinline__ float bf16_to_f32(bf16_bits b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// float -> bf16, round to nearest even (finite inputs).
+__device__ __forceinline__ bf16_bits f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<bf16_bits>(u >> 16);
+}
+
+__device__ __forceinline__ void set_status(uint32_t* status, uint32_t bit) {
+  atomicOr(status, bit);
+}
+
+// Element loads for the two storage types.
+template <typename E> struct Elem;
+template <> struct Elem<float> {
+  static __device__ __forceinline__ float load(const float* p, size_t i) { return p[i]; }
+  static __device__ __forceinline__ void store(float* p, size_t i, float v) { p[i] = v; }
+};
+template <> struct Elem<bf16_bits> {
+  static __device__ __forceinline__ float load(const bf16_bits* p, size_t i) {
+    return bf16_to_f32(p[i]);
+  }
+  static __device__ __forceinline__ void store(bf16_bits* p, size_t i, float v) {
+    p[i] = f32_to_bf16(v);
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Attention launch plan (host side; depends on the shape only).
+struct AttnPlan {
+  int variant;          // 0: VALU (fp32 or tiny), 1: MFMA bf16
+  int D;
+  int WQ, WK, QW, KW;   // waves across query rows / across keys; rows and keys per wave
+  int NK;               // keys per LDS tile = KW * WK
+  int rows;             // query rows per workgroup = WQ * QW
+  int n_qtiles, n_splits, tps;
+  int n_ct_max;         // context tiles, upper bound
+  int n_tt;             // tree tiles
+  int W64;              // 64-bit ancestor words per node
+  int T_tree;           // number of distinct trees (1 or B)
+  int u_max;            // sparse: max distinct blocks per workgroup
+  size_t lds_bytes;
+  size_t anc_off, part_o_off, part_ml_off, total;
+};
+
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* table;
+  const int32_t* ctx;
+  const int32_t* parent;
+  const uint64_t* anc;
+  const int32_t* sel;
+  int32_t ksel;
+  void* out;
+  float* part_o;
+  float* part_ml;
+  uint32_t* status;
+  int B, T, Hq, Hkv, G, M, D, bs, max_blocks, num_blocks, tree_stride;
+  float scale_log2;
+  int n_qtiles, n_splits, tps, W64, u_max;
+};
+
+struct AcceptArgs {
+  const void* logits;
+  int logits_f32;
+  const float* draft;
+  const int32_t* parent;
+  const int32_t* token;
+  const float* unif;
+  float tau;
+  int B, T, V, tree_stride;
+  int32_t* path;
+  int32_t* path_len;
+  int32_t* bonus;
+  uint32_t* status;
+};
+
+struct CommitArgs {
+  void* k;
+  void* v;
+  const int32_t* table;
+  int32_t* ctx;
+  const int32_t* path;
+  const int32_t* path_len;
+  uint32_t* status;
+  int B, T, Hkv, D, bs, max_blocks, num_blocks, esize;
+};
+
+struct TopkArgs {
+  const void* q;
+  const void* k;
+  const int32_t* table;
+  const int32_t* ctx;
+  int32_t* sel;
+  float* means;    // [B][nbmax][Hkv][D]
+  float* scores;   // [B*T*Hq][nbmax]
+  uint32_t* status;
+  int B, T, Hq, Hkv, G, D, bs, max_blocks, num_blocks, topk, nbmax;
+};
+
+// Launchers (one per kernel family).
+hipError_t launch_anc_mask(const int32_t* parent, int T, int W64, int n_trees, uint64_t* anc,
+                           uint32_t* status, hipStream_t st);
+hipError_t launch_attn_valu(const AttnArgs& a, bool f32, hipStream_t st);
+hipError_t launch_attn_mfma(const AttnArgs& a, const AttnPlan& p, hipStream_t st);
+hipError_t launch_accept(const AcceptArgs& a, hipStream_t st);
+hipError_t launch_commit(const CommitArgs& a, hipStream_t st);
+hipError_t launch_topk(const TopkArgs& a, bool f32, hipStream_t st);
+
+}  // namespace sdtree

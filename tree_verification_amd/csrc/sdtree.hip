@@ -1,0 +1,283 @@
+// Host side of the sdtree C ABI: argument validation (always before any HIP
+// call), launch planning, workspace carving, kernel launches.
+#include <math.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "common.h"
+
+namespace sdtree {
+
+constexpr int kMaxT = 4096;
+constexpr int kMaxKsel = 64;
+constexpr size_t kLdsLimit = 160 * 1024;
+
+static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+static sd_status check_shape(const sd_shape* s) {
+  if (!s) return SD_INVALID_ARG;
+  if (s->B < 1 || s->T < 1 || s->Hq < 1 || s->Hkv < 1 || s->D < 1 || s->bs < 1 ||
+      s->max_blocks < 1 || s->num_blocks < 1)
+    return SD_BAD_SHAPE;
+  if (s->Hq % s->Hkv != 0) return SD_BAD_SHAPE;
+  if (s->tree_stride != 0 && s->tree_stride != s->T) return SD_BAD_SHAPE;
+  if (s->dtype != SD_F32 && s->dtype != SD_BF16) return SD_BAD_DTYPE;
+  if (s->D != 64 && s->D != 128) return SD_UNSUPPORTED;
+  if (s->bs % 8 != 0) return SD_UNSUPPORTED;
+  if (s->T > kMaxT) return SD_UNSUPPORTED;
+  if ((long long)s->max_blocks * s->bs > (1ll << 30)) return SD_UNSUPPORTED;
+  if ((long long)s->num_blocks * s->Hkv * s->bs * s->D > (1ll << 40)) return SD_UNSUPPORTED;
+  if (!(s->scale >= 0.f) || isinf(s->scale)) return SD_INVALID_ARG;
+  return SD_OK;
+}
+
+// The plan depends on the shape only, so workspace sizing and launch agree.
+static AttnPlan plan_attn(const sd_shape* s, int ksel, bool sparse) {
+  AttnPlan p;
+  memset(&p, 0, sizeof(p));
+  const int G = s->Hq / s->Hkv;
+  const int M = s->T * G;
+  p.D = s->D;
+  p.W64 = (s->T + 63) / 64;
+  p.T_tree = s->tree_stride ? s->B : 1;
+  p.anc_off = kWsHeader;
+  const size_t anc_bytes = (size_t)p.T_tree * s->T * p.W64 * 8;
+  p.part_o_off = align_up(p.anc_off + anc_bytes, 256);
+  if (s->dtype == SD_F32) {
+    p.variant = 0;
+    p.n_splits = 1;
+    p.part_ml_off = p.part_o_off;
+    p.total = p.part_o_off;
+    return p;
+  }
+  p.variant = 1;
+  if (M <= 32) {
+    p.WQ = 1; p.WK = 4; p.QW = 32; p.KW = 32;
+  } else if (M <= 64) {
+    p.WQ = 2; p.WK = 2; p.QW = 32; p.KW = 32;
+  } else {
+    p.WQ = 4; p.WK = 1; p.QW = 32; p.KW = 64;
+  }
+  p.NK = p.KW * p.WK;
+  p.rows = p.WQ * p.QW;
+  p.n_qtiles = (M + p.rows - 1) / p.rows;
+  p.n_tt = (s->T + p.NK - 1) / p.NK;
+  const long long cap = (long long)s->max_blocks * s->bs;
+  if (sparse) {
+    p.u_max = (int)std::min<long long>(s->max_blocks, (long long)p.rows * ksel);
+    p.n_ct_max = (int)(((long long)p.u_max * s->bs + p.NK - 1) / p.NK);
+  } else {
+    const long long ctx_max = std::max<long long>(cap - s->T, 0);
+    p.n_ct_max = (int)((ctx_max + p.NK - 1) / p.NK);
+  }
+  const int ntiles = p.n_ct_max + p.n_tt;
+  const long long base = (long long)s->B * s->Hkv * p.n_qtiles;
+  // Aim for about 2 workgroups per CU on 256 CUs, with at least 8 tiles each.
+  const long long want = 512;
+  int splits = (int)std::max<long long>(1, (want + base - 1) / base);
+  splits = std::min(splits, std::max(1, ntiles / 8));
+  p.tps = (ntiles + splits - 1) / splits;
+  p.n_splits = (ntiles + p.tps - 1) / p.tps;
+  const size_t tiles = (size_t)2 * p.NK * (p.D + 8) * 2 + (size_t)2 * p.D * (p.NK + 8) * 2;
+  const size_t merge = p.WK > 1 ? (size_t)4 * (p.QW * p.D + 2 * p.QW) * 4 : 0;
+  size_t lds = std::max(tiles, merge) + 128;
+  if (sparse) {
+    const size_t bw = (size_t)(s->max_blocks + 31) / 32;
+    lds += 4 * bw * 2 + 4 * (size_t)p.u_max + 4 * (size_t)p.rows * ((p.u_max + 31) / 32);
+  }
+  p.lds_bytes = align_up(lds, 16);
+  const size_t nrows = (size_t)s->B * s->T * s->Hq;
+  if (p.n_splits > 1) {
+    p.part_ml_off = align_up(p.part_o_off + nrows * p.n_splits * p.D * 4, 256);
+    p.total = align_up(p.part_ml_off + nrows * p.n_splits * 2 * 4, 256);
+  } else {
+    p.part_ml_off = p.part_o_off;
+    p.total = p.part_o_off;
+  }
+  return p;
+}
+
+static size_t topk_ws(const sd_shape* s, size_t* means_off, size_t* scores_off) {
+  const size_t nbmax = (size_t)s->max_blocks;
+  const size_t mo = kWsHeader;
+  const size_t so = align_up(mo + (size_t)s->B * nbmax * s->Hkv * s->D * 4, 256);
+  if (means_off) *means_off = mo;
+  if (scores_off) *scores_off = so;
+  return align_up(so + (size_t)s->B * s->T * s->Hq * nbmax * 4, 256);
+}
+
+static sd_status hip_status(hipError_t e) { return e == hipSuccess ? SD_OK : SD_HIP_ERROR; }
+
+}  // namespace sdtree
+
+using namespace sdtree;
+
+extern "C" {
+
+const char* sd_status_str(sd_status s) {
+  switch (s) {
+    case SD_OK: return "ok";
+    case SD_INVALID_ARG: return "invalid argument";
+    case SD_BAD_SHAPE: return "bad shape";
+    case SD_BAD_DTYPE: return "bad dtype";
+    case SD_UNSUPPORTED: return "unsupported";
+    case SD_CAPACITY: return "workspace too small";
+    case SD_HIP_ERROR: return "HIP error";
+    case SD_DEVICE_DATA_ERROR: return "device data error";
+  }
+  return "unknown status";
+}
+
+size_t sd_workspace_bytes(int32_t call_id, const void* shape, int32_t extra) {
+  if (!shape) return 0;
+  if (call_id == SD_CALL_ATTN) {
+    const sd_shape* s = static_cast<const sd_shape*>(shape);
+    if (check_shape(s) != SD_OK) return 0;
+    if (extra < 0 || extra > kMaxKsel) return 0;
+    return plan_attn(s, extra, extra > 0).total;
+  }
+  if (call_id == SD_CALL_ACCEPT) {
+    const sd_accept_shape* s = static_cast<const sd_accept_shape*>(shape);
+    if (s->B < 1 || s->T < 1 || s->V < 1) return 0;
+    return kWsHeader;
+  }
+  if (call_id == SD_CALL_COMMIT) {
+    const sd_shape* s = static_cast<const sd_shape*>(shape);
+    return check_shape(s) == SD_OK ? kWsHeader : 0;
+  }
+  if (call_id == SD_CALL_TOPK) {
+    const sd_shape* s = static_cast<const sd_shape*>(shape);
+    if (check_shape(s) != SD_OK || extra < 1) return 0;
+    return topk_ws(s, nullptr, nullptr);
+  }
+  return 0;
+}
+
+sd_status sd_tree_verify_attn(const sd_shape* shape, const void* q, const void* k_pages,
+                              const void* v_pages, const int32_t* block_table,
+                              const int32_t* ctx_lens, const int32_t* tree_parent,
+                              const int32_t* sel_blocks, int32_t k_sel, void* out, void* ws,
+                              size_t ws_bytes, void* stream) {
+  sd_status st = check_shape(shape);
+  if (st != SD_OK) return st;
+  if (!q || !k_pages || !v_pages || !block_table || !ctx_lens || !tree_parent || !out || !ws)
+    return SD_INVALID_ARG;
+  const bool sparse = sel_blocks != nullptr;
+  if (sparse && (k_sel < 1 || k_sel > kMaxKsel)) return SD_INVALID_ARG;
+  if (!sparse && k_sel != 0) return SD_INVALID_ARG;
+  const sd_shape& s = *shape;
+  const AttnPlan p = plan_attn(&s, k_sel, sparse);
+  if (ws_bytes < p.total) return SD_CAPACITY;
+  if (p.variant == 1 && p.lds_bytes > kLdsLimit) return SD_UNSUPPORTED;
+
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  unsigned char* w = static_cast<unsigned char*>(ws);
+  uint32_t* status = reinterpret_cast<uint32_t*>(w);
+  uint64_t* anc = reinterpret_cast<uint64_t*>(w + p.anc_off);
+  hipError_t e = launch_anc_mask(tree_parent, s.T, p.W64, p.T_tree, anc, status, hs);
+  if (e != hipSuccess) return SD_HIP_ERROR;
+
+  AttnArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = q; a.k = k_pages; a.v = v_pages; a.table = block_table; a.ctx = ctx_lens;
+  a.parent = tree_parent; a.anc = anc; a.sel = sel_blocks; a.ksel = k_sel; a.out = out;
+  a.part_o = reinterpret_cast<float*>(w + p.part_o_off);
+  a.part_ml = reinterpret_cast<float*>(w + p.part_ml_off);
+  a.status = status;
+  a.B = s.B; a.T = s.T; a.Hq = s.Hq; a.Hkv = s.Hkv; a.G = s.Hq / s.Hkv; a.M = s.T * a.G;
+  a.D = s.D; a.bs = s.bs; a.max_blocks = s.max_blocks; a.num_blocks = s.num_blocks;
+  a.tree_stride = s.tree_stride;
+  const float scale = s.scale > 0.f ? s.scale : 1.f / sqrtf((float)s.D);
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.n_qtiles = p.n_qtiles; a.n_splits = p.n_splits; a.tps = p.tps; a.W64 = p.W64; a.u_max = p.u_max;
+  if (p.variant == 0) return hip_status(launch_attn_valu(a, s.dtype == SD_F32, hs));
+  return hip_status(launch_attn_mfma(a, p, hs));
+}
+
+sd_status sd_accept(const sd_accept_shape* shape, const void* target_logits,
+                    const float* draft_probs, const int32_t* tree_parent,
+                    const int32_t* tree_token, const float* uniforms, float temperature,
+                    int32_t* path, int32_t* path_len, int32_t* bonus, void* ws, size_t ws_bytes,
+                    void* stream) {
+  if (!shape) return SD_INVALID_ARG;
+  const sd_accept_shape& s = *shape;
+  if (s.B < 1 || s.T < 1 || s.V < 1) return SD_BAD_SHAPE;
+  if (s.tree_stride != 0 && s.tree_stride != s.T) return SD_BAD_SHAPE;
+  if (s.logit_dtype != SD_F32 && s.logit_dtype != SD_BF16) return SD_BAD_DTYPE;
+  if (s.T > kMaxT) return SD_UNSUPPORTED;
+  if (!(temperature >= 0.f) || isinf(temperature)) return SD_INVALID_ARG;
+  if (!target_logits || !tree_parent || !tree_token || !path || !path_len || !bonus || !ws)
+    return SD_INVALID_ARG;
+  if (temperature > 0.f && !uniforms) return SD_INVALID_ARG;
+  if (ws_bytes < kWsHeader) return SD_CAPACITY;
+  AcceptArgs a;
+  memset(&a, 0, sizeof(a));
+  a.logits = target_logits;
+  a.logits_f32 = s.logit_dtype == SD_F32;
+  a.draft = temperature > 0.f ? draft_probs : nullptr;
+  a.parent = tree_parent; a.token = tree_token; a.unif = uniforms; a.tau = temperature;
+  a.B = s.B; a.T = s.T; a.V = s.V; a.tree_stride = s.tree_stride;
+  a.path = path; a.path_len = path_len; a.bonus = bonus;
+  a.status = static_cast<uint32_t*>(ws);
+  return hip_status(launch_accept(a, static_cast<hipStream_t>(stream)));
+}
+
+sd_status sd_kv_commit(const sd_shape* shape, void* k_pages, void* v_pages,
+                       const int32_t* block_table, int32_t* ctx_lens, const int32_t* path,
+                       const int32_t* path_len, void* ws, size_t ws_bytes, void* stream) {
+  sd_status st = check_shape(shape);
+  if (st != SD_OK) return st;
+  if (!k_pages || !v_pages || !block_table || !ctx_lens || !path || !path_len || !ws)
+    return SD_INVALID_ARG;
+  if (ws_bytes < kWsHeader) return SD_CAPACITY;
+  CommitArgs a;
+  memset(&a, 0, sizeof(a));
+  a.k = k_pages; a.v = v_pages; a.table = block_table; a.ctx = ctx_lens; a.path = path;
+  a.path_len = path_len;
+  a.B = shape->B; a.T = shape->T; a.Hkv = shape->Hkv; a.D = shape->D; a.bs = shape->bs;
+  a.max_blocks = shape->max_blocks; a.num_blocks = shape->num_blocks;
+  a.esize = shape->dtype == SD_F32 ? 4 : 2;
+  a.status = static_cast<uint32_t*>(ws);
+  return hip_status(launch_commit(a, static_cast<hipStream_t>(stream)));
+}
+
+sd_status sd_topk_blocks(const sd_shape* shape, const void* q, const void* k_pages,
+                         const int32_t* block_table, const int32_t* ctx_lens, int32_t k,
+                         int32_t* sel_blocks, void* ws, size_t ws_bytes, void* stream) {
+  sd_status st = check_shape(shape);
+  if (st != SD_OK) return st;
+  if (!q || !k_pages || !block_table || !ctx_lens || !sel_blocks || !ws) return SD_INVALID_ARG;
+  if (k < 1) return SD_INVALID_ARG;
+  size_t mo, so;
+  const size_t need = topk_ws(shape, &mo, &so);
+  if (ws_bytes < need) return SD_CAPACITY;
+  unsigned char* w = static_cast<unsigned char*>(ws);
+  TopkArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = q; a.k = k_pages; a.table = block_table; a.ctx = ctx_lens; a.sel = sel_blocks;
+  a.means = reinterpret_cast<float*>(w + mo);
+  a.scores = reinterpret_cast<float*>(w + so);
+  a.status = reinterpret_cast<uint32_t*>(w);
+  a.B = shape->B; a.T = shape->T; a.Hq = shape->Hq; a.Hkv = shape->Hkv;
+  a.G = shape->Hq / shape->Hkv; a.D = shape->D; a.bs = shape->bs;
+  a.max_blocks = shape->max_blocks; a.num_blocks = shape->num_blocks; a.topk = k;
+  a.nbmax = shape->max_blocks;
+  return hip_status(launch_topk(a, shape->dtype == SD_F32, static_cast<hipStream_t>(stream)));
+}
+
+sd_status sd_device_status(void* ws, void* stream, uint32_t* bits) {
+  if (!ws) return SD_INVALID_ARG;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (hipStreamSynchronize(hs) != hipSuccess) return SD_HIP_ERROR;
+  uint32_t v = 0;
+  if (hipMemcpy(&v, ws, sizeof(v), hipMemcpyDeviceToHost) != hipSuccess) return SD_HIP_ERROR;
+  if (v) {
+    const uint32_t zero = 0;
+    if (hipMemcpy(ws, &zero, sizeof(zero), hipMemcpyHostToDevice) != hipSuccess) return SD_HIP_ERROR;
+  }
+  if (bits) *bits = v;
+  return v ? SD_DEVICE_DATA_ERROR : SD_OK;
+}
+
+}  // extern "C"
