@@ -25,7 +25,9 @@
  *     workspace status word and the affected unit is skipped;
  *     sd_device_status reads (and clears) it.
  *   - No exceptions, aborts or printing.  One workspace must not be used by two
- *     calls that may run concurrently.
+ *     calls that may run concurrently, and a workspace serves one call kind:
+ *     sd_accept keeps barrier counters in its workspace that must read zero
+ *     when a call starts (every call leaves them at zero).
  *
  * Layouts (row-major, innermost last)
  *   q, out        [B, T, Hq, D]                 element type `dtype`
@@ -69,6 +71,8 @@ typedef enum sd_dtype { SD_F32 = 0, SD_BF16 = 1 } sd_dtype;
 #define SD_ERR_CAPACITY   0x4u   /* ctx_b + T exceeds max_blocks * bs, or ctx_b < 0 */
 #define SD_ERR_TOKEN      0x8u   /* tree token outside [0, V) */
 #define SD_ERR_SELECTION  0x10u  /* sel_blocks entry not a context block / not ascending */
+#define SD_ERR_TIMEOUT    0x20u  /* a cross-workgroup wait gave up; results of the call are invalid
+                                    and the workspace must be zero-filled again */
 
 typedef struct sd_shape {
   int32_t B;            /* sequences */
@@ -76,7 +80,7 @@ typedef struct sd_shape {
   int32_t Hq;           /* query heads */
   int32_t Hkv;          /* KV heads; Hq % Hkv == 0 */
   int32_t D;            /* head dim: 64 or 128 */
-  int32_t bs;           /* tokens per KV block; a multiple of 8 */
+  int32_t bs;           /* tokens per KV block: a power of two >= 8 */
   int32_t max_blocks;   /* columns of block_table */
   int32_t num_blocks;   /* blocks in k_pages / v_pages */
   int32_t dtype;        /* sd_dtype of q, k_pages, v_pages, out */

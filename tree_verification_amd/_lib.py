@@ -112,18 +112,29 @@ def make_shape(q, k_pages, block_table, tree_parent, scale=0.0):
 
 
 class Workspace:
-    """A zero-filled device scratch buffer, grown on demand (one per device)."""
+    """Zero-filled device scratch buffers, one per (device, call kind), grown on
+    demand.  Call kinds never share a buffer: the acceptance walk keeps barrier
+    counters in its workspace that must read zero when a call starts."""
 
     def __init__(self):
         self._buf = {}
 
-    def get(self, device, nbytes):
-        key = torch.device(device).index
+    @staticmethod
+    def _index(device):
+        dev = torch.device(device)
+        return dev.index if dev.index is not None else torch.cuda.current_device()
+
+    def get(self, device, nbytes, kind):
+        key = (self._index(device), kind)
         buf = self._buf.get(key)
         if buf is None or buf.numel() < nbytes:
-            buf = torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+            buf = torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device="cuda:%d" % key[0])
             self._buf[key] = buf
         return buf
+
+    def all(self, device):
+        idx = self._index(device)
+        return [b for (i, _), b in self._buf.items() if i == idx]
 
 
 _WS = Workspace()
@@ -142,7 +153,7 @@ def tree_verify_attn(q, k_pages, v_pages, block_table, ctx_lens, tree_parent, ou
     need = workspace_bytes(SD_CALL_ATTN, shape, k_sel)
     if need == 0:
         raise SdError("sd_workspace_bytes", 2)
-    ws = _WS.get(q.device, need) if ws is None else ws
+    ws = _WS.get(q.device, need, SD_CALL_ATTN) if ws is None else ws
     _check("sd_tree_verify_attn", lib().sd_tree_verify_attn(
         ctypes.byref(shape), _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table),
         _ptr(ctx_lens), _ptr(tree_parent), _ptr(sel_blocks), k_sel, _ptr(out), _ptr(ws),
@@ -163,7 +174,7 @@ def accept(target_logits, draft_probs, tree_parent, tree_token, uniforms, temper
     if bonus is None:
         bonus = torch.empty(B, dtype=torch.int32, device=dev)
     need = workspace_bytes(SD_CALL_ACCEPT, shape)
-    ws = _WS.get(dev, need) if ws is None else ws
+    ws = _WS.get(dev, need, SD_CALL_ACCEPT) if ws is None else ws
     _check("sd_accept", lib().sd_accept(
         ctypes.byref(shape), _ptr(target_logits), _ptr(draft_probs), _ptr(tree_parent),
         _ptr(tree_token), _ptr(uniforms), float(temperature), _ptr(path), _ptr(path_len),
@@ -177,7 +188,7 @@ def kv_commit(k_pages, v_pages, block_table, ctx_lens, path, path_len, ws=None):
     shape = SdShape(B, T, Hkv, Hkv, D, bs, block_table.shape[1], nb, _dtype_code[k_pages.dtype],
                     T, 0.0)
     need = workspace_bytes(SD_CALL_COMMIT, shape)
-    ws = _WS.get(k_pages.device, need) if ws is None else ws
+    ws = _WS.get(k_pages.device, need, SD_CALL_COMMIT) if ws is None else ws
     _check("sd_kv_commit", lib().sd_kv_commit(
         ctypes.byref(shape), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(ctx_lens),
         _ptr(path), _ptr(path_len), _ptr(ws), ws.numel(), _stream(k_pages.device)))
@@ -190,7 +201,7 @@ def topk_blocks(q, k_pages, block_table, ctx_lens, k, sel=None, ws=None):
     if sel is None:
         sel = torch.empty((B, T, Hq, k), dtype=torch.int32, device=q.device)
     need = workspace_bytes(SD_CALL_TOPK, shape, k)
-    ws = _WS.get(q.device, need) if ws is None else ws
+    ws = _WS.get(q.device, need, SD_CALL_TOPK) if ws is None else ws
     _check("sd_topk_blocks", lib().sd_topk_blocks(
         ctypes.byref(shape), _ptr(q), _ptr(k_pages), _ptr(block_table), _ptr(ctx_lens), int(k),
         _ptr(sel), _ptr(ws), ws.numel(), _stream(q.device)))
@@ -198,10 +209,14 @@ def topk_blocks(q, k_pages, block_table, ctx_lens, k, sel=None, ws=None):
 
 
 def device_status(ws=None, device="cuda"):
-    """Reads and clears the sticky device error bits of a workspace."""
-    ws = _WS.get(device, 256) if ws is None else ws
-    bits = ctypes.c_uint32(0)
-    code = lib().sd_device_status(_ptr(ws), _stream(ws.device), ctypes.byref(bits))
-    if code not in (0, 7):
-        raise SdError("sd_device_status", code)
-    return bits.value
+    """Reads and clears the sticky device error bits of a workspace (default:
+    every workspace this binding allocated on the device), OR-ed together."""
+    bufs = _WS.all(device) if ws is None else [ws]
+    out = 0
+    for w in bufs:
+        bits = ctypes.c_uint32(0)
+        code = lib().sd_device_status(_ptr(w), _stream(w.device), ctypes.byref(bits))
+        if code not in (0, 7):
+            raise SdError("sd_device_status", code)
+        out |= bits.value
+    return out

@@ -157,15 +157,26 @@ __global__ void __launch_bounds__(256) attn_valu_kernel(AttnArgs a) {
 // WK: WQ waves cover different query rows and share every key; WK waves take
 // disjoint key slices of each tile and merge their softmax states at the end.
 //
-// Per tile of NK keys: K rows [NK][D] and V^T rows [D][NK] are loaded with
-// 16-byte global loads into registers (prefetched one tile ahead), stored to
-// one of two LDS buffers and read by every wave.  S^T = K Q^T is formed with
-// v_mfma_f32_16x16x32_bf16 with Q^T held in registers; the K rows fed to the
-// two 16-row halves of each 32-key group are interleaved so that the
-// accumulator layout of S^T is directly the B operand of O^T = V^T P^T.
-// Each lane therefore owns one query column, and the online-softmax scale is a
-// per-lane scalar; the row max needs two cross-lane steps.
-template <int D, int QW, int WQ, int WK, int KW>
+// Key tiles of NK keys stream through an S-stage LDS ring: each K row [D] and
+// each V^T row [NK] is brought in with 16-byte direct global-to-LDS loads
+// (global_load_lds_dwordx4), issued S - 1 tiles ahead and waited for with an
+// explicit vmcnt before the tile's barrier, so up to S - 1 tiles are in flight
+// while one is computed.  LDS rows are unpadded; the 16-byte chunk a lane
+// writes is chosen (XOR swizzle) so that the 16 rows read by one MFMA operand
+// fetch fall on distinct banks.  V^T chunks that cannot be copied whole (a
+// context or tree edge that is not 8-aligned) are assembled in registers.
+//
+// S^T = K Q^T is formed with v_mfma_f32_16x16x32_bf16 with Q^T held in
+// registers; the K rows fed to the two 16-row halves of each 32-key group are
+// interleaved so that the accumulator layout of S^T is directly the B operand
+// of O^T = V^T P^T.  Each lane therefore owns one query column, the
+// online-softmax scale is a per-lane scalar and the row max needs two
+// cross-lane steps.
+// Reference-max slack of the online softmax, in log2 units: probabilities are
+// formed relative to a running max that may lag the true one by up to this.
+constexpr float kLazy = 8.0f;
+
+template <int D, int QW, int WQ, int WK, int KW, int S>
 __global__ void __launch_bounds__(256, 1) attn_mfma_kernel(AttnArgs a) {
   constexpr int NK = KW * WK;
   constexpr int ROWS = WQ * QW;
@@ -173,23 +184,36 @@ __global__ void __launch_bounds__(256, 1) attn_mfma_kernel(AttnArgs a) {
   constexpr int DS = D / 32;
   constexpr int DB = D / 16;
   constexpr int KG = KW / 32;
-  constexpr int KSTR = D + 8;
-  constexpr int VSTR = NK + 8;
-  constexpr int KCH = D / 8;
-  constexpr int K_ITEMS = NK * KCH / 256;
-  constexpr int V_ITEMS = D * (NK / 8) / 256;
-  static_assert(K_ITEMS * 256 == NK * KCH && V_ITEMS * 256 == D * (NK / 8), "tile split");
+  constexpr int CK = D / 8;                      // 16-byte chunks per K row
+  constexpr int CV = NK / 8;                     // 16-byte chunks per V^T row
+  constexpr int K_BYTES = NK * D * 2;
+  constexpr int V_BYTES = D * NK * 2;
+  constexpr int K_OPS = K_BYTES / (256 * 16);    // DMA instructions per thread per tile
+  constexpr int V_OPS = V_BYTES / (256 * 16);
+  constexpr int OPS = K_OPS + V_OPS;
+  static_assert(K_OPS * 256 * 16 == K_BYTES && V_OPS * 256 * 16 == V_BYTES, "tile split");
   static_assert(WQ * WK == 4, "four wavefronts");
+  static_assert(S >= 2 && (S - 2) * OPS <= 63, "vmcnt range");
 
-  // K rows 16 apart fall on the same LDS banks with a 17-chunk stride; the
-  // 16-byte chunk index is XOR-ed with 4 on rows whose bit 4 is set.
-  auto kswz = [](int row) { return ((row >> 4) & 1) << 2; };
+  // Swizzles: chunk c of K row r sits at position c ^ kswz(r); chunk c of V^T
+  // row d at c ^ vswz(d).  (Rows one MFMA operand reads: 16 K rows
+  // {8a + 4h + b} of a 32-key group, or 16 consecutive V^T rows.)
+  auto kswz = [](int r) -> int {
+    return CK == 16 ? ((r & 3) | ((r >> 1) & 12)) : (((r >> 1) & 1) | (((r >> 3) & 3) << 1));
+  };
+  auto vswz = [](int d) -> int { return CV == 16 ? (d & 15) : ((d >> 1) & 7); };
+
   extern __shared__ __align__(16) unsigned char smem[];
-  bf16_bits* Ks = reinterpret_cast<bf16_bits*>(smem);
-  bf16_bits* Vs = Ks + 2 * NK * KSTR;
-  unsigned char* tflag = reinterpret_cast<unsigned char*>(Vs + 2 * D * VSTR);
-  uint32_t* ubits = reinterpret_cast<uint32_t*>(tflag + 128);
-  __shared__ int s_nU;
+  unsigned char* Kst = smem;                                 // [S][K_BYTES]
+  unsigned char* Vst = smem + S * K_BYTES;                   // [S][V_BYTES]
+  unsigned char* tflag = Vst + S * V_BYTES;                  // [128]
+  int* tlist = reinterpret_cast<int*>(tflag + 128);          // [128]
+  // element offset of (block, head g) for this split's context blocks / the tree blocks
+  long long* ctab = reinterpret_cast<long long*>(tlist + 128);
+  long long* ttab = ctab + a.ct_max;
+  uint64_t* ancL = reinterpret_cast<uint64_t*>(ttab + a.tt_max);
+  uint32_t* ubits = reinterpret_cast<uint32_t*>(ancL + a.anc_lds_words);
+  __shared__ int s_nU, s_err, s_ntree;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -213,6 +237,7 @@ __global__ void __launch_bounds__(256, 1) attn_mfma_kernel(AttnArgs a) {
   const int b = L / a.Hkv;
 
   const int T = a.T, G = a.G, M = a.M, bs = a.bs;
+  const int bsh = a.bs_shift, bsm = bs - 1;
   const bf16_bits* __restrict__ Kp = reinterpret_cast<const bf16_bits*>(a.k);
   const bf16_bits* __restrict__ Vp = reinterpret_cast<const bf16_bits*>(a.v);
   const int32_t* __restrict__ table = a.table + (size_t)b * a.max_blocks;
@@ -240,32 +265,35 @@ __global__ void __launch_bounds__(256, 1) attn_mfma_kernel(AttnArgs a) {
     }
   }
 
-  // ---- tree tiles touched by any row of this workgroup -------------------
+  // ---- ancestors of this workgroup's nodes; tree tiles any of them touch ---
   const int n_tt = (T + NK - 1) / NK;
+  const int r_hi = min(row0 + ROWS, M);
+  const int i_lo = row0 / G;
+  const int i_hi = row0 < r_hi ? (r_hi - 1) / G : i_lo - 1;
   if (tid < 128) tflag[tid] = 0;
+  if (tid == 0) s_err = 0;
   __syncthreads();
   {
-    const int r_hi = min(row0 + ROWS, M);
-    if (row0 < r_hi) {
-      const int i_lo = row0 / G, i_hi = (r_hi - 1) / G;
-      const int cnt = (i_hi - i_lo + 1) * a.W64;
-      for (int idx = tid; idx < cnt; idx += 256) {
-        const int i = i_lo + idx / a.W64, w = idx % a.W64;
-        if (a.anc[((size_t)bt * T + i) * a.W64 + w] != 0ull) tflag[(w * 64) / NK] = 1;
-      }
+    const int cnt = (i_hi - i_lo + 1) * a.W64;
+    for (int idx = tid; idx < cnt; idx += 256) {
+      const int i = i_lo + idx / a.W64, w = idx % a.W64;
+      const uint64_t word = a.anc[((size_t)bt * T + i) * a.W64 + w];
+      ancL[idx] = word;  // the plan sizes ancL for every node of the tile
+      if (word != 0ull) tflag[(w * 64) / NK] = 1;
     }
   }
+  int err = 0;
 
   // ---- sparse: union of the blocks selected by this workgroup's rows -----
-  const int nblk_ctx = cap_ok ? (ctx + bs - 1) / bs : 0;
+  const int nblk_ctx = cap_ok ? (ctx + bs - 1) >> bsh : 0;
   const int UW = (a.u_max + 31) >> 5;
   const int BW = (nblk_ctx + 31) >> 5;
   uint32_t* upre = ubits + ((a.max_blocks + 31) >> 5);
   int* U = reinterpret_cast<int*>(upre + ((a.max_blocks + 31) >> 5));
-  uint32_t* rowbits = reinterpret_cast<uint32_t*>(U + a.u_max);
+  int* Uphys = U + a.u_max;
+  uint32_t* rowbits = reinterpret_cast<uint32_t*>(Uphys + a.u_max);
   int nU = 0;
   if (sparse) {
-    const int r_hi = min(row0 + ROWS, M);
     for (int w = tid; w < BW; w += 256) ubits[w] = 0;
     for (int w = tid; w < ROWS * UW; w += 256) rowbits[w] = 0;
     __syncthreads();
@@ -278,7 +306,7 @@ __global__ void __launch_bounds__(256, 1) attn_mfma_kernel(AttnArgs a) {
         const int n = sr[e];
         if (n < 0) continue;
         if (n >= nblk_ctx || (e > 0 && sr[e - 1] >= n)) {
-          set_status(a.status, SD_ERR_SELECTION);
+          err |= SD_ERR_SELECTION;
           continue;
         }
         atomicOr(&ubits[n >> 5], 1u << (n & 31));
@@ -301,7 +329,15 @@ __global__ void __launch_bounds__(256, 1) attn_mfma_kernel(AttnArgs a) {
       while (bits) {
         const int bpos = __ffs(bits) - 1;
         bits &= bits - 1;
-        U[o++] = w * 32 + bpos;
+        const int n = w * 32 + bpos;
+        int phys = table[n];
+        if (phys < 0 || phys >= a.num_blocks) {
+          err |= SD_ERR_BLOCK;
+          phys = 0;
+        }
+        U[o] = n;
+        Uphys[o] = phys;
+        ++o;
       }
     }
     if (cap_ok) {
@@ -319,98 +355,140 @@ __global__ void __launch_bounds__(256, 1) attn_mfma_kernel(AttnArgs a) {
   }
   __syncthreads();
 
-  // ---- tile range of this split ------------------------------------------
-  const int nct = !cap_ok ? 0 : (sparse ? (nU * bs + NK - 1) / NK : (ctx + NK - 1) / NK);
+  // ---- tile range of this split, usable tiles ------------------------------
+  const int nct = !cap_ok ? 0 : (sparse ? ((nU << bsh) + NK - 1) / NK : (ctx + NK - 1) / NK);
   const int ntot = cap_ok ? nct + n_tt : 0;
   const int t_lo = split * a.tps;
   const int t_hi = min(t_lo + a.tps, ntot);
-  auto usable = [&](int t) { return t < nct || tflag[t - nct]; };
-  auto next_tile = [&](int t) {
-    ++t;
-    while (t < t_hi && !usable(t)) ++t;
-    return t;
-  };
+  const int n_ctx_here = max(0, min(t_hi, nct) - t_lo);
+  if (tid == 0) {
+    int n = 0;
+    for (int t = max(t_lo, nct); t < t_hi; ++t)
+      if (tflag[t - nct]) tlist[n++] = t;
+    s_ntree = n;
+  }
 
-  // Logical position of key k of tile t, or -1.
-  auto key_pos = [&](int t, int k) -> int {
+  // Physical block ids this split reads, staged once: dense context blocks
+  // [cb0, cb0 + ccount) and the blocks holding the tree slots [tb0, tb0 + tcount).
+  const int cb0 = (t_lo * NK) >> bsh;
+  const int ccount = (!sparse && n_ctx_here > 0)
+                         ? min((min(t_hi, nct) * NK - 1) >> bsh, (ctx - 1) >> bsh) - cb0 + 1 : 0;
+  const int tb0 = ctx >> bsh;
+  const int tcount = (cap_ok && t_hi > nct) ? ((ctx + T - 1) >> bsh) - tb0 + 1 : 0;
+  const long long blk_elems = (long long)a.Hkv * bs * D;
+  const long long head_off = (long long)g * bs * D;   // head g inside a K or a V block
+  for (int j = tid; j < ccount + tcount; j += 256) {
+    const int n = j < ccount ? cb0 + j : tb0 + (j - ccount);
+    int phys = table[n];
+    if (phys < 0 || phys >= a.num_blocks) {
+      err |= SD_ERR_BLOCK;
+      phys = 0;
+    }
+    const long long off = phys * blk_elems + head_off;
+    if (j < ccount) ctab[j] = off;
+    else ttab[j - ccount] = off;
+  }
+  if (err) atomicOr(&s_err, err);
+  __syncthreads();
+  const int nuse = n_ctx_here + s_ntree;
+  auto tile_at = [&](int k) { return k < n_ctx_here ? t_lo + k : tlist[k - n_ctx_here]; };
+
+  // Logical position of key k of tile t (< 0: none) and the element offset of
+  // its (block, head g).
+  auto key_at = [&](int t, int k, long long& boff) -> int {
     if (t < nct) {
       if (!sparse) {
         const int p = t * NK + k;
-        return p < ctx ? p : -1;
+        if (p >= ctx) return -1;
+        boff = ctab[(p >> bsh) - cb0];
+        return p;
       }
       const int vi = t * NK + k;
-      const int e = vi / bs;
+      const int e = vi >> bsh;
       if (e >= nU) return -1;
-      const int p = U[e] * bs + vi % bs;
-      return p < ctx ? p : -1;
+      const int p = (U[e] << bsh) + (vi & bsm);
+      if (p >= ctx) return -1;
+      boff = (long long)Uphys[e] * blk_elems + head_off;
+      return p;
     }
     const int j = (t - nct) * NK + k;
-    return j < T ? ctx + j : -1;
+    if (j >= T) return -1;
+    const int p = ctx + j;
+    boff = ttab[(p >> bsh) - tb0];
+    return p;
   };
-  auto block_of = [&](int pos) -> int {
-    const int blk = table[pos / bs];
-    if (blk < 0 || blk >= a.num_blocks) {
-      set_status(a.status, SD_ERR_BLOCK);
-      return -1;
-    }
-    return blk;
+  // Do the 8-key chunks of tile t copy whole (8-aligned, all valid or all not)?
+  auto v_clean = [&](int t) -> bool {
+    if ((ctx & 7) == 0) return t < nct || ((t - nct) * NK + NK <= T) || (T & 7) == 0;
+    return t < nct && !sparse && t * NK + NK <= ctx;
   };
+  const bf16_bits* zeros = reinterpret_cast<const bf16_bits*>(a.zeros);
 
-  uint4 kreg[K_ITEMS], vreg[V_ITEMS];
-  auto load_tile = [&](int t) {
+  // Per-thread DMA geometry (loop invariant).  K: DMA n of a tile writes slot
+  // s = lane + 64 (wave + 4 n), i.e. row s / CK, position s % CK, so it copies
+  // global chunk (s % CK) ^ kswz(row).  V^T: row s / CV, chunk (s % CV) ^ vswz.
+  int k_row[K_OPS], k_col[K_OPS], v_row[V_OPS], v_key[V_OPS];
 #pragma unroll
-    for (int n = 0; n < K_ITEMS; ++n) {
-      const int it = tid + 256 * n;
-      const int row = it / KCH, ch = it % KCH;
-      const int pos = key_pos(t, row);
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (pos >= 0) {
-        const int blk = block_of(pos);
-        if (blk >= 0)
-          v = *reinterpret_cast<const uint4*>(Kp + (((size_t)blk * a.Hkv + g) * bs + pos % bs) * D +
-                                              ch * 8);
+  for (int n = 0; n < K_OPS; ++n) {
+    const int sl = lane + 64 * (wave + 4 * n);
+    k_row[n] = sl / CK;
+    k_col[n] = ((sl % CK) ^ kswz(sl / CK)) * 8;
+  }
+#pragma unroll
+  for (int n = 0; n < V_OPS; ++n) {
+    const int sl = lane + 64 * (wave + 4 * n);
+    v_row[n] = sl / CV;
+    v_key[n] = ((sl % CV) ^ vswz(sl / CV)) * 8;
+  }
+
+  // Issue the loads of tile t into ring slot `slot`.
+  auto issue = [&](int t, int slot) {
+    unsigned char* kst = Kst + slot * K_BYTES;
+    unsigned char* vst = Vst + slot * V_BYTES;
+    if (t < nct && !sparse && t * NK + NK <= ctx) {
+      // whole dense context tile: block bases from the staged table
+#pragma unroll
+      for (int n = 0; n < K_OPS; ++n) {
+        const int p = t * NK + k_row[n];
+        const bf16_bits* src = Kp + ctab[(p >> bsh) - cb0] + (long long)((p & bsm) * D + k_col[n]);
+        __builtin_amdgcn_global_load_lds(src, kst + (wave + 4 * n) * 1024, 16, 0, 0);
       }
-      kreg[n] = v;
+#pragma unroll
+      for (int n = 0; n < V_OPS; ++n) {
+        const int p = t * NK + v_key[n];
+        const bf16_bits* src = Vp + ctab[(p >> bsh) - cb0] + (long long)(v_row[n] * bs + (p & bsm));
+        __builtin_amdgcn_global_load_lds(src, vst + (wave + 4 * n) * 1024, 16, 0, 0);
+      }
+      return;
     }
 #pragma unroll
-    for (int n = 0; n < V_ITEMS; ++n) {
-      const int it = tid + 256 * n;
-      const int d = it / (NK / 8), kc = it % (NK / 8);
-      const int p0 = key_pos(t, kc * 8);
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (p0 >= 0 && (p0 & 7) == 0 && key_pos(t, kc * 8 + 7) == p0 + 7) {
-        const int blk = block_of(p0);
-        if (blk >= 0)
-          v = *reinterpret_cast<const uint4*>(Vp + (((size_t)blk * a.Hkv + g) * D + d) * bs + p0 % bs);
-      } else {
+    for (int n = 0; n < K_OPS; ++n) {
+      long long boff = 0;
+      const int p = key_at(t, k_row[n], boff);
+      const bf16_bits* src = p >= 0 ? Kp + boff + (long long)((p & bsm) * D + k_col[n]) : zeros;
+      __builtin_amdgcn_global_load_lds(src, kst + (wave + 4 * n) * 1024, 16, 0, 0);
+    }
+    if (v_clean(t)) {
+#pragma unroll
+      for (int n = 0; n < V_OPS; ++n) {
+        long long boff = 0;
+        const int p = key_at(t, v_key[n], boff);
+        const bf16_bits* src = p >= 0 ? Vp + boff + (long long)(v_row[n] * bs + (p & bsm)) : zeros;
+        __builtin_amdgcn_global_load_lds(src, vst + (wave + 4 * n) * 1024, 16, 0, 0);
+      }
+    } else {
+      // assemble each 8-key chunk element by element (zeros past the edge)
+#pragma unroll
+      for (int n = 0; n < V_OPS; ++n) {
         uint32_t w[4] = {0, 0, 0, 0};
         for (int e = 0; e < 8; ++e) {
-          const int p = key_pos(t, kc * 8 + e);
-          if (p < 0) continue;
-          const int blk = block_of(p);
-          if (blk < 0) continue;
-          const uint32_t x = Vp[(((size_t)blk * a.Hkv + g) * D + d) * bs + p % bs];
-          w[e >> 1] |= x << (16 * (e & 1));
+          long long boff = 0;
+          const int p = key_at(t, v_key[n] + e, boff);
+          if (p >= 0) w[e >> 1] |= (uint32_t)Vp[boff + v_row[n] * bs + (p & bsm)] << (16 * (e & 1));
         }
-        v = make_uint4(w[0], w[1], w[2], w[3]);
+        const int sl = lane + 64 * (wave + 4 * n);
+        *reinterpret_cast<uint4*>(vst + sl * 16) = make_uint4(w[0], w[1], w[2], w[3]);
       }
-      vreg[n] = v;
-    }
-  };
-  auto store_tile = [&](int buf) {
-    bf16_bits* Kt = Ks + buf * NK * KSTR;
-    bf16_bits* Vt = Vs + buf * D * VSTR;
-#pragma unroll
-    for (int n = 0; n < K_ITEMS; ++n) {
-      const int it = tid + 256 * n;
-      const int row = it / KCH, ch = it % KCH;
-      *reinterpret_cast<uint4*>(Kt + row * KSTR + ((ch ^ kswz(row)) * 8)) = kreg[n];
-    }
-#pragma unroll
-    for (int n = 0; n < V_ITEMS; ++n) {
-      const int it = tid + 256 * n;
-      const int d = it / (NK / 8), kc = it % (NK / 8);
-      *reinterpret_cast<uint4*>(Vt + d * VSTR + kc * 8) = vreg[n];
     }
   };
 
@@ -435,9 +513,9 @@ __global__ void __launch_bounds__(256, 1) attn_mfma_kernel(AttnArgs a) {
   }
   const int kbase = wk * KW;
 
-  auto compute_tile = [&](int buf, int t) {
-    const bf16_bits* Kt = Ks + buf * NK * KSTR;
-    const bf16_bits* Vt = Vs + buf * D * VSTR;
+  auto compute_tile = [&](int slot, int t) {
+    const unsigned char* Kt = Kst + slot * K_BYTES;
+    const unsigned char* Vt = Vst + slot * V_BYTES;
     f32x4 s[QB][2 * KG];
 #pragma unroll
     for (int kg = 0; kg < KG; ++kg) {
@@ -448,8 +526,8 @@ __global__ void __launch_bounds__(256, 1) attn_mfma_kernel(AttnArgs a) {
         for (int qb = 0; qb < QB; ++qb) s[qb][2 * kg + half] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ds = 0; ds < DS; ++ds) {
-          const bf16x8 ka =
-              *reinterpret_cast<const bf16x8*>(Kt + key * KSTR + (((ds * 4 + lg) ^ kswz(key)) * 8));
+          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(
+              Kt + key * (D * 2) + (((ds * 4 + lg) ^ kswz(key)) * 16));
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb)
             s[qb][2 * kg + half] =
@@ -473,11 +551,11 @@ __global__ void __launch_bounds__(256, 1) attn_mfma_kernel(AttnArgs a) {
               bits = p >= ctx ? 0u : (p + 8 <= ctx ? 0xFFu : ((1u << (ctx - p)) - 1u));
             } else {
               const int vi = t * NK + k0;
-              const int e = vi / bs;
+              const int e = vi >> bsh;
               bits = 0u;
               if (e < nU && node[qb] >= 0 &&
                   ((rowbits[rloc[qb] * UW + (e >> 5)] >> (e & 31)) & 1u)) {
-                const int p = U[e] * bs + vi % bs;
+                const int p = (U[e] << bsh) + (vi & bsm);
                 bits = p >= ctx ? 0u : (p + 8 <= ctx ? 0xFFu : ((1u << (ctx - p)) - 1u));
               }
             }
@@ -485,7 +563,7 @@ __global__ void __launch_bounds__(256, 1) attn_mfma_kernel(AttnArgs a) {
             const int j0 = (t - nct) * NK + k0;
             bits = 0u;
             if (node[qb] >= 0 && j0 < T) {
-              const uint64_t word = a.anc[((size_t)bt * T + node[qb]) * a.W64 + (j0 >> 6)];
+              const uint64_t word = ancL[(node[qb] - i_lo) * a.W64 + (j0 >> 6)];
               bits = (uint32_t)(word >> (j0 & 63)) & 0xFFu;
             }
           }
@@ -493,27 +571,42 @@ __global__ void __launch_bounds__(256, 1) attn_mfma_kernel(AttnArgs a) {
         vis[qb][kg] = bits;
       }
     }
-    // online softmax, P^T operands
+    // online softmax on raw scores; scale folded into the exponent.  The
+    // reference max m_run is only raised when a score exceeds it by more than
+    // 2^kLazy, so p <= 2^kLazy and the accumulators are rarely rescaled.
     bf16x8 pf[QB][KG];
+    const float c = a.scale_log2;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      float mx = -1e30f;
+      float mx = -INFINITY;
+      if (!full_ctx) {
+#pragma unroll
+        for (int kg = 0; kg < KG; ++kg)
+#pragma unroll
+          for (int half = 0; half < 2; ++half)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              if (!((vis[qb][kg] >> (4 * half + j)) & 1u)) s[qb][2 * kg + half][j] = -INFINITY;
+      }
 #pragma unroll
       for (int kg = 0; kg < KG; ++kg)
 #pragma unroll
         for (int half = 0; half < 2; ++half)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            float v = s[qb][2 * kg + half][j] * a.scale_log2;
-            if (!((vis[qb][kg] >> (4 * half + j)) & 1u)) v = -1e30f;
-            s[qb][2 * kg + half][j] = v;
-            mx = fmaxf(mx, v);
-          }
+          for (int j = 0; j < 4; ++j) mx = fmaxf(mx, s[qb][2 * kg + half][j]);
       mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mn = fmaxf(m_run[qb], mx);
-      const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - mn);
-      m_run[qb] = mn;
+      const float ms = mx * c;
+      const bool raise = ms > m_run[qb] + kLazy;
+      if (__builtin_amdgcn_ballot_w64(raise)) {
+        const float mn = raise ? ms : m_run[qb];
+        const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - mn);
+        m_run[qb] = mn;
+        l_run[qb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) o[qb][db] *= alpha;
+      }
+      const float nm = -m_run[qb];
       float lsum = 0.f;
 #pragma unroll
       for (int kg = 0; kg < KG; ++kg) {
@@ -521,26 +614,27 @@ __global__ void __launch_bounds__(256, 1) attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
         for (int half = 0; half < 2; ++half)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const float v = s[qb][2 * kg + half][j];
-            const float p = v > -1e29f ? __builtin_amdgcn_exp2f(v - mn) : 0.f;
-            const bf16_bits pb = f32_to_bf16(p);
-            lsum += bf16_to_f32(pb);
-            pk[4 * half + j] = __builtin_bit_cast(__bf16, pb);
+          for (int j = 0; j < 4; j += 2) {
+            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][2 * kg + half][j], c, nm));
+            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][2 * kg + half][j + 1], c, nm));
+            lsum += p0 + p1;
+            const bf16x2 pp = __builtin_convertvector((f32x2){p0, p1}, bf16x2);
+            pk[4 * half + j] = pp[0];
+            pk[4 * half + j + 1] = pp[1];
           }
         pf[qb][kg] = pk;
       }
-      l_run[qb] = l_run[qb] * alpha + lsum;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) o[qb][db] *= alpha;
+      l_run[qb] += lsum;
     }
     // O^T += V^T P^T
 #pragma unroll
     for (int kg = 0; kg < KG; ++kg) {
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
+        const int d = db * 16 + l16;
+        const int c = (kbase + 32 * kg + 8 * lg) >> 3;
         const bf16x8 va =
-            *reinterpret_cast<const bf16x8*>(Vt + (db * 16 + l16) * VSTR + kbase + 32 * kg + 8 * lg);
+            *reinterpret_cast<const bf16x8*>(Vt + d * (NK * 2) + ((c ^ vswz(d)) * 16));
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
           o[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pf[qb][kg], o[qb][db], 0, 0, 0);
@@ -548,28 +642,35 @@ __global__ void __launch_bounds__(256, 1) attn_mfma_kernel(AttnArgs a) {
     }
   };
 
-  // ---- main loop: double-buffered LDS, register prefetch one tile ahead ---
-  int t = t_lo;
-  while (t < t_hi && !usable(t)) ++t;
-  if (t < t_hi) {
-    load_tile(t);
-    store_tile(0);
-  }
-  __syncthreads();
-  int tn = t < t_hi ? next_tile(t) : t_hi;
-  if (tn < t_hi) load_tile(tn);
-  int buf = 0;
-  while (t < t_hi) {
-    compute_tile(buf, t);
-    if (tn < t_hi) store_tile(buf ^ 1);
-    __syncthreads();
-    t = tn;
-    buf ^= 1;
-    if (t < t_hi) {
-      tn = next_tile(t);
-      if (tn < t_hi) load_tile(tn);
+  // ---- main loop: S-stage ring, loads issued S - 1 tiles ahead --------------
+  // Drain the set-up loads so that inside the loop the only vector-memory
+  // operations in flight are the ring's; each tile is then waited for with
+  // vmcnt(tiles issued after it * OPS).
+  __builtin_amdgcn_s_waitcnt(0);
+#pragma unroll
+  for (int k = 0; k < S - 1; ++k)
+    if (k < nuse) issue(tile_at(k), k);
+  for (int k = 0; k < nuse; ++k) {
+    const int ahead = min(S - 2, nuse - 1 - k);
+    if constexpr (S >= 4) {
+      if (ahead >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * OPS));
+      else if (ahead == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(OPS));
+      else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    } else if constexpr (S == 3) {
+      if (ahead >= 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(OPS));
+      else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    } else {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     }
+    __builtin_amdgcn_s_waitcnt(lgkmcnt_imm(0));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (k + S - 1 < nuse) issue(tile_at(k + S - 1), (k + S - 1) % S);
+    compute_tile(k % S, tile_at(k));
   }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
 
   // ---- finish: per-column sums, merge key-sliced waves, write -------------
 #pragma unroll
@@ -578,7 +679,6 @@ __global__ void __launch_bounds__(256, 1) attn_mfma_kernel(AttnArgs a) {
     l_run[qb] += __shfl_xor(l_run[qb], 32);
   }
   if constexpr (WK > 1) {
-    __syncthreads();
     float* xm = reinterpret_cast<float*>(smem);  // [4][QW]
     float* xl = xm + 4 * QW;                     // [4][QW]
     float* xo = xl + 4 * QW;                     // [4][QW][D]
@@ -647,7 +747,10 @@ __global__ void __launch_bounds__(256, 1) attn_mfma_kernel(AttnArgs a) {
       }
     }
   }
-  if (!cap_ok && tid == 0 && split == 0 && qtile == 0) set_status(a.status, SD_ERR_CAPACITY);
+  if (tid == 0) {
+    if (!cap_ok && split == 0 && qtile == 0) set_status(a.status, SD_ERR_CAPACITY);
+    if (s_err) set_status(a.status, (uint32_t)s_err);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -701,9 +804,9 @@ hipError_t launch_attn_valu(const AttnArgs& a, bool f32, hipStream_t st) {
   return a.D == 64 ? launch_valu_d<64>(a, f32, st) : launch_valu_d<128>(a, f32, st);
 }
 
-template <int D, int QW, int WQ, int WK, int KW>
+template <int D, int QW, int WQ, int WK, int KW, int S>
 static hipError_t launch_mfma_cfg(const AttnArgs& a, size_t lds, hipStream_t st) {
-  auto fn = attn_mfma_kernel<D, QW, WQ, WK, KW>;
+  auto fn = attn_mfma_kernel<D, QW, WQ, WK, KW, S>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
@@ -714,9 +817,14 @@ static hipError_t launch_mfma_cfg(const AttnArgs& a, size_t lds, hipStream_t st)
 
 template <int D>
 static hipError_t launch_mfma_d(const AttnArgs& a, const AttnPlan& p, hipStream_t st) {
-  if (p.WQ == 1) return launch_mfma_cfg<D, 32, 1, 4, 32>(a, p.lds_bytes, st);
-  if (p.WQ == 2) return launch_mfma_cfg<D, 32, 2, 2, 32>(a, p.lds_bytes, st);
-  return launch_mfma_cfg<D, 32, 4, 1, 64>(a, p.lds_bytes, st);
+  if (p.WQ == 1) return launch_mfma_cfg<D, 32, 1, 4, 32, 2>(a, p.lds_bytes, st);
+  if (p.WQ == 2) {
+    if (p.stages == 4) return launch_mfma_cfg<D, 32, 2, 2, 32, 4>(a, p.lds_bytes, st);
+    return launch_mfma_cfg<D, 32, 2, 2, 32, 2>(a, p.lds_bytes, st);
+  }
+  if (p.stages == 4) return launch_mfma_cfg<D, 32, 4, 1, 64, 4>(a, p.lds_bytes, st);
+  if (p.stages == 3) return launch_mfma_cfg<D, 32, 4, 1, 64, 3>(a, p.lds_bytes, st);
+  return launch_mfma_cfg<D, 32, 4, 1, 64, 2>(a, p.lds_bytes, st);
 }
 
 hipError_t launch_attn_mfma(const AttnArgs& a, const AttnPlan& p, hipStream_t st) {

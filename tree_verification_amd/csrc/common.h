@@ -11,10 +11,15 @@ namespace sdtree {
 typedef uint16_t bf16_bits;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // Workspace header: the sticky status word and small counters live in the
 // first 256 bytes; call-specific regions follow.
 constexpr size_t kWsHeader = 256;
+// 64 bytes inside the header that no kernel writes: a zero source for loads
+// of keys that do not exist.
+constexpr size_t kWsZeros = 128;
 
 __device__ __forceinline__ float bf16_to_f32(bf16_bits b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
@@ -26,6 +31,11 @@ __device__ __forceinline__ bf16_bits f32_to_bf16(float f) {
   u += 0x7FFFu + ((u >> 16) & 1u);
   return static_cast<bf16_bits>(u >> 16);
 }
+
+// s_waitcnt immediates (gfx9 encoding): wait until at most n vector-memory /
+// n LDS-or-scalar operations are outstanding, leaving the other counters free.
+constexpr unsigned vmcnt_imm(unsigned n) { return (n & 15u) | ((n >> 4) << 14) | (7u << 4) | (15u << 8); }
+constexpr unsigned lgkmcnt_imm(unsigned n) { return 15u | (3u << 14) | (7u << 4) | ((n & 15u) << 8); }
 
 __device__ __forceinline__ void set_status(uint32_t* status, uint32_t bit) {
   atomicOr(status, bit);
@@ -60,6 +70,9 @@ struct AttnPlan {
   int W64;              // 64-bit ancestor words per node
   int T_tree;           // number of distinct trees (1 or B)
   int u_max;            // sparse: max distinct blocks per workgroup
+  int ct_max, tt_max;   // LDS block-id table sizes (context tiles of one split, tree slots)
+  int stages;           // LDS ring depth
+  int anc_lds_words;
   size_t lds_bytes;
   size_t anc_off, part_o_off, part_ml_off, total;
 };
@@ -81,7 +94,15 @@ struct AttnArgs {
   int B, T, Hq, Hkv, G, M, D, bs, max_blocks, num_blocks, tree_stride;
   float scale_log2;
   int n_qtiles, n_splits, tps, W64, u_max;
+  int bs_shift;         // log2(bs)
+  int ct_max, tt_max;   // LDS entries for context / tree block ids
+  int anc_lds_words;    // ancestor words the kernel may stage in LDS
+  const void* zeros;    // >= 16 zero bytes in device memory
 };
+
+// Per-sequence synchronisation scratch of the acceptance walk: barrier
+// counter, exit counter, a broadcast slot, then [2][P][2] float64 partials.
+constexpr size_t kAccSeqBytes = 1024;
 
 struct AcceptArgs {
   const void* logits;
@@ -96,7 +117,11 @@ struct AcceptArgs {
   int32_t* path_len;
   int32_t* bonus;
   uint32_t* status;
+  unsigned char* sync;  // B * kAccSeqBytes, zero before the first call (P > 1 only)
+  int P, SL, NC;        // workgroups per sequence, tokens per workgroup, 2048-token chunks
 };
+
+int accept_wgs(int B, int V);
 
 struct CommitArgs {
   void* k;

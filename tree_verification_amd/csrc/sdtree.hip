@@ -24,7 +24,7 @@ static sd_status check_shape(const sd_shape* s) {
   if (s->tree_stride != 0 && s->tree_stride != s->T) return SD_BAD_SHAPE;
   if (s->dtype != SD_F32 && s->dtype != SD_BF16) return SD_BAD_DTYPE;
   if (s->D != 64 && s->D != 128) return SD_UNSUPPORTED;
-  if (s->bs % 8 != 0) return SD_UNSUPPORTED;
+  if (s->bs < 8 || (s->bs & (s->bs - 1)) != 0) return SD_UNSUPPORTED;
   if (s->T > kMaxT) return SD_UNSUPPORTED;
   if ((long long)s->max_blocks * s->bs > (1ll << 30)) return SD_UNSUPPORTED;
   if ((long long)s->num_blocks * s->Hkv * s->bs * s->D > (1ll << 40)) return SD_UNSUPPORTED;
@@ -73,19 +73,45 @@ static AttnPlan plan_attn(const sd_shape* s, int ksel, bool sparse) {
   }
   const int ntiles = p.n_ct_max + p.n_tt;
   const long long base = (long long)s->B * s->Hkv * p.n_qtiles;
-  // Aim for about 2 workgroups per CU on 256 CUs, with at least 8 tiles each.
-  const long long want = 512;
+  // At least one workgroup per CU (256 CUs) when the context allows, with at
+  // least 8 tiles per split, and at most 2048 context block ids per split.
+  const long long want = 256;
   int splits = (int)std::max<long long>(1, (want + base - 1) / base);
   splits = std::min(splits, std::max(1, ntiles / 8));
+  const int per_tile = std::max(1, p.NK / s->bs);
+  splits = std::max(splits, (ntiles * per_tile + 2047) / 2048);
   p.tps = (ntiles + splits - 1) / splits;
   p.n_splits = (ntiles + p.tps - 1) / p.tps;
-  const size_t tiles = (size_t)2 * p.NK * (p.D + 8) * 2 + (size_t)2 * p.D * (p.NK + 8) * 2;
-  const size_t merge = p.WK > 1 ? (size_t)4 * (p.QW * p.D + 2 * p.QW) * 4 : 0;
-  size_t lds = std::max(tiles, merge) + 128;
+  p.ct_max = (int)(((long long)p.tps * p.NK + s->bs - 1) / s->bs) + 2;
+  p.tt_max = (s->T + s->bs - 1) / s->bs + 2;
+  // LDS: the K / V^T ring, tree-tile flags and list, block-id tables, staged
+  // ancestor words, sparse tables.  The key-slice merge reuses the ring.
+  const size_t stage = (size_t)p.NK * p.D * 2 * 2;
+  const int nnodes = (p.rows + G - 1) / G + 1;
+  const size_t anc_need = (size_t)nnodes * p.W64;
+  size_t extras = 128 + 4 * 128 + 8 * (size_t)(p.ct_max + p.tt_max);
   if (sparse) {
     const size_t bw = (size_t)(s->max_blocks + 31) / 32;
-    lds += 4 * bw * 2 + 4 * (size_t)p.u_max + 4 * (size_t)p.rows * ((p.u_max + 31) / 32);
+    extras += 4 * bw * 2 + 8 * (size_t)p.u_max + 4 * (size_t)p.rows * ((p.u_max + 31) / 32);
   }
+  p.anc_lds_words = (int)anc_need;
+  extras += 8 * anc_need;
+  // deepest ring that fits: 4 or 3 stages for the wide tile, 4 or 2 for the
+  // middle one, 2 for the key-sliced one
+  const int cand[3] = {4, 3, 2};
+  p.stages = 0;
+  for (int c : cand) {
+    if (p.WQ == 1 && c != 2) continue;
+    if (p.WQ == 2 && c == 3) continue;
+    const size_t merge = p.WK > 1 ? (size_t)4 * (p.QW * p.D + 2 * p.QW) * 4 : 0;
+    if (std::max(c * stage, merge) + extras <= kLdsLimit) {
+      p.stages = c;
+      break;
+    }
+  }
+  if (p.stages == 0) p.stages = 2;   // reported as SD_UNSUPPORTED by the LDS check
+  const size_t merge = p.WK > 1 ? (size_t)4 * (p.QW * p.D + 2 * p.QW) * 4 : 0;
+  size_t lds = std::max(p.stages * stage, merge) + extras;
   p.lds_bytes = align_up(lds, 16);
   const size_t nrows = (size_t)s->B * s->T * s->Hq;
   if (p.n_splits > 1) {
@@ -105,6 +131,13 @@ static size_t topk_ws(const sd_shape* s, size_t* means_off, size_t* scores_off) 
   if (means_off) *means_off = mo;
   if (scores_off) *scores_off = so;
   return align_up(so + (size_t)s->B * s->T * s->Hq * nbmax * 4, 256);
+}
+
+// Acceptance scratch: the status header, plus per-sequence barrier state when
+// a sequence is split over several workgroups.
+static size_t accept_ws(const sd_accept_shape* s) {
+  const int P = accept_wgs(s->B, s->V);
+  return kWsHeader + (P > 1 ? (size_t)s->B * kAccSeqBytes : 0);
 }
 
 static sd_status hip_status(hipError_t e) { return e == hipSuccess ? SD_OK : SD_HIP_ERROR; }
@@ -140,7 +173,7 @@ size_t sd_workspace_bytes(int32_t call_id, const void* shape, int32_t extra) {
   if (call_id == SD_CALL_ACCEPT) {
     const sd_accept_shape* s = static_cast<const sd_accept_shape*>(shape);
     if (s->B < 1 || s->T < 1 || s->V < 1) return 0;
-    return kWsHeader;
+    return accept_ws(s);
   }
   if (call_id == SD_CALL_COMMIT) {
     const sd_shape* s = static_cast<const sd_shape*>(shape);
@@ -191,6 +224,10 @@ sd_status sd_tree_verify_attn(const sd_shape* shape, const void* q, const void* 
   const float scale = s.scale > 0.f ? s.scale : 1.f / sqrtf((float)s.D);
   a.scale_log2 = scale * 1.4426950408889634f;
   a.n_qtiles = p.n_qtiles; a.n_splits = p.n_splits; a.tps = p.tps; a.W64 = p.W64; a.u_max = p.u_max;
+  a.bs_shift = __builtin_ctz((unsigned)s.bs);
+  a.ct_max = p.ct_max; a.tt_max = p.tt_max;
+  a.anc_lds_words = p.anc_lds_words;
+  a.zeros = w + kWsZeros;
   if (p.variant == 0) return hip_status(launch_attn_valu(a, s.dtype == SD_F32, hs));
   return hip_status(launch_attn_mfma(a, p, hs));
 }
@@ -210,7 +247,7 @@ sd_status sd_accept(const sd_accept_shape* shape, const void* target_logits,
   if (!target_logits || !tree_parent || !tree_token || !path || !path_len || !bonus || !ws)
     return SD_INVALID_ARG;
   if (temperature > 0.f && !uniforms) return SD_INVALID_ARG;
-  if (ws_bytes < kWsHeader) return SD_CAPACITY;
+  if (ws_bytes < accept_ws(&s)) return SD_CAPACITY;
   AcceptArgs a;
   memset(&a, 0, sizeof(a));
   a.logits = target_logits;
@@ -220,6 +257,10 @@ sd_status sd_accept(const sd_accept_shape* shape, const void* target_logits,
   a.B = s.B; a.T = s.T; a.V = s.V; a.tree_stride = s.tree_stride;
   a.path = path; a.path_len = path_len; a.bonus = bonus;
   a.status = static_cast<uint32_t*>(ws);
+  a.sync = static_cast<unsigned char*>(ws) + kWsHeader;
+  a.P = accept_wgs(s.B, s.V);
+  a.SL = (((s.V + a.P - 1) / a.P) + 7) / 8 * 8;
+  a.NC = (a.SL + 2047) / 2048;
   return hip_status(launch_accept(a, static_cast<hipStream_t>(stream)));
 }
 
