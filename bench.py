@@ -1,0 +1,329 @@
+"""Benchmark of the tree-verification pass on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload llama3_8b_tree64]
+
+One step is one verification pass over one batch: tree-masked attention
+(sd_tree_verify_attn, which also builds the ancestor masks), the acceptance
+walk (sd_accept) and the commit of the accepted paths (sd_kv_commit); the
+sparse workload first selects blocks (sd_topk_blocks) and attends sparsely.
+The context lengths are restored after each commit (a 4-byte-per-sequence
+device copy inside the step) so every step does the same work.
+
+Prints one JSON line: verified tree tokens/s (B * T per step) over the timed
+steps, the attention call against the HBM or MFMA roofline (algorithmic
+bytes or FLOPs per call / event-timed call duration), and the CPU oracle
+timed on a bounded sample of the same workload.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+FP32_PEAK_TFLOPS = 157.3       # MI355X fp32 vector
+METRIC = "verified tree tokens/s + achieved HBM GB/s (or MFMA %) of tree-verify, 1 GPU"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama3_8b_tree64")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="approximate CPU time budget of the oracle sample")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="skip the attention roofline of the 2048-node tree workload")
+    return ap.parse_args()
+
+
+def ancestor_sizes(parent):
+    """|anc*(i)| for every node (depth + 1)."""
+    T = len(parent)
+    depth = np.zeros(T, dtype=np.int64)
+    for i in range(1, T):
+        depth[i] = depth[parent[i]] + 1 if parent[i] >= 0 else 0
+    return depth + 1
+
+
+def attention_cost(cfg, x, sel=None):
+    """Algorithmic bytes and FLOPs of one attention call.
+    Bytes: every context K/V row read once (the selected blocks' rows when
+    sparse, deduplicated per KV group), the tree slots' K/V, q and out.
+    FLOPs: 4 * D per (query head, visible key) pair."""
+    e = 4 if cfg.dtype == "f32" else 2
+    B, T, Hq, Hkv, D = cfg.B, cfg.T, cfg.Hq, cfg.Hkv, cfg.D
+    ctx = x.ctx_lens.astype(np.int64)
+    pairs = 0
+    kv_rows = 0
+    for b in range(B):
+        par = x.tree_parent[0] if x.tree_parent.shape[0] == 1 else x.tree_parent[b]
+        anc = int(ancestor_sizes(par).sum())
+        if sel is None:
+            pairs += Hq * (T * int(ctx[b]) + anc)
+            kv_rows += Hkv * (int(ctx[b]) + T)
+        else:
+            G = Hq // Hkv
+            for g in range(Hkv):
+                blocks = np.unique(sel[b, :, g * G:(g + 1) * G].ravel())
+                blocks = blocks[blocks >= 0]
+                valid = np.minimum(cfg.bs, ctx[b] - blocks * cfg.bs).sum()
+                kv_rows += int(valid) + T
+            for i in range(T):
+                for h in range(Hq):
+                    s = sel[b, i, h]
+                    s = s[s >= 0]
+                    pairs += int(np.minimum(cfg.bs, ctx[b] - s * cfg.bs).sum())
+            pairs += Hq * anc
+    bytes_ = kv_rows * D * e * 2 + 2 * B * T * Hq * D * e
+    flops = 4 * D * pairs
+    return bytes_, flops
+
+
+def roofline_for(cfg, bytes_, flops, seconds):
+    ai = flops / bytes_
+    ridge = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if cfg.dtype == "f32":
+        ridge = FP32_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if ai < ridge:
+        achieved = bytes_ / seconds / 1e9
+        return {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    peak = FP32_PEAK_TFLOPS if cfg.dtype == "f32" else BF16_PEAK_TFLOPS
+    achieved = flops / seconds / 1e12
+    return {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4)}
+
+
+def traffic_for(kernel_key, workload):
+    """HBM bytes per attention call from committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE passes, if they were taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s_%s.json" % (kernel_key, workload))
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    src = open(os.path.join(ROOT, "tree_verification_amd", "csrc", "attn.hip"), "rb").read()
+    if rec.get("attn_hip_sha256") != hashlib.sha256(src).hexdigest():
+        return None
+    return rec.get("bytes_per_call")
+
+
+class Workload:
+    def __init__(self, name):
+        import torch
+        import tree_verification_amd as tva
+        from synth import CONFIGS, make_inputs
+        self.tva = tva
+        self.torch = torch
+        self.cfg = cfg = CONFIGS[name]
+        self.x = x = make_inputs(cfg)
+
+        def dev(a):
+            a = np.ascontiguousarray(a)
+            if a.dtype == np.uint16:
+                return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+            return torch.from_numpy(a).cuda()
+        self.q, self.k, self.v = dev(x.q), dev(x.k_pages), dev(x.v_pages)
+        self.table, self.ctx = dev(x.block_table), dev(x.ctx_lens)
+        self.ctx0 = self.ctx.clone()
+        self.parent, self.token = dev(x.tree_parent), dev(x.tree_token)
+        self.logits, self.unif = dev(x.target_logits), dev(x.uniforms)
+        self.draft = dev(x.draft_probs) if cfg.mode == "mss" else None
+        self.tau = 0.0 if cfg.mode == "greedy" else cfg.temperature
+        self.out = torch.empty_like(self.q)
+        B, T = cfg.B, cfg.T
+        self.path = torch.empty((B, T), dtype=torch.int32, device="cuda")
+        self.plen = torch.empty(B, dtype=torch.int32, device="cuda")
+        self.bonus = torch.empty(B, dtype=torch.int32, device="cuda")
+        self.sel = None
+        if cfg.topk:
+            self.sel = torch.empty((B, T, cfg.Hq, cfg.topk), dtype=torch.int32, device="cuda")
+
+    def attention(self):
+        self.tva.tree_verify_attn(self.q, self.k, self.v, self.table, self.ctx, self.parent,
+                                  out=self.out, sel_blocks=self.sel)
+
+    def step(self, ev=None):
+        tva = self.tva
+        if self.sel is not None:
+            tva.topk_blocks(self.q, self.k, self.table, self.ctx, self.cfg.topk, sel=self.sel)
+        if ev is not None:
+            ev[0].record()
+        self.attention()
+        if ev is not None:
+            ev[1].record()
+        tva.accept(self.logits, self.draft, self.parent, self.token, self.unif, self.tau,
+                   path=self.path, path_len=self.plen, bonus=self.bonus)
+        tva.kv_commit(self.k, self.v, self.table, self.ctx, self.path, self.plen)
+        self.ctx.copy_(self.ctx0)
+
+
+def time_calls(w, reps=10):
+    """Per-call device times (event-timed loops of each call alone)."""
+    torch = w.torch
+    tva = w.tva
+    res = {}
+
+    def loop(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e3
+    res["attention_us"] = loop(w.attention)
+    res["accept_us"] = loop(lambda: tva.accept(w.logits, w.draft, w.parent, w.token, w.unif, w.tau,
+                                               path=w.path, path_len=w.plen, bonus=w.bonus))
+
+    def commit():
+        tva.kv_commit(w.k, w.v, w.table, w.ctx, w.path, w.plen)
+        w.ctx.copy_(w.ctx0)
+    res["commit_plus_restore_us"] = loop(commit)
+    if w.sel is not None:
+        res["topk_us"] = loop(lambda: tva.topk_blocks(w.q, w.k, w.table, w.ctx, w.cfg.topk, sel=w.sel))
+    return {k: round(v, 1) for k, v in res.items()}
+
+
+def cpu_baseline(w, budget_s):
+    """The oracle on a bounded sample of the same workload, scaled to a step."""
+    import oracle
+    cfg, x = w.cfg, w.x
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = os.cpu_count()
+    rng = np.random.default_rng(7)
+    # attention rows: calibrate on a few rows, then fill about 60% of the budget
+    sel = None
+    if cfg.topk:
+        t0 = time.perf_counter()
+        sel = oracle.topk_blocks(x.q[:1, :1], x.k_pages, x.block_table[:1], x.ctx_lens[:1], cfg.bs,
+                                 cfg.topk, cfg.dtype)
+        topk_one = time.perf_counter() - t0          # block means of one sequence + 1 node
+    def rows_of(n):
+        return [(int(rng.integers(cfg.B)), int(rng.integers(cfg.T)), int(rng.integers(cfg.Hq)))
+                for _ in range(n)]
+    t0 = time.perf_counter()
+    oracle.attention_dense(x.q, x.k_pages, x.v_pages, x.block_table, x.ctx_lens, x.tree_parent,
+                           cfg.bs, cfg.dtype, rows=rows_of(4))
+    per_row = (time.perf_counter() - t0) / 4
+    n_rows = int(max(8, min(4096, 0.6 * budget_s / max(per_row, 1e-6))))
+    rows = rows_of(n_rows)
+    t0 = time.perf_counter()
+    oracle.attention_dense(x.q, x.k_pages, x.v_pages, x.block_table, x.ctx_lens, x.tree_parent,
+                           cfg.bs, cfg.dtype, rows=rows)
+    t_attn = (time.perf_counter() - t0) / n_rows * cfg.B * cfg.T * cfg.Hq
+    n_seq = min(cfg.B, 2)
+    t0 = time.perf_counter()
+    path, plen, _ = oracle.accept(x.target_logits[:n_seq], cfg.logit_dtype,
+                                  None if x.draft_probs is None else x.draft_probs[:n_seq],
+                                  x.tree_parent[:n_seq] if x.tree_parent.shape[0] > 1 else x.tree_parent,
+                                  x.tree_token[:n_seq] if x.tree_token.shape[0] > 1 else x.tree_token,
+                                  x.uniforms[:n_seq], w.tau)
+    t_acc = (time.perf_counter() - t0) / n_seq * cfg.B
+    t0 = time.perf_counter()
+    oracle.commit(x.k_pages, x.v_pages, x.block_table[:n_seq], x.ctx_lens[:n_seq], path, plen, cfg.bs)
+    t_commit = (time.perf_counter() - t0) / n_seq * cfg.B
+    t_step = t_attn + t_acc + t_commit
+    sample = ("%d attention rows of %d, acceptance and commit of %d of %d sequences, scaled to one step"
+              % (n_rows, cfg.B * cfg.T * cfg.Hq, n_seq, cfg.B))
+    if cfg.topk:
+        t_step += topk_one * cfg.B
+        sample += "; block selection of one sequence scaled by B"
+    return {"value": round(cfg.B * cfg.T / t_step, 3), "unit": "verified tree tokens/s",
+            "cores": int(threads), "kind": "oracle", "sample": sample,
+            "step_s_est": round(t_step, 3)}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(--gpus %d, WORLD_SIZE %d requested)" % (args.gpus, world), file=sys.stderr)
+        sys.exit(2)
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    w = Workload(args.workload)
+    cfg = w.cfg
+    for _ in range(args.warmup):
+        w.step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        w.step(evs[k])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    attn_s = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e-3
+    step_s = (t1 - t0) / args.steps
+    status = w.tva.device_status()
+    assert status == 0, "device status bits set: %#x" % status
+    plen = w.plen.cpu().numpy()
+
+    sel_np = None if w.sel is None else w.sel.cpu().numpy()
+    bytes_, flops = attention_cost(cfg, w.x, sel_np)
+    roof = roofline_for(cfg, bytes_, flops, attn_s)
+    roof["traffic"] = traffic_for("attn", cfg.name)
+    calls = time_calls(w)
+
+    secondary = None
+    if not args.no_secondary and args.workload != "specexec_70b_tree2048":
+        w2 = Workload("specexec_70b_tree2048")
+        t2 = time_calls(w2, reps=10)["attention_us"] * 1e-6
+        b2, f2 = attention_cost(w2.cfg, w2.x)
+        r2 = roofline_for(w2.cfg, b2, f2, t2)
+        secondary = {"workload": "specexec_70b_tree2048 attention (B=1, 64/8 heads, T=2048, ctx 2048)",
+                     "attention_us": round(t2 * 1e6, 1), "roofline": r2,
+                     "verified_tree_tokens_per_s": round(w2.cfg.B * w2.cfg.T / t2, 1)}
+        del w2
+
+    cpu = None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_seconds)
+    value = cfg.B * cfg.T / step_s
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "verified tree tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_s * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded; shapes of the workload, no datasets or weights)",
+        "config": {"workload": cfg.name, "B": cfg.B, "T": cfg.T, "Hq": cfg.Hq, "Hkv": cfg.Hkv,
+                   "D": cfg.D, "ctx": [cfg.ctx_lo, cfg.ctx_hi], "block": cfg.bs, "V": cfg.V,
+                   "accept": cfg.mode, "temperature": w.tau, "topk": cfg.topk or None},
+        "roofline": dict(roof, kernel="sd_tree_verify_attn (ancestor masks + attention)",
+                         attention_us=round(attn_s * 1e6, 2), bytes_per_call=int(bytes_),
+                         flops_per_call=int(flops)),
+        "cpu_baseline": cpu,
+        "accepted_tokens_per_s": round(float(plen.sum()) / step_s, 1),
+        "mean_path_len": round(float(plen.mean()), 3),
+        "calls_us": calls,
+        "secondary": secondary,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()
