@@ -15,11 +15,13 @@
 // A sequence is walked by P workgroups of 256 threads; workgroup w owns the
 // vocabulary slice [w * SL, (w + 1) * SL), read in chunks of 2048 tokens with
 // one 16-byte load per thread per chunk (a bf16 slice stays in registers for
-// the whole step).  After each pass the P workgroups publish a two-value
-// partial to the workspace and meet at a barrier (an atomic counter with a
-// bounded spin; the launch is cooperative, so all P are resident); every
-// workgroup then reduces the P partials in the same order and takes the same
-// decision.  An inverse-CDF draw picks the slice holding the crossing point
+// the whole step).  After each pass the P workgroups exchange a two-value
+// partial through barrier-tagged atomic slots in the workspace (bounded spin;
+// B * P <= 256 workgroups, one per CU, are all resident); every workgroup then
+// reduces the P partials in the same order and takes the same decision.  At
+// each node the loads that the walk will need are issued together: the
+// test scalars of the children, the draft row, and the first child's logits
+// (the likeliest next node).  An inverse-CDF draw picks the slice holding the crossing point
 // from the per-slice masses and only that workgroup rescans its slice.  Sums
 // are float64; the probability a test is taken on is recomputed in float64.
 #include "common.h"
@@ -33,6 +35,7 @@ constexpr int kMaxCh = 4;             // chunks kept in registers
 constexpr int kMaxT = 4096;
 constexpr int kMaxRej = 64;
 constexpr int kMaxP = 16;
+constexpr int kMaxKid = 64;          // children whose test scalars are prefetched
 constexpr unsigned kSpinLimit = 1u << 20;
 
 __device__ __forceinline__ double wave_sum_d(double v) {
@@ -89,14 +92,18 @@ template <typename LT, bool CACHED>
 __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
   constexpr bool kBF = sizeof(LT) == 2;
   static_assert(!CACHED || kBF, "only bf16 rows are cached");
+  __shared__ int s_par[kMaxT];
+  __shared__ int s_tok[kMaxT];
   __shared__ int kids[kMaxT];
+  __shared__ float kid_l[kMaxKid], kid_q[kMaxKid], kid_u[kMaxKid];
   __shared__ int wcnt[kAW];
   __shared__ double red_d[kAW];
   __shared__ float red_f[kAW];
   __shared__ int red_i[kAW];
   __shared__ double mass[kMaxP];    // per-slice mass of the distribution to draw from
   __shared__ double zrej[kMaxRej];  // residual normalisers at the current node
-  __shared__ double s_part[2];
+  __shared__ double zinv[kMaxRej];  // their reciprocals (0 when the mass was 0)
+  __shared__ uint32_t xv[kMaxP][2];
   __shared__ int s_flag, s_to, s_first, s_last, s_x;
 
   const int P = a.P;
@@ -104,22 +111,21 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int T = a.T, V = a.V;
   const int bt = a.tree_stride ? b : 0;
-  const int32_t* par = a.parent + (size_t)bt * T;
-  const int32_t* tok = a.token + (size_t)bt * T;
   int32_t* path = a.path + (size_t)b * T;
-  unsigned char* seq = a.sync + (size_t)b * kAccSeqBytes;
-  unsigned* ctr = reinterpret_cast<unsigned*>(seq);
-  unsigned* done = ctr + 1;
-  int* xslot = reinterpret_cast<int*>(ctr + 2);
-  double* part = reinterpret_cast<double*>(seq + 64);  // [2][P][2]
+  // Exchange slots of this sequence: [2 parities][P workgroups][2 values], each
+  // a 64-bit word (barrier number << 32 | 32-bit value), then the exit counter.
+  unsigned long long* slots = reinterpret_cast<unsigned long long*>(a.sync + (size_t)b * kAccSeqBytes);
+  unsigned* done = reinterpret_cast<unsigned*>(slots + 2 * kMaxP * 2);
 
-  // The tree must be topologically ordered with valid tokens.
+  // The tree (kept in LDS) must be topologically ordered with valid tokens.
   int bad = 0;
   for (int n = tid; n < T; n += kAT) {
-    const int p = par[n];
+    const int p = a.parent[(size_t)bt * T + n];
+    const int t = a.token[(size_t)bt * T + n];
     if (n == 0 ? p != -1 : (p < 0 || p >= n)) bad |= SD_ERR_PARENT;
-    const int t = tok[n];
     if (t < 0 || t >= V) bad |= SD_ERR_TOKEN;
+    s_par[n] = p;
+    s_tok[n] = t;
   }
   if (tid == 0) {
     s_flag = 0;
@@ -142,52 +148,59 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
   const int sl0 = min(wg * a.SL, V), sl1 = min(sl0 + a.SL, V);
   const int NC = a.NC;
   const bool vec = (V & 7) == 0;
+  const bool mss = a.tau > 0.f && a.draft != nullptr;
   const float c2 = a.tau > 0.f ? 1.4426950408889634f / a.tau : 0.f;
   const double invtau_d = a.tau > 0.f ? 1.0 / (double)a.tau : 0.0;
   auto y0_of = [&](int c) { return sl0 + c * kChunk + tid * 8; };
+  auto row_of = [&](int node) {
+    return reinterpret_cast<const LT*>(a.logits) + ((size_t)b * T + node) * V;
+  };
 
   // ---- cross-workgroup exchange ---------------------------------------------
+  // exchange(v0, v1): every workgroup of the sequence publishes two 32-bit
+  // values tagged with the barrier number; lanes j < P of wave 0 poll slot j
+  // until it carries this barrier's number (bounded), and the P pairs land in
+  // xv[] for the whole workgroup.  Slots alternate between two parities, so a
+  // workgroup can never overwrite a value another one has not read yet.  No
+  // fences are needed: each value travels in a single atomic word.
   int nbar = 0;
-  auto barrier = [&]() {
+  auto exchange = [&](uint32_t v0, uint32_t v1) {
     __syncthreads();
-    if (P > 1) {
-      ++nbar;
+    ++nbar;
+    if (P == 1) {
       if (tid == 0) {
-        __threadfence();
-        atomicAdd(ctr, 1u);
-        const unsigned target = (unsigned)nbar * (unsigned)P;
-        if (!s_to) {
-          unsigned spins = 0;
-          while (__hip_atomic_load(ctr, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < target) {
-            __builtin_amdgcn_s_sleep(2);
-            if (++spins > kSpinLimit) {
-              s_to = 1;
-              break;
-            }
+        xv[0][0] = v0;
+        xv[0][1] = v1;
+      }
+    } else {
+      unsigned long long* sl = slots + (size_t)(nbar & 1) * kMaxP * 2;
+      const unsigned long long tag = (unsigned long long)(unsigned)nbar << 32;
+      if (tid == 0) {
+        __hip_atomic_store(sl + wg * 2 + 0, tag | v0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(sl + wg * 2 + 1, tag | v1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      if (tid < P) {
+        unsigned long long w0, w1;
+        unsigned spins = 0;
+        for (;;) {
+          w0 = __hip_atomic_load(sl + tid * 2 + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          w1 = __hip_atomic_load(sl + tid * 2 + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if ((w0 >> 32) == (unsigned)nbar && (w1 >> 32) == (unsigned)nbar) break;
+          if (++spins > kSpinLimit) {
+            s_to = 1;
+            break;
           }
+          __builtin_amdgcn_s_sleep(1);
         }
-        __threadfence();
-      }
-      __syncthreads();
-    }
-  };
-  auto publish = [&](double v0, double v1) {
-    if (tid == 0) {
-      if (P > 1) {
-        double* p = part + (((nbar + 1) & 1) * P + wg) * 2;
-        store_d(p, v0);
-        store_d(p + 1, v1);
-      } else {
-        s_part[0] = v0;
-        s_part[1] = v1;
+        xv[tid][0] = (uint32_t)w0;
+        xv[tid][1] = (uint32_t)w1;
       }
     }
+    __syncthreads();
   };
-  auto fetch = [&](int j, int k) -> double {
-    return P == 1 ? s_part[k] : load_d(part + ((nbar & 1) * P + j) * 2 + k);
-  };
+  auto xf = [&](int j, int k) { return __uint_as_float(xv[j][k]); };
 
-  // ---- workgroup reductions ---------------------------------------------------
+  // ---- workgroup reduction of a float64 sum -------------------------------------
   auto wg_sum = [&](double v) -> double {
     v = wave_sum_d(v);
     __syncthreads();
@@ -197,22 +210,13 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
     for (int w = 0; w < kAW; ++w) t += red_d[w];
     return t;
   };
-  auto wg_max = [&](float v) -> float {
-    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
-    __syncthreads();
-    if (lane == 0) red_f[wave] = v;
-    __syncthreads();
-    float t = red_f[0];
-    for (int w = 1; w < kAW; ++w) t = fmaxf(t, red_f[w]);
-    return t;
-  };
 
   // children of `cur` in ascending index order -> kids[0..return)
   auto gather_children = [&](int cur) -> int {
     int nk = 0;
     for (int base = 0; base < T; base += kAT) {
       const int n = base + tid;
-      const bool f = n < T && par[n] == cur;
+      const bool f = n < T && s_par[n] == cur;
       const unsigned long long bal = __ballot(f);
       if (lane == 0) wcnt[wave] = __popcll(bal);
       __syncthreads();
@@ -227,8 +231,31 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
     return nk;
   };
 
-  uint4 lc[kMaxCh];  // this thread's bf16 logits (when `cache`)
-  const LT* row = nullptr;
+  // Row caches (CACHED): the current node's logits, the first child's logits
+  // (prefetched in case it is accepted) and, for rejection sampling, the
+  // current node's draft probabilities.
+  uint4 lc[kMaxCh], pfc[kMaxCh];
+  float qc[kMaxCh][8];
+  const LT* row = row_of(0);
+  const float* qrow = nullptr;
+  auto load_row = [&](const LT* r, uint4* dst) {
+    if constexpr (CACHED) {
+#pragma unroll
+      for (int c = 0; c < kMaxCh; ++c) {
+        const int y0 = y0_of(c);
+        if (c < NC && y0 < sl1) {
+          if (vec && y0 + 8 <= V) {
+            dst[c] = *reinterpret_cast<const uint4*>(r + y0);
+          } else {
+            uint32_t w[4] = {0, 0, 0, 0};
+            for (int e = 0; e < 8; ++e)
+              if (y0 + e < V) w[e >> 1] |= (uint32_t)r[y0 + e] << (16 * (e & 1));
+            dst[c] = make_uint4(w[0], w[1], w[2], w[3]);
+          }
+        }
+      }
+    }
+  };
   auto logits8 = [&](int c, float* v) {
     const int y0 = y0_of(c);
     if (y0 >= sl1) {
@@ -244,6 +271,20 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
         v[e] = y0 + e < V ? bf16_to_f32((bf16_bits)(w[e >> 1] >> (16 * (e & 1)))) : -INFINITY;
     } else {
       load8<LT>(row, y0, V, vec, -INFINITY, v);
+    }
+  };
+  auto q8_of = [&](int c, float* q8) {
+    if constexpr (CACHED) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) q8[e] = qc[c][e];
+    } else {
+      const int y0 = y0_of(c);
+      if (y0 < sl1) {
+        load8<float>(qrow, y0, V, vec, 0.f, q8);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) q8[e] = 0.f;
+      }
     }
   };
 
@@ -280,7 +321,7 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
       double w8[8];
       wf(c, w8);
       double ls = 0.0;
-_Pragma("unroll")
+      _Pragma("unroll")
       for (int e = 0; e < 8; ++e) ls += w8[e];
       double inc = ls;
       for (int off = 1; off < 64; off <<= 1) {
@@ -327,27 +368,43 @@ _Pragma("unroll")
   };
 
   int cur = 0, plen = 1;
+  bool have_row = false;   // lc already holds the current node's row (prefetched)
   if (wg == 0 && tid == 0) path[0] = 0;
   for (int step = 0; step < T; ++step) {
     const int nk = gather_children(cur);
-    row = reinterpret_cast<const LT*>(a.logits) + ((size_t)b * T + cur) * V;
-    if constexpr (CACHED) {
-      {
+    row = row_of(cur);
+    // Issue this node's loads together: the scalars of the child tests, the
+    // row (unless prefetched), the draft row, and the first child's row.
+    float kl = 0.f, kq = 0.f, ku = 0.f;
+    const bool kid_lane = mss && tid < min(nk, kMaxKid);
+    if (kid_lane) {
+      const int node = kids[tid];
+      const int x = s_tok[node];
+      kl = Elem<LT>::load(row, x);
+      kq = a.draft[((size_t)b * T + cur) * V + x];
+      ku = a.unif[((size_t)b * T + node) * 2 + 0];
+    }
+    if (!have_row) load_row(row, lc);
+    if (mss) {
+      qrow = a.draft + ((size_t)b * T + cur) * V;
+      if constexpr (CACHED) {
 #pragma unroll
         for (int c = 0; c < kMaxCh; ++c) {
           const int y0 = y0_of(c);
           if (c < NC && y0 < sl1) {
-            if (vec && y0 + 8 <= V) {
-              lc[c] = *reinterpret_cast<const uint4*>(row + y0);
-            } else {
-              uint32_t w[4] = {0, 0, 0, 0};
-              for (int e = 0; e < 8; ++e)
-                if (y0 + e < V) w[e >> 1] |= (uint32_t)row[y0 + e] << (16 * (e & 1));
-              lc[c] = make_uint4(w[0], w[1], w[2], w[3]);
-            }
+            load8<float>(qrow, y0, V, vec, 0.f, qc[c]);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) qc[c][e] = 0.f;
           }
         }
       }
+    }
+    if (nk > 0) load_row(row_of(kids[0]), pfc);
+    if (kid_lane) {
+      kid_l[tid] = kl;
+      kid_q[tid] = kq;
+      kid_u[tid] = ku;
     }
     int nxt = -1;
     bool stop = false;
@@ -359,7 +416,7 @@ _Pragma("unroll")
         float v[8];
         logits8(c, v);
         const int y0 = y0_of(c);
-_Pragma("unroll")
+        _Pragma("unroll")
         for (int e = 0; e < 8; ++e)
           if (v[e] > bv) {
             bv = v[e];
@@ -387,21 +444,20 @@ _Pragma("unroll")
           bv = red_f[w];
           bi = red_i[w];
         }
-      publish((double)bv, (double)bi);
-      barrier();
-      double gv = -INFINITY;
+      exchange(__float_as_uint(bv), (uint32_t)bi);
+      float gv = -INFINITY;
       int gi = V;
       for (int j = 0; j < P; ++j) {
-        const double v = fetch(j, 0);
-        const int i = (int)fetch(j, 1);
+        const float v = xf(j, 0);
+        const int i = (int)xv[j][1];
         if (v > gv || (v == gv && i < gi)) {
           gv = v;
           gi = i;
         }
       }
       for (int c = 0; c < nk; ++c)
-        if (tok[kids[c]] == gi) {
-          nxt = kids[c];
+        if (s_tok[kids[c]] == gi) {
+          nxt = c;
           break;
         }
       if (nxt < 0) {
@@ -409,32 +465,52 @@ _Pragma("unroll")
         stop = true;
       }
     } else {
-      // statistics of this slice: max, then mass relative to that max
-      float mw = -INFINITY;
+      // statistics of this slice in one pass: running max and the mass
+      // relative to it, merged across lanes and waves
+      float mt = -INFINITY;
+      double st = 0.0;
       FOR_CHUNKS(c,
         float v[8];
         logits8(c, v);
-_Pragma("unroll")
-        for (int e = 0; e < 8; ++e) mw = fmaxf(mw, v[e]);
+        float cm = v[0];
+        _Pragma("unroll")
+        for (int e = 1; e < 8; ++e) cm = fmaxf(cm, v[e]);
+        if (cm > -INFINITY) {
+          const float mn = fmaxf(mt, cm);
+          double add = 0.0;
+          _Pragma("unroll")
+          for (int e = 0; e < 8; ++e) add += (double)__builtin_amdgcn_exp2f((v[e] - mn) * c2);
+          st = (mt == -INFINITY ? 0.0 : st * (double)__builtin_amdgcn_exp2f((mt - mn) * c2)) + add;
+          mt = mn;
+        }
       )
-      mw = wg_max(mw);
-      double sw = 0.0;
-      if (mw != -INFINITY) {
-        FOR_CHUNKS(c,
-          float v[8];
-          logits8(c, v);
-_Pragma("unroll")
-          for (int e = 0; e < 8; ++e) sw += (double)__builtin_amdgcn_exp2f((v[e] - mw) * c2);
-        )
+      for (int off = 32; off >= 1; off >>= 1) {
+        const float om = __shfl_xor(mt, off);
+        const double os = __shfl_xor(st, off);
+        const float mn = fmaxf(mt, om);
+        if (mn > -INFINITY)
+          st = (mt == -INFINITY ? 0.0 : st * (double)__builtin_amdgcn_exp2f((mt - mn) * c2)) +
+               (om == -INFINITY ? 0.0 : os * (double)__builtin_amdgcn_exp2f((om - mn) * c2));
+        mt = mn;
       }
-      sw = wg_sum(sw);
-      publish((double)mw, sw);
-      barrier();
+      __syncthreads();
+      if (lane == 0) {
+        red_f[wave] = mt;
+        red_d[wave] = st;
+      }
+      __syncthreads();
+      float mw = red_f[0];
+      for (int w = 1; w < kAW; ++w) mw = fmaxf(mw, red_f[w]);
+      double sw = 0.0;
+      if (mw > -INFINITY)
+        for (int w = 0; w < kAW; ++w)
+          if (red_f[w] > -INFINITY) sw += red_d[w] * (double)__builtin_amdgcn_exp2f((red_f[w] - mw) * c2);
+      exchange(__float_as_uint(mw), __float_as_uint((float)sw));
       float m = -INFINITY;
-      for (int j = 0; j < P; ++j) m = fmaxf(m, (float)fetch(j, 0));
+      for (int j = 0; j < P; ++j) m = fmaxf(m, xf(j, 0));
       if (tid < P) {
-        const float mj = (float)fetch(tid, 0);
-        mass[tid] = mj == -INFINITY ? 0.0 : fetch(tid, 1) * (double)__builtin_amdgcn_exp2f((mj - m) * c2);
+        const float mj = xf(tid, 0);
+        mass[tid] = mj == -INFINITY ? 0.0 : (double)xf(tid, 1) * (double)__builtin_amdgcn_exp2f((mj - m) * c2);
       }
       __syncthreads();
       double z0 = 0.0;
@@ -446,19 +522,15 @@ _Pragma("unroll")
         for (int e = 0; e < 8; ++e)
           w8[e] = v[e] == -INFINITY ? 0.0 : (double)__builtin_amdgcn_exp2f((v[e] - m) * c2);
       };
-      const float* qrow = a.draft ? a.draft + ((size_t)b * T + cur) * V : nullptr;
-      if (qrow == nullptr) {
+      if (!mss) {
         const float u = a.unif[((size_t)b * T + cur) * 2 + 1];
         const int x = draw(u, ew8);
-        if (x >= 0 && tid == 0) {
-          if (P > 1) __hip_atomic_store(xslot, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          else s_x = x;
-        }
-        barrier();
-        const int xs = P > 1 ? __hip_atomic_load(xslot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : s_x;
+        exchange((uint32_t)(x + 1), 0u);   // only the drawing workgroup has x >= 0
+        int xs = -1;
+        for (int j = 0; j < P; ++j) xs = max(xs, (int)xv[j][0] - 1);
         for (int c = 0; c < nk; ++c)
-          if (tok[kids[c]] == xs) {
-            nxt = kids[c];
+          if (s_tok[kids[c]] == xs) {
+            nxt = c;
             break;
           }
         if (nxt < 0) {
@@ -468,71 +540,48 @@ _Pragma("unroll")
       } else {
         int nrej = 0;
         // residual after `upto` rejections, elementwise; zrej[j] is the j-th normaliser
+        // (multiplying by the reciprocals: a relative difference of ~1e-16
+        // from dividing, far inside the decision tolerance)
         auto resid = [&](double r0, double qy, int upto) -> double {
           double r = r0;
           for (int j = 0; j < upto; ++j)
-            if (zrej[j] > 0.0) r = fmax(r - qy, 0.0) / zrej[j];  // zero mass: unchanged
+            if (zinv[j] > 0.0) r = fmax(r - qy, 0.0) * zinv[j];  // zero mass: unchanged
           return r;
         };
-        auto q8_of = [&](int c, float* q8) {
-          const int y0 = y0_of(c);
-          if (y0 < sl1) {
-            load8<float>(qrow, y0, V, vec, 0.f, q8);
-          } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) q8[e] = 0.f;
-          }
-        };
+        const double iz0 = 1.0 / z0;
         for (int c = 0; c < nk && nrej < kMaxRej; ++c) {
           const int node = kids[c];
-          const int x = tok[node];
-          const double lx = (double)Elem<LT>::load(row, x);
-          const double rx0 = exp((lx - (double)m) * invtau_d) / z0;
-          const double qx = (double)qrow[x];
-          const double rx = resid(rx0, qx, nrej);
-          const double u = (double)a.unif[((size_t)b * T + node) * 2 + 0];
+          const int x = s_tok[node];
+          const double lx = c < kMaxKid ? (double)kid_l[c] : (double)Elem<LT>::load(row, x);
+          const double qx = c < kMaxKid ? (double)kid_q[c] : (double)qrow[x];
+          const double u = c < kMaxKid ? (double)kid_u[c] : (double)a.unif[((size_t)b * T + node) * 2];
+          const double rx = resid(exp((lx - (double)m) * invtau_d) / z0, qx, nrej);
           if (u * qx < rx) {
-            nxt = node;
+            nxt = c;
             break;
           }
           // rejected: this slice's mass of max(r - q, 0)
           double pz = 0.0;
-          if constexpr (CACHED) {
-            float q8[kMaxCh][8];
-#pragma unroll
-            for (int k = 0; k < kMaxCh; ++k)
-              if (k < NC) q8_of(k, q8[k]);
-#pragma unroll
-            for (int k = 0; k < kMaxCh; ++k) {
-              if (k < NC) {
-                double w8[8];
-                ew8(k, w8);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                  const double qy = (double)q8[k][e];
-                  pz += fmax(resid(w8[e] / z0, qy, nrej) - qy, 0.0);
-                }
-              }
+          FOR_CHUNKS(cc,
+            double w8[8];
+            float q8[8];
+            ew8(cc, w8);
+            q8_of(cc, q8);
+            _Pragma("unroll")
+            for (int e = 0; e < 8; ++e) {
+              const double qy = (double)q8[e];
+              pz += fmax(resid(w8[e] * iz0, qy, nrej) - qy, 0.0);
             }
-          } else {
-            for (int c = 0; c < NC; ++c) {
-              float q8[8];
-              double w8[8];
-              q8_of(c, q8);
-              ew8(c, w8);
-              for (int e = 0; e < 8; ++e) {
-                const double qy = (double)q8[e];
-                pz += fmax(resid(w8[e] / z0, qy, nrej) - qy, 0.0);
-              }
-            }
-          }
+          )
           pz = wg_sum(pz);
-          publish(pz, 0.0);
-          barrier();
+          exchange(__float_as_uint((float)pz), 0u);
           double z = 0.0;
-          for (int j = 0; j < P; ++j) z += fetch(j, 0);
-          if (z > 0.0 && tid < P) mass[tid] = fetch(tid, 0);
-          if (tid == 0) zrej[nrej] = z;
+          for (int j = 0; j < P; ++j) z += (double)xf(j, 0);
+          if (z > 0.0 && tid < P) mass[tid] = (double)xf(tid, 0);
+          if (tid == 0) {
+            zrej[nrej] = z;
+            zinv[nrej] = z > 0.0 ? 1.0 / z : 0.0;
+          }
           __syncthreads();
           ++nrej;
         }
@@ -549,7 +598,7 @@ _Pragma("unroll")
             q8_of(c, q8);
             ew8(c, w8);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) w8[e] = resid(w8[e] / z0, (double)q8[e], nr) * units;
+            for (int e = 0; e < 8; ++e) w8[e] = resid(w8[e] * iz0, (double)q8[e], nr) * units;
           };
           const int x = draw(u, rw8);
           if (x >= 0 && tid == 0) a.bonus[b] = x;
@@ -558,17 +607,31 @@ _Pragma("unroll")
       }
     }
     if (stop) break;
-    if (wg == 0 && tid == 0) path[plen] = nxt;
+    const int nnode = kids[nxt];
+    if (wg == 0 && tid == 0) path[plen] = nnode;
     ++plen;
-    cur = nxt;
+    cur = nnode;
+    have_row = false;
+    if constexpr (CACHED) {
+      if (nxt == 0) {
+#pragma unroll
+        for (int c = 0; c < kMaxCh; ++c) lc[c] = pfc[c];
+        have_row = true;
+      }
+    }
+    __syncthreads();
   }
   if (wg == 0 && tid == 0) a.path_len[b] = plen;
-  if (P > 1 && tid == 0) {
-    // the last workgroup of the sequence to leave resets the counters
-    __threadfence();
-    if (atomicAdd(done, 1u) == (unsigned)P - 1) {
-      __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (P > 1) {
+    // the last workgroup of the sequence to leave clears the slots, so the
+    // next call starts from barrier number 1 again
+    __syncthreads();
+    if (tid == 0) s_flag = atomicAdd(done, 1u) == (unsigned)P - 1;
+    __syncthreads();
+    if (s_flag) {
+      for (int j = tid; j < 2 * kMaxP * 2; j += kAT)
+        __hip_atomic_store(slots + j, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (tid == 0) __hip_atomic_store(done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
   if (tid == 0 && s_to) set_status(a.status, SD_ERR_TIMEOUT);
@@ -587,10 +650,12 @@ hipError_t launch_accept(const AcceptArgs& a, hipStream_t st) {
                    : a.NC <= kMaxCh ? reinterpret_cast<const void*>(accept_kernel<bf16_bits, true>)
                                     : reinterpret_cast<const void*>(accept_kernel<bf16_bits, false>);
   const dim3 grid((unsigned)a.B * a.P), block(kAT);
+  // B * P <= 256: with one workgroup per CU every workgroup of the grid is
+  // resident at once, which the cross-workgroup waits rely on (they are
+  // bounded in any case).
   AcceptArgs copy = a;
   void* args[] = {&copy};
-  if (a.P == 1) return hipLaunchKernel(fn, grid, block, args, 0, st);
-  return hipLaunchCooperativeKernel(fn, grid, block, args, 0, st);
+  return hipLaunchKernel(fn, grid, block, args, 0, st);
 }
 
 }  // namespace sdtree

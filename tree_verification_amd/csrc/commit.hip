@@ -2,17 +2,27 @@
 //
 // After acceptance the accepted nodes become committed context in path order:
 // position ctx_b + j takes the K/V held at ctx_b + path[j], then ctx_b grows by
-// the path length.  One workgroup per sequence; each thread owns one 16-byte
-// chunk of a K row or one V element column of one KV head and copies it for
-// j = 0, 1, ... in order.  Because the path is increasing with path[j] >= j,
-// a source slot is always read before any write can reach it, so the copy is
-// safe in place.
+// the path length.  One workgroup per sequence copies the path in groups of
+// JG entries: every thread first loads its share of the group (16-byte K
+// chunks and V^T elements, all heads) into registers, the workgroup
+// synchronises, then the stores are issued.  The path is increasing with
+// path[j] >= j, so a group's destinations (positions < ctx + j0 + JG) never
+// overlap the sources of a later group (positions >= ctx + j0 + JG): the copy
+// is safe in place.  Shapes whose group does not fit the registers copy one
+// entry at a time (source and destination of one entry never overlap).
 #include "common.h"
 
 namespace sdtree {
 
-__global__ void __launch_bounds__(256) commit_kernel(CommitArgs a) {
+constexpr int kCommitThreads = 256;
+constexpr int kKRegs = 4;        // 16-byte K chunks per thread per group
+constexpr int kVRegs = 24;       // V^T elements per thread per group
+constexpr int kCommitGroup = 16; // path entries per group
+constexpr int kCommitUnits = 256; // (entry, KV head) units per group
+
+__global__ void __launch_bounds__(kCommitThreads) commit_kernel(CommitArgs a) {
   __shared__ int s_ok, s_ctx, s_len;
+  __shared__ int s_path[kMaxCommitT];
   const int b = blockIdx.x, tid = threadIdx.x;
   const int32_t* path = a.path + (size_t)b * a.T;
   const int32_t* table = a.table + (size_t)b * a.max_blocks;
@@ -37,39 +47,113 @@ __global__ void __launch_bounds__(256) commit_kernel(CommitArgs a) {
   __syncthreads();
   if (!s_ok) return;
   const int ctx = s_ctx, L = s_len;
-  const int kchunks = a.D * a.esize / 16;             // 16-byte chunks per K row
-  const int items = a.Hkv * (kchunks + a.D);          // K chunks, then V columns
+  for (int j = tid; j < L; j += kCommitThreads) s_path[j] = path[j];
+  __syncthreads();
+
+  // A unit is (path entry, KV head).  Threads own fixed columns of a unit: a
+  // 16-byte K chunk (kch per row) or one V^T element (D per column); their
+  // byte offsets live in LDS, so the copy loops do no index arithmetic.
+  const int kch = a.D * a.esize / 16;                 // 16-byte chunks per K row (power of 2)
+  const int rowb = a.D * a.esize;
   unsigned char* K = reinterpret_cast<unsigned char*>(a.k);
   unsigned char* V = reinterpret_cast<unsigned char*>(a.v);
-  for (int it = tid; it < items; it += blockDim.x) {
-    const int g = it / (kchunks + a.D);
-    const int r = it % (kchunks + a.D);
+  const int kstep = kCommitThreads / kch, vstep = kCommitThreads / a.D;
+  const int kcol = tid % kch, ku0 = tid / kch;
+  const int vcol = tid % a.D, vu0 = tid / a.D;
+  int JG = min(kCommitUnits, min(kKRegs * kstep, kVRegs * vstep)) / a.Hkv;
+  JG = min(JG, kCommitGroup);
+  __shared__ long long s_ks[kCommitUnits], s_kd[kCommitUnits], s_vs[kCommitUnits], s_vd[kCommitUnits];
+  const long long blk_bytes = (long long)a.Hkv * a.bs * rowb;
+  const long long head_k = (long long)a.bs * rowb;
+  const long long head_v = (long long)a.D * a.bs * a.esize;
+  const long long kc_off = (long long)kcol * 16;
+  const long long vc_off = (long long)vcol * a.bs * a.esize;
+  // offsets of units [0, nj * Hkv) for path entries j0 .. j0 + nj - 1
+  auto stage = [&](int j0, int nj) {
+    for (int u = tid; u < nj * a.Hkv; u += kCommitThreads) {
+      const int jj = u / a.Hkv, g = u % a.Hkv;
+      const int src = ctx + s_path[j0 + jj], dst = ctx + j0 + jj;
+      const long long sb = (long long)table[src / a.bs] * blk_bytes;
+      const long long db = (long long)table[dst / a.bs] * blk_bytes;
+      const bool same = s_path[j0 + jj] == j0 + jj;
+      s_ks[u] = sb + g * head_k + (long long)(src % a.bs) * rowb;
+      s_kd[u] = same ? -1 : db + g * head_k + (long long)(dst % a.bs) * rowb;
+      s_vs[u] = sb + g * head_v + (long long)(src % a.bs) * a.esize;
+      s_vd[u] = same ? -1 : db + g * head_v + (long long)(dst % a.bs) * a.esize;
+    }
+    __syncthreads();
+  };
+
+  if (JG >= 1) {
+    for (int j0 = 0; j0 < L; j0 += JG) {
+      const int nj = min(JG, L - j0);
+      const int nu = nj * a.Hkv;
+      stage(j0, nj);
+      uint4 kr[kKRegs];
+      uint32_t vr[kVRegs];
+#pragma unroll
+      for (int r = 0; r < kKRegs; ++r) {
+        const int u = ku0 + r * kstep;
+        kr[r] = u < nu ? *reinterpret_cast<const uint4*>(K + s_ks[u] + kc_off) : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int r = 0; r < kVRegs; ++r) {
+        const int u = vu0 + r * vstep;
+        vr[r] = 0;
+        if (u < nu)
+          vr[r] = a.esize == 2 ? *reinterpret_cast<const uint16_t*>(V + s_vs[u] + vc_off)
+                               : *reinterpret_cast<const uint32_t*>(V + s_vs[u] + vc_off);
+      }
+      __syncthreads();
+#pragma unroll
+      for (int r = 0; r < kKRegs; ++r) {
+        const int u = ku0 + r * kstep;
+        if (u < nu && s_kd[u] >= 0) *reinterpret_cast<uint4*>(K + s_kd[u] + kc_off) = kr[r];
+      }
+#pragma unroll
+      for (int r = 0; r < kVRegs; ++r) {
+        const int u = vu0 + r * vstep;
+        if (u < nu && s_vd[u] >= 0) {
+          if (a.esize == 2) *reinterpret_cast<uint16_t*>(V + s_vd[u] + vc_off) = (uint16_t)vr[r];
+          else *reinterpret_cast<uint32_t*>(V + s_vd[u] + vc_off) = vr[r];
+        }
+      }
+      __syncthreads();
+    }
+  } else {
+    // one entry at a time: its source and destination never overlap
     for (int j = 0; j < L; ++j) {
-      const int src = ctx + path[j], dst = ctx + j;
-      if (src == dst) continue;
-      const size_t sb = (size_t)table[src / a.bs], so = src % a.bs;
-      const size_t db = (size_t)table[dst / a.bs], dof = dst % a.bs;
-      if (r < kchunks) {
-        const size_t row = (size_t)a.D * a.esize;
-        const uint4 x = *reinterpret_cast<const uint4*>(K + ((sb * a.Hkv + g) * a.bs + so) * row + r * 16);
-        *reinterpret_cast<uint4*>(K + ((db * a.Hkv + g) * a.bs + dof) * row + r * 16) = x;
-      } else {
-        const int d = r - kchunks;
-        const size_t s_off = (((sb * a.Hkv + g) * a.D + d) * a.bs + so) * a.esize;
-        const size_t d_off = (((db * a.Hkv + g) * a.D + d) * a.bs + dof) * a.esize;
-        if (a.esize == 2)
-          *reinterpret_cast<uint16_t*>(V + d_off) = *reinterpret_cast<const uint16_t*>(V + s_off);
-        else
-          *reinterpret_cast<uint32_t*>(V + d_off) = *reinterpret_cast<const uint32_t*>(V + s_off);
+      for (int g0 = 0; g0 < a.Hkv; g0 += kCommitUnits) {
+        const int ng = min(kCommitUnits, a.Hkv - g0);
+        for (int u = tid; u < ng; u += kCommitThreads) {
+          const int src = ctx + s_path[j], dst = ctx + j, g = g0 + u;
+          const long long sb = (long long)table[src / a.bs] * blk_bytes;
+          const long long db = (long long)table[dst / a.bs] * blk_bytes;
+          s_ks[u] = sb + g * head_k + (long long)(src % a.bs) * rowb;
+          s_kd[u] = db + g * head_k + (long long)(dst % a.bs) * rowb;
+          s_vs[u] = sb + g * head_v + (long long)(src % a.bs) * a.esize;
+          s_vd[u] = db + g * head_v + (long long)(dst % a.bs) * a.esize;
+        }
+        __syncthreads();
+        if (s_path[j] != j) {
+          for (int u = ku0; u < ng; u += kstep)
+            *reinterpret_cast<uint4*>(K + s_kd[u] + kc_off) = *reinterpret_cast<const uint4*>(K + s_ks[u] + kc_off);
+          for (int u = vu0; u < ng; u += vstep) {
+            if (a.esize == 2)
+              *reinterpret_cast<uint16_t*>(V + s_vd[u] + vc_off) = *reinterpret_cast<const uint16_t*>(V + s_vs[u] + vc_off);
+            else
+              *reinterpret_cast<uint32_t*>(V + s_vd[u] + vc_off) = *reinterpret_cast<const uint32_t*>(V + s_vs[u] + vc_off);
+          }
+        }
+        __syncthreads();
       }
     }
   }
-  __syncthreads();
   if (tid == 0) a.ctx[b] = ctx + L;
 }
 
 hipError_t launch_commit(const CommitArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(commit_kernel, dim3(a.B), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(commit_kernel, dim3(a.B), dim3(kCommitThreads), 0, st, a);
   return hipGetLastError();
 }
 

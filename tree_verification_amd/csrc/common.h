@@ -123,6 +123,8 @@ struct AcceptArgs {
 
 int accept_wgs(int B, int V);
 
+constexpr int kMaxCommitT = 4096;
+
 struct CommitArgs {
   void* k;
   void* v;
