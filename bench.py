@@ -44,6 +44,9 @@ def parse():
                     help="approximate CPU time budget of the oracle sample")
     ap.add_argument("--no-secondary", action="store_true",
                     help="skip the attention roofline of the 2048-node tree workload")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="after the run, copy MIB MiB device-to-device 3 times (a plain copy "
+                         "kernel of known size that scales the HBM byte counters)")
     return ap.parse_args()
 
 
@@ -105,15 +108,25 @@ def roofline_for(cfg, bytes_, flops, seconds):
             "frac": round(achieved / peak, 4)}
 
 
+ATTN_SOURCES = ("attn.hip", "common.h", "sdtree.hip")
+
+
+def attn_source_hash():
+    """sha256 over the sources that decide the attention kernels and their plan."""
+    h = hashlib.sha256()
+    for f in ATTN_SOURCES:
+        h.update(open(os.path.join(ROOT, "tree_verification_amd", "csrc", f), "rb").read())
+    return h.hexdigest()
+
+
 def traffic_for(kernel_key, workload):
     """HBM bytes per attention call from committed rocprofv3 FETCH_SIZE /
-    WRITE_SIZE passes, if they were taken on the current kernel source."""
+    WRITE_SIZE passes, if they were taken on the current kernel sources."""
     path = os.path.join(ROOT, "profiles", "traffic_%s_%s.json" % (kernel_key, workload))
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    src = open(os.path.join(ROOT, "tree_verification_amd", "csrc", "attn.hip"), "rb").read()
-    if rec.get("attn_hip_sha256") != hashlib.sha256(src).hexdigest():
+    if rec.get("source_sha256") != attn_source_hash():
         return None
     return rec.get("bytes_per_call")
 
@@ -322,7 +335,15 @@ def main():
         "calls_us": calls,
         "secondary": secondary,
     }
-    print(json.dumps(line))
+    print(json.dumps(line), flush=True)
+    if args.copy_calibration > 0:
+        n = args.copy_calibration << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda")
+        src.fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
 
 
 if __name__ == "__main__":

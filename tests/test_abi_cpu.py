@@ -65,8 +65,9 @@ def test_attention_rejects_null_small_ws_and_bad_ksel():
 
 def test_workspace_sizes():
     s = _shape()
-    dense = L.sd_workspace_bytes(1, ctypes.byref(s), 0)
-    assert dense >= 256 + 16 * 64 * 8   # header + one ancestor word per node
+    assert L.sd_workspace_bytes(1, ctypes.byref(s), 0) >= 256
+    # float32: header + one precomputed ancestor word per node
+    assert L.sd_workspace_bytes(1, ctypes.byref(_shape(dtype=0)), 0) >= 256 + 16 * 64 * 8
     assert L.sd_workspace_bytes(1, ctypes.byref(s), 65) == 0
     assert L.sd_workspace_bytes(3, ctypes.byref(s), 32) >= 16 * 260 * 8 * 128 * 4
     assert L.sd_workspace_bytes(3, ctypes.byref(s), 0) == 0

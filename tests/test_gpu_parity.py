@@ -316,3 +316,20 @@ def test_bad_block_id_sets_status():
     tva.tree_verify_attn(d["q"], d["k"], d["v"], d["table"], d["ctx"], d["parent"])
     torch.cuda.synchronize()
     assert tva.device_status() & 0x2
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_bad_parent_sets_status(dtype):
+    c = small_variant("llama3_8b_tree64", B=2, T=8, ctx_lo=40, ctx_hi=40, dtype=dtype)
+    x = make_inputs(c)
+    x.tree_parent[1, 5] = 6                       # points forward
+    d = to_device(x)
+    _say("attention bad parent %s" % dtype)
+    tva.tree_verify_attn(d["q"], d["k"], d["v"], d["table"], d["ctx"], d["parent"])
+    torch.cuda.synchronize()
+    assert tva.device_status() & 0x1
+    x.tree_parent[1, 5] = x.tree_parent[1, 4]     # valid again: no bit
+    d = to_device(x)
+    tva.tree_verify_attn(d["q"], d["k"], d["v"], d["table"], d["ctx"], d["parent"])
+    torch.cuda.synchronize()
+    assert tva.device_status() == 0

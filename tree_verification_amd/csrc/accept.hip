@@ -32,7 +32,7 @@ constexpr int kAT = 256;              // threads per workgroup
 constexpr int kAW = kAT / 64;         // wavefronts per workgroup
 constexpr int kChunk = kAT * 8;       // tokens per chunk
 constexpr int kMaxCh = 4;             // chunks kept in registers
-constexpr int kMaxT = 4096;
+constexpr int kMaxT = kMaxTreeNodes;
 constexpr int kMaxRej = 64;
 constexpr int kMaxP = 16;
 constexpr int kMaxKid = 64;          // children whose test scalars are prefetched

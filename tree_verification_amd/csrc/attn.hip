@@ -270,19 +270,41 @@ __global__ void __launch_bounds__(256, 1) attn_mfma_kernel(AttnArgs a) {
   const int r_hi = min(row0 + ROWS, M);
   const int i_lo = row0 / G;
   const int i_hi = row0 < r_hi ? (r_hi - 1) / G : i_lo - 1;
+  // The parents of nodes 0..i_hi are staged in the still idle K/V ring; each of
+  // the tile's nodes then collects its inclusive ancestor set by walking up to
+  // a root, validating the parents on the way (a parent precedes its child; a
+  // non-root node may have parent -1, a forest).  ancL is sized by the plan for
+  // every node of the tile.
+  int* s_par = reinterpret_cast<int*>(smem);
+  static_assert(2 * (K_BYTES + V_BYTES) >= 4 * kMaxTreeNodes, "parents fit the ring");
+  const int nn = i_hi - i_lo + 1;
   if (tid < 128) tflag[tid] = 0;
   if (tid == 0) s_err = 0;
+  for (int j = tid; j <= i_hi; j += 256) s_par[j] = a.parent[(size_t)bt * T + j];
+  for (int idx = tid; idx < nn * a.W64; idx += 256) ancL[idx] = 0ull;
   __syncthreads();
-  {
-    const int cnt = (i_hi - i_lo + 1) * a.W64;
-    for (int idx = tid; idx < cnt; idx += 256) {
-      const int i = i_lo + idx / a.W64, w = idx % a.W64;
-      const uint64_t word = a.anc[((size_t)bt * T + i) * a.W64 + w];
-      ancL[idx] = word;  // the plan sizes ancL for every node of the tile
-      if (word != 0ull) tflag[(w * 64) / NK] = 1;
-    }
-  }
   int err = 0;
+  for (int idx = tid; idx < nn; idx += 256) {
+    uint64_t* row = ancL + idx * a.W64;
+    int n = i_lo + idx, cur_w = n >> 6;
+    uint64_t acc = 0;
+    while (true) {
+      const int w = n >> 6;
+      if (w != cur_w) {
+        row[cur_w] = acc;
+        tflag[(cur_w * 64) / NK] = 1;
+        cur_w = w;
+        acc = 0;
+      }
+      acc |= 1ull << (n & 63);
+      const int par = s_par[n];
+      if (n == 0 ? par != -1 : (par >= n || par < -1)) err |= SD_ERR_PARENT;
+      if (n == 0 || par >= n || par < 0) break;
+      n = par;
+    }
+    row[cur_w] = acc;
+    tflag[(cur_w * 64) / NK] = 1;
+  }
 
   // ---- sparse: union of the blocks selected by this workgroup's rows -----
   const int nblk_ctx = cap_ok ? (ctx + bs - 1) >> bsh : 0;

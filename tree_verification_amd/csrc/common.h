@@ -123,7 +123,8 @@ struct AcceptArgs {
 
 int accept_wgs(int B, int V);
 
-constexpr int kMaxCommitT = 4096;
+constexpr int kMaxTreeNodes = 4096;  // largest tree (T) any call accepts
+constexpr int kMaxCommitT = kMaxTreeNodes;
 
 struct CommitArgs {
   void* k;

@@ -9,7 +9,6 @@
 
 namespace sdtree {
 
-constexpr int kMaxT = 4096;
 constexpr int kMaxKsel = 64;
 constexpr size_t kLdsLimit = 160 * 1024;
 
@@ -25,7 +24,7 @@ static sd_status check_shape(const sd_shape* s) {
   if (s->dtype != SD_F32 && s->dtype != SD_BF16) return SD_BAD_DTYPE;
   if (s->D != 64 && s->D != 128) return SD_UNSUPPORTED;
   if (s->bs < 8 || (s->bs & (s->bs - 1)) != 0) return SD_UNSUPPORTED;
-  if (s->T > kMaxT) return SD_UNSUPPORTED;
+  if (s->T > kMaxTreeNodes) return SD_UNSUPPORTED;
   if ((long long)s->max_blocks * s->bs > (1ll << 30)) return SD_UNSUPPORTED;
   if ((long long)s->num_blocks * s->Hkv * s->bs * s->D > (1ll << 40)) return SD_UNSUPPORTED;
   if (!(s->scale >= 0.f) || isinf(s->scale)) return SD_INVALID_ARG;
@@ -42,7 +41,8 @@ static AttnPlan plan_attn(const sd_shape* s, int ksel, bool sparse) {
   p.W64 = (s->T + 63) / 64;
   p.T_tree = s->tree_stride ? s->B : 1;
   p.anc_off = kWsHeader;
-  const size_t anc_bytes = (size_t)p.T_tree * s->T * p.W64 * 8;
+  // precomputed ancestor masks, read by the per-row float32 kernel only
+  const size_t anc_bytes = s->dtype == SD_F32 ? (size_t)p.T_tree * s->T * p.W64 * 8 : 0;
   p.part_o_off = align_up(p.anc_off + anc_bytes, 256);
   if (s->dtype == SD_F32) {
     p.variant = 0;
@@ -208,8 +208,12 @@ sd_status sd_tree_verify_attn(const sd_shape* shape, const void* q, const void* 
   unsigned char* w = static_cast<unsigned char*>(ws);
   uint32_t* status = reinterpret_cast<uint32_t*>(w);
   uint64_t* anc = reinterpret_cast<uint64_t*>(w + p.anc_off);
-  hipError_t e = launch_anc_mask(tree_parent, s.T, p.W64, p.T_tree, anc, status, hs);
-  if (e != hipSuccess) return SD_HIP_ERROR;
+  if (p.variant == 0) {
+    // the per-row kernel reads precomputed ancestor masks; the MFMA kernel
+    // walks the tree itself
+    hipError_t e = launch_anc_mask(tree_parent, s.T, p.W64, p.T_tree, anc, status, hs);
+    if (e != hipSuccess) return SD_HIP_ERROR;
+  }
 
   AttnArgs a;
   memset(&a, 0, sizeof(a));
@@ -242,7 +246,7 @@ sd_status sd_accept(const sd_accept_shape* shape, const void* target_logits,
   if (s.B < 1 || s.T < 1 || s.V < 1) return SD_BAD_SHAPE;
   if (s.tree_stride != 0 && s.tree_stride != s.T) return SD_BAD_SHAPE;
   if (s.logit_dtype != SD_F32 && s.logit_dtype != SD_BF16) return SD_BAD_DTYPE;
-  if (s.T > kMaxT) return SD_UNSUPPORTED;
+  if (s.T > kMaxTreeNodes) return SD_UNSUPPORTED;
   if (!(temperature >= 0.f) || isinf(temperature)) return SD_INVALID_ARG;
   if (!target_logits || !tree_parent || !tree_token || !path || !path_len || !bonus || !ws)
     return SD_INVALID_ARG;
