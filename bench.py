@@ -47,6 +47,10 @@ def parse():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after the run, copy MIB MiB device-to-device 3 times (a plain copy "
                          "kernel of known size that scales the HBM byte counters)")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no run: turn the counter_collection.csv files of a rocprofv3 "
+                         "--pmc FETCH_SIZE pass and a --pmc WRITE_SIZE pass (both of a run "
+                         "with --copy-calibration) into profiles/traffic_attn_<workload>.json")
     return ap.parse_args()
 
 
@@ -131,6 +135,90 @@ def traffic_for(kernel_key, workload):
     return rec.get("bytes_per_call")
 
 
+def _counter_means(path, counter):
+    """Mean counter value (KiB per dispatch) of every kernel in a rocprofv3
+    counter_collection.csv, keyed by (kernel name, grid size)."""
+    import csv
+    acc = {}
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] != counter:
+            continue
+        k = (r["Kernel_Name"], int(r["Grid_Size"]))
+        acc.setdefault(k, []).append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in acc.items()}
+
+
+def write_traffic(workload, fetch_csv, write_csv, copy_mib):
+    """HBM bytes per attention call: FETCH_SIZE and WRITE_SIZE of the attention
+    kernels (KiB per dispatch), each scaled by the ratio of the known size of
+    the calibration copy to what the same counter reads for it."""
+    copy_bytes = copy_mib << 20
+    out = {"workload": workload, "copy_bytes": copy_bytes,
+           "source_sha256": attn_source_hash(), "counters": {}}
+    total = 0.0
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        means = _counter_means(path, counter)
+        copies = [v for (n, _), v in means.items() if "copyBuffer" in n]
+        cal = max(copies)          # the largest copy is the calibration copy
+        scale = copy_bytes / (cal * 1024.0)
+        attn = {n: v for (n, _), v in means.items()
+                if "attn_mfma_kernel" in n or "attn_combine_kernel" in n}
+        kib = sum(attn.values())
+        out["counters"][counter] = {"attention_kib_per_call": round(kib, 3),
+                                    "copy_kib": round(cal, 3), "scale": round(scale, 5),
+                                    "bytes_per_call": int(kib * 1024.0 * scale),
+                                    "kernels": sorted(attn)}
+        total += kib * 1024.0 * scale
+    out["bytes_per_call"] = int(total)
+    path = os.path.join(ROOT, "profiles", "traffic_attn_%s.json" % workload)
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out))
+
+
+class HipEvent:
+    """A HIP event on torch's current stream, created with
+    hipEventDisableSystemFence: recording it skips the system-scope fence
+    (an L2 writeback) that a default event performs, which would otherwise be
+    counted inside the interval it bounds."""
+    _rt = None
+
+    @classmethod
+    def runtime(cls):
+        if cls._rt is None:
+            import ctypes
+            path = next(l.split()[-1] for l in open("/proc/self/maps") if "libamdhip64" in l)
+            rt = ctypes.CDLL(path)     # the runtime torch already loaded
+            rt.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            rt.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            rt.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                               ctypes.c_void_p]
+            rt.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            cls._rt = rt
+        return cls._rt
+
+    def __init__(self):
+        import ctypes
+        self.h = ctypes.c_void_p()
+        assert self.runtime().hipEventCreateWithFlags(ctypes.byref(self.h), 0x20000000) == 0
+
+    def record(self):
+        import torch
+        assert self.runtime().hipEventRecord(self.h, torch.cuda.current_stream().cuda_stream) == 0
+
+    def elapsed_time(self, end):
+        """Milliseconds from this event to `end` (both complete)."""
+        import ctypes
+        ms = ctypes.c_float()
+        assert self.runtime().hipEventElapsedTime(ctypes.byref(ms), self.h, end.h) == 0
+        return ms.value
+
+    def __del__(self):
+        if self._rt is not None and self.h:
+            self._rt.hipEventDestroy(self.h)
+
+
 class Workload:
     def __init__(self, name):
         import torch
@@ -190,7 +278,7 @@ def time_calls(w, reps=10):
     def loop(fn):
         fn()
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0, e1 = HipEvent(), HipEvent()
         e0.record()
         for _ in range(reps):
             fn()
@@ -264,6 +352,10 @@ def cpu_baseline(w, budget_s):
 
 def main():
     args = parse()
+    if args.write_traffic:
+        write_traffic(args.workload, args.write_traffic[0], args.write_traffic[1],
+                      args.copy_calibration or 1024)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -277,8 +369,7 @@ def main():
     for _ in range(args.warmup):
         w.step()
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+    evs = [(HipEvent(), HipEvent()) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
@@ -326,7 +417,7 @@ def main():
         "config": {"workload": cfg.name, "B": cfg.B, "T": cfg.T, "Hq": cfg.Hq, "Hkv": cfg.Hkv,
                    "D": cfg.D, "ctx": [cfg.ctx_lo, cfg.ctx_hi], "block": cfg.bs, "V": cfg.V,
                    "accept": cfg.mode, "temperature": w.tau, "topk": cfg.topk or None},
-        "roofline": dict(roof, kernel="sd_tree_verify_attn (ancestor masks + attention)",
+        "roofline": dict(roof, kernel="sd_tree_verify_attn (tree-masked attention kernel)",
                          attention_us=round(attn_s * 1e6, 2), bytes_per_call=int(bytes_),
                          flops_per_call=int(flops)),
         "cpu_baseline": cpu,
