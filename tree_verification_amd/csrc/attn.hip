@@ -177,7 +177,9 @@ __global__ void __launch_bounds__(256) attn_valu_kernel(AttnArgs a) {
 constexpr float kLazy = 8.0f;
 
 template <int D, int QW, int WQ, int WK, int KW, int S>
-__global__ void __launch_bounds__(256, 1) attn_mfma_kernel(AttnArgs a) {
+__global__ void __launch_bounds__(WQ * WK * 64) attn_mfma_kernel(AttnArgs a) {
+  constexpr int NWAVE = WQ * WK;
+  constexpr int NT = NWAVE * 64;
   constexpr int NK = KW * WK;
   constexpr int ROWS = WQ * QW;
   constexpr int QB = QW / 16;
@@ -188,12 +190,12 @@ __global__ void __launch_bounds__(256, 1) attn_mfma_kernel(AttnArgs a) {
   constexpr int CV = NK / 8;                     // 16-byte chunks per V^T row
   constexpr int K_BYTES = NK * D * 2;
   constexpr int V_BYTES = D * NK * 2;
-  constexpr int K_OPS = K_BYTES / (256 * 16);    // DMA instructions per thread per tile
-  constexpr int V_OPS = V_BYTES / (256 * 16);
+  constexpr int K_OPS = K_BYTES / (NT * 16);     // DMA instructions per thread per tile
+  constexpr int V_OPS = V_BYTES / (NT * 16);
   constexpr int OPS = K_OPS + V_OPS;
-  static_assert(K_OPS * 256 * 16 == K_BYTES && V_OPS * 256 * 16 == V_BYTES, "tile split");
-  static_assert(WQ * WK == 4, "four wavefronts");
-  static_assert(S >= 2 && (S - 2) * OPS <= 63, "vmcnt range");
+  static_assert(K_OPS * NT * 16 == K_BYTES && V_OPS * NT * 16 == V_BYTES, "tile split");
+  static_assert(NWAVE == 4 || NWAVE == 8, "four or eight wavefronts");
+  static_assert(S >= 2 && (S - 1) * OPS <= 63, "vmcnt range");
 
   // Swizzles: chunk c of K row r sits at position c ^ kswz(r); chunk c of V^T
   // row d at c ^ vswz(d).  (Rows one MFMA operand reads: 16 K rows
@@ -280,11 +282,11 @@ __global__ void __launch_bounds__(256, 1) attn_mfma_kernel(AttnArgs a) {
   const int nn = i_hi - i_lo + 1;
   if (tid < 128) tflag[tid] = 0;
   if (tid == 0) s_err = 0;
-  for (int j = tid; j <= i_hi; j += 256) s_par[j] = a.parent[(size_t)bt * T + j];
-  for (int idx = tid; idx < nn * a.W64; idx += 256) ancL[idx] = 0ull;
+  for (int j = tid; j <= i_hi; j += NT) s_par[j] = a.parent[(size_t)bt * T + j];
+  for (int idx = tid; idx < nn * a.W64; idx += NT) ancL[idx] = 0ull;
   __syncthreads();
   int err = 0;
-  for (int idx = tid; idx < nn; idx += 256) {
+  for (int idx = tid; idx < nn; idx += NT) {
     uint64_t* row = ancL + idx * a.W64;
     int n = i_lo + idx, cur_w = n >> 6;
     uint64_t acc = 0;
@@ -316,12 +318,12 @@ __global__ void __launch_bounds__(256, 1) attn_mfma_kernel(AttnArgs a) {
   uint32_t* rowbits = reinterpret_cast<uint32_t*>(Uphys + a.u_max);
   int nU = 0;
   if (sparse) {
-    for (int w = tid; w < BW; w += 256) ubits[w] = 0;
-    for (int w = tid; w < ROWS * UW; w += 256) rowbits[w] = 0;
+    for (int w = tid; w < BW; w += NT) ubits[w] = 0;
+    for (int w = tid; w < ROWS * UW; w += NT) rowbits[w] = 0;
     __syncthreads();
     const int nsel = max(r_hi - row0, 0) * a.ksel;
     if (cap_ok) {
-      for (int idx = tid; idx < nsel; idx += 256) {
+      for (int idx = tid; idx < nsel; idx += NT) {
         const int r = row0 + idx / a.ksel, e = idx % a.ksel;
         const int i = r / G, h = g * G + r % G;
         const int32_t* sr = a.sel + (((size_t)b * T + i) * a.Hq + h) * a.ksel;
@@ -345,7 +347,7 @@ __global__ void __launch_bounds__(256, 1) attn_mfma_kernel(AttnArgs a) {
     }
     __syncthreads();
     nU = s_nU;
-    for (int w = tid; w < BW; w += 256) {
+    for (int w = tid; w < BW; w += NT) {
       uint32_t bits = ubits[w];
       int o = upre[w];
       while (bits) {
@@ -363,7 +365,7 @@ __global__ void __launch_bounds__(256, 1) attn_mfma_kernel(AttnArgs a) {
       }
     }
     if (cap_ok) {
-      for (int idx = tid; idx < nsel; idx += 256) {
+      for (int idx = tid; idx < nsel; idx += NT) {
         const int rl = idx / a.ksel, e = idx % a.ksel;
         const int r = row0 + rl;
         const int i = r / G, h = g * G + r % G;
@@ -399,7 +401,7 @@ __global__ void __launch_bounds__(256, 1) attn_mfma_kernel(AttnArgs a) {
   const int tcount = (cap_ok && t_hi > nct) ? ((ctx + T - 1) >> bsh) - tb0 + 1 : 0;
   const long long blk_elems = (long long)a.Hkv * bs * D;
   const long long head_off = (long long)g * bs * D;   // head g inside a K or a V block
-  for (int j = tid; j < ccount + tcount; j += 256) {
+  for (int j = tid; j < ccount + tcount; j += NT) {
     const int n = j < ccount ? cb0 + j : tb0 + (j - ccount);
     int phys = table[n];
     if (phys < 0 || phys >= a.num_blocks) {
@@ -417,7 +419,7 @@ __global__ void __launch_bounds__(256, 1) attn_mfma_kernel(AttnArgs a) {
 
   // Logical position of key k of tile t (< 0: none) and the element offset of
   // its (block, head g).
-  auto key_at = [&](int t, int k, long long& boff) -> int {
+  auto key_at = [&](int t, int k, long long& boff) __attribute__((always_inline)) -> int {
     if (t < nct) {
       if (!sparse) {
         const int p = t * NK + k;
@@ -440,7 +442,7 @@ __global__ void __launch_bounds__(256, 1) attn_mfma_kernel(AttnArgs a) {
     return p;
   };
   // Do the 8-key chunks of tile t copy whole (8-aligned, all valid or all not)?
-  auto v_clean = [&](int t) -> bool {
+  auto v_clean = [&](int t) __attribute__((always_inline)) -> bool {
     if ((ctx & 7) == 0) return t < nct || ((t - nct) * NK + NK <= T) || (T & 7) == 0;
     return t < nct && !sparse && t * NK + NK <= ctx;
   };
@@ -452,34 +454,28 @@ __global__ void __launch_bounds__(256, 1) attn_mfma_kernel(AttnArgs a) {
   int k_row[K_OPS], k_col[K_OPS], v_row[V_OPS], v_key[V_OPS];
 #pragma unroll
   for (int n = 0; n < K_OPS; ++n) {
-    const int sl = lane + 64 * (wave + 4 * n);
+    const int sl = lane + 64 * (wave + NWAVE * n);
     k_row[n] = sl / CK;
     k_col[n] = ((sl % CK) ^ kswz(sl / CK)) * 8;
   }
 #pragma unroll
   for (int n = 0; n < V_OPS; ++n) {
-    const int sl = lane + 64 * (wave + 4 * n);
+    const int sl = lane + 64 * (wave + NWAVE * n);
     v_row[n] = sl / CV;
     v_key[n] = ((sl % CV) ^ vswz(sl / CV)) * 8;
   }
 
-  // Issue the loads of tile t into ring slot `slot`.
-  auto issue = [&](int t, int slot) {
+  // Issue the loads of tile t's K (issue_k) or V^T (issue_v) into ring slot
+  // `slot`.  Every thread issues the same number of DMA operations.
+  auto dense_full = [&](int t) { return t < nct && !sparse && t * NK + NK <= ctx; };
+  auto issue_k = [&](int t, int slot) __attribute__((always_inline)) {
     unsigned char* kst = Kst + slot * K_BYTES;
-    unsigned char* vst = Vst + slot * V_BYTES;
-    if (t < nct && !sparse && t * NK + NK <= ctx) {
-      // whole dense context tile: block bases from the staged table
+    if (dense_full(t)) {
 #pragma unroll
       for (int n = 0; n < K_OPS; ++n) {
         const int p = t * NK + k_row[n];
         const bf16_bits* src = Kp + ctab[(p >> bsh) - cb0] + (long long)((p & bsm) * D + k_col[n]);
-        __builtin_amdgcn_global_load_lds(src, kst + (wave + 4 * n) * 1024, 16, 0, 0);
-      }
-#pragma unroll
-      for (int n = 0; n < V_OPS; ++n) {
-        const int p = t * NK + v_key[n];
-        const bf16_bits* src = Vp + ctab[(p >> bsh) - cb0] + (long long)(v_row[n] * bs + (p & bsm));
-        __builtin_amdgcn_global_load_lds(src, vst + (wave + 4 * n) * 1024, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(src, kst + (wave + NWAVE * n) * 1024, 16, 0, 0);
       }
       return;
     }
@@ -488,7 +484,19 @@ __global__ void __launch_bounds__(256, 1) attn_mfma_kernel(AttnArgs a) {
       long long boff = 0;
       const int p = key_at(t, k_row[n], boff);
       const bf16_bits* src = p >= 0 ? Kp + boff + (long long)((p & bsm) * D + k_col[n]) : zeros;
-      __builtin_amdgcn_global_load_lds(src, kst + (wave + 4 * n) * 1024, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(src, kst + (wave + NWAVE * n) * 1024, 16, 0, 0);
+    }
+  };
+  auto issue_v = [&](int t, int slot) __attribute__((always_inline)) {
+    unsigned char* vst = Vst + slot * V_BYTES;
+    if (dense_full(t)) {
+#pragma unroll
+      for (int n = 0; n < V_OPS; ++n) {
+        const int p = t * NK + v_key[n];
+        const bf16_bits* src = Vp + ctab[(p >> bsh) - cb0] + (long long)(v_row[n] * bs + (p & bsm));
+        __builtin_amdgcn_global_load_lds(src, vst + (wave + NWAVE * n) * 1024, 16, 0, 0);
+      }
+      return;
     }
     if (v_clean(t)) {
 #pragma unroll
@@ -496,10 +504,11 @@ __global__ void __launch_bounds__(256, 1) attn_mfma_kernel(AttnArgs a) {
         long long boff = 0;
         const int p = key_at(t, v_key[n], boff);
         const bf16_bits* src = p >= 0 ? Vp + boff + (long long)(v_row[n] * bs + (p & bsm)) : zeros;
-        __builtin_amdgcn_global_load_lds(src, vst + (wave + 4 * n) * 1024, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(src, vst + (wave + NWAVE * n) * 1024, 16, 0, 0);
       }
     } else {
-      // assemble each 8-key chunk element by element (zeros past the edge)
+      // assemble each 8-key chunk element by element (zeros past the edge);
+      // these plain loads are waited for here, so the DMA counts stay exact
 #pragma unroll
       for (int n = 0; n < V_OPS; ++n) {
         uint32_t w[4] = {0, 0, 0, 0};
@@ -508,7 +517,7 @@ __global__ void __launch_bounds__(256, 1) attn_mfma_kernel(AttnArgs a) {
           const int p = key_at(t, v_key[n] + e, boff);
           if (p >= 0) w[e >> 1] |= (uint32_t)Vp[boff + v_row[n] * bs + (p & bsm)] << (16 * (e & 1));
         }
-        const int sl = lane + 64 * (wave + 4 * n);
+        const int sl = lane + 64 * (wave + NWAVE * n);
         *reinterpret_cast<uint4*>(vst + sl * 16) = make_uint4(w[0], w[1], w[2], w[3]);
       }
     }
@@ -534,11 +543,12 @@ __global__ void __launch_bounds__(256, 1) attn_mfma_kernel(AttnArgs a) {
     rloc[qb] = r - row0;
   }
   const int kbase = wk * KW;
+  typedef f32x4 STile[QB][2 * KG];
+  typedef bf16x8 PTile[QB][KG];
 
-  auto compute_tile = [&](int slot, int t) {
+  // S^T = K Q^T for this wave's keys of the tile in ring slot `slot`.
+  auto qk = [&](int slot, STile& s) __attribute__((always_inline)) {
     const unsigned char* Kt = Kst + slot * K_BYTES;
-    const unsigned char* Vt = Vst + slot * V_BYTES;
-    f32x4 s[QB][2 * KG];
 #pragma unroll
     for (int kg = 0; kg < KG; ++kg) {
 #pragma unroll
@@ -557,77 +567,85 @@ __global__ void __launch_bounds__(256, 1) attn_mfma_kernel(AttnArgs a) {
         }
       }
     }
-    // visibility of this lane's 8 keys per 32-key group
-    uint32_t vis[QB][KG];
-    const bool full_ctx = (t < nct) && !sparse && (t * NK + NK <= ctx);
+  };
+
+  // Masks the scores of tile t that a query column may not see.
+  auto mask_tile = [&](int t, STile& s) __attribute__((always_inline)) {
 #pragma unroll
     for (int kg = 0; kg < KG; ++kg) {
       const int k0 = kbase + 32 * kg + 8 * lg;
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        uint32_t bits = 0xFFu;
-        if (!full_ctx) {
-          if (t < nct) {
-            if (!sparse) {
-              const int p = t * NK + k0;
-              bits = p >= ctx ? 0u : (p + 8 <= ctx ? 0xFFu : ((1u << (ctx - p)) - 1u));
-            } else {
-              const int vi = t * NK + k0;
-              const int e = vi >> bsh;
-              bits = 0u;
-              if (e < nU && node[qb] >= 0 &&
-                  ((rowbits[rloc[qb] * UW + (e >> 5)] >> (e & 31)) & 1u)) {
-                const int p = (U[e] << bsh) + (vi & bsm);
-                bits = p >= ctx ? 0u : (p + 8 <= ctx ? 0xFFu : ((1u << (ctx - p)) - 1u));
-              }
-            }
+        uint32_t bits;
+        if (t < nct) {
+          if (!sparse) {
+            const int p = t * NK + k0;
+            bits = p >= ctx ? 0u : (p + 8 <= ctx ? 0xFFu : ((1u << (ctx - p)) - 1u));
           } else {
-            const int j0 = (t - nct) * NK + k0;
+            const int vi = t * NK + k0;
+            const int e = vi >> bsh;
             bits = 0u;
-            if (node[qb] >= 0 && j0 < T) {
-              const uint64_t word = ancL[(node[qb] - i_lo) * a.W64 + (j0 >> 6)];
-              bits = (uint32_t)(word >> (j0 & 63)) & 0xFFu;
+            if (e < nU && node[qb] >= 0 &&
+                ((rowbits[rloc[qb] * UW + (e >> 5)] >> (e & 31)) & 1u)) {
+              const int p = (U[e] << bsh) + (vi & bsm);
+              bits = p >= ctx ? 0u : (p + 8 <= ctx ? 0xFFu : ((1u << (ctx - p)) - 1u));
             }
           }
+        } else {
+          const int j0 = (t - nct) * NK + k0;
+          bits = 0u;
+          if (node[qb] >= 0 && j0 < T) {
+            const uint64_t word = ancL[(node[qb] - i_lo) * a.W64 + (j0 >> 6)];
+            bits = (uint32_t)(word >> (j0 & 63)) & 0xFFu;
+          }
         }
-        vis[qb][kg] = bits;
-      }
-    }
-    // online softmax on raw scores; scale folded into the exponent.  The
-    // reference max m_run is only raised when a score exceeds it by more than
-    // 2^kLazy, so p <= 2^kLazy and the accumulators are rarely rescaled.
-    bf16x8 pf[QB][KG];
-    const float c = a.scale_log2;
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      float mx = -INFINITY;
-      if (!full_ctx) {
-#pragma unroll
-        for (int kg = 0; kg < KG; ++kg)
-#pragma unroll
-          for (int half = 0; half < 2; ++half)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-              if (!((vis[qb][kg] >> (4 * half + j)) & 1u)) s[qb][2 * kg + half][j] = -INFINITY;
-      }
-#pragma unroll
-      for (int kg = 0; kg < KG; ++kg)
 #pragma unroll
         for (int half = 0; half < 2; ++half)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) mx = fmaxf(mx, s[qb][2 * kg + half][j]);
+          for (int j = 0; j < 4; ++j)
+            if (!((bits >> (4 * half + j)) & 1u)) s[qb][2 * kg + half][j] = -INFINITY;
+      }
+    }
+  };
+
+  // Online softmax of one tile's (masked) scores; the scale is folded into the
+  // exponent.  The reference max m_run is only raised when a score exceeds it
+  // by more than 2^kLazy, so p <= 2^kLazy and the accumulators are rarely
+  // rescaled.
+  const float c = a.scale_log2;
+  auto row_max = [&](const STile& s, float (&ms)[QB]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int e = 0; e < 2 * KG; ++e)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) mx = fmaxf(mx, s[qb][e][j]);
       mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float ms = mx * c;
-      const bool raise = ms > m_run[qb] + kLazy;
-      if (__builtin_amdgcn_ballot_w64(raise)) {
-        const float mn = raise ? ms : m_run[qb];
+      ms[qb] = mx * c;
+    }
+  };
+  auto rescale = [&](const float (&ms)[QB]) __attribute__((always_inline)) {
+    bool any = false;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) any |= ms[qb] > m_run[qb] + kLazy;
+    if (__builtin_amdgcn_ballot_w64(any)) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const bool raise = ms[qb] > m_run[qb] + kLazy;
+        const float mn = raise ? ms[qb] : m_run[qb];
         const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - mn);
         m_run[qb] = mn;
         l_run[qb] *= alpha;
 #pragma unroll
         for (int db = 0; db < DB; ++db) o[qb][db] *= alpha;
       }
+    }
+  };
+  auto exp_tile = [&](const STile& s, PTile& pf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
       const float nm = -m_run[qb];
       float lsum = 0.f;
 #pragma unroll
@@ -648,15 +666,18 @@ __global__ void __launch_bounds__(256, 1) attn_mfma_kernel(AttnArgs a) {
       }
       l_run[qb] += lsum;
     }
-    // O^T += V^T P^T
+  };
+  // O^T += V^T P^T for the tile in ring slot `slot`.
+  auto pv = [&](int slot, const PTile& pf) __attribute__((always_inline)) {
+    const unsigned char* Vt = Vst + slot * V_BYTES;
 #pragma unroll
     for (int kg = 0; kg < KG; ++kg) {
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         const int d = db * 16 + l16;
-        const int c = (kbase + 32 * kg + 8 * lg) >> 3;
+        const int cc = (kbase + 32 * kg + 8 * lg) >> 3;
         const bf16x8 va =
-            *reinterpret_cast<const bf16x8*>(Vt + d * (NK * 2) + ((c ^ vswz(d)) * 16));
+            *reinterpret_cast<const bf16x8*>(Vt + d * (NK * 2) + ((cc ^ vswz(d)) * 16));
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
           o[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pf[qb][kg], o[qb][db], 0, 0, 0);
@@ -664,32 +685,75 @@ __global__ void __launch_bounds__(256, 1) attn_mfma_kernel(AttnArgs a) {
     }
   };
 
-  // ---- main loop: S-stage ring, loads issued S - 1 tiles ahead --------------
-  // Drain the set-up loads so that inside the loop the only vector-memory
-  // operations in flight are the ring's; each tile is then waited for with
-  // vmcnt(tiles issued after it * OPS).
-  __builtin_amdgcn_s_waitcnt(0);
-#pragma unroll
-  for (int k = 0; k < S - 1; ++k)
-    if (k < nuse) issue(tile_at(k), k);
-  for (int k = 0; k < nuse; ++k) {
-    const int ahead = min(S - 2, nuse - 1 - k);
-    if constexpr (S >= 4) {
-      if (ahead >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * OPS));
-      else if (ahead == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(OPS));
-      else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    } else if constexpr (S == 3) {
-      if (ahead >= 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(OPS));
-      else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    } else {
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    }
+  // One tile: scores, mask (unless the tile is a whole dense context tile),
+  // online softmax, P V.
+  auto compute_tile = [&](int slot, int t, bool masked) __attribute__((always_inline)) {
+    STile s;
+    qk(slot, s);
+    if (masked) mask_tile(t, s);
+    float ms[QB];
+    row_max(s, ms);
+    rescale(ms);
+    PTile pf;
+    exp_tile(s, pf);
+    pv(slot, pf);
+  };
+  auto sync_tiles = [&](int vm) __attribute__((always_inline)) {
+    if (vm == 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * OPS));
+    else if (vm == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(OPS));
+    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __builtin_amdgcn_s_waitcnt(lgkmcnt_imm(0));
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if (k + S - 1 < nuse) issue(tile_at(k + S - 1), (k + S - 1) % S);
-    compute_tile(k % S, tile_at(k));
+  };
+
+  // ---- main loop: S-stage ring, tile k + S - 1 issued while tile k computes --
+  // Every thread issues the same DMA operations per tile, so tile k has landed
+  // once at most the operations of the (up to S - 2) tiles issued after it are
+  // outstanding.  The leading whole dense context tiles run in a tight loop
+  // whose prefetches are whole dense tiles too; the remaining tiles (context
+  // tail, tree tiles, sparse tiles) run in the general loop.  The set-up loads
+  // are drained first.
+  __builtin_amdgcn_s_waitcnt(0);
+#pragma unroll
+  for (int k = 0; k < S - 1; ++k)
+    if (k < nuse) {
+      issue_k(tile_at(k), k);
+      issue_v(tile_at(k), k);
+    }
+  const int n_full = sparse ? 0 : max(0, min(t_hi, ctx / NK) - t_lo);
+  const int n_tight = max(0, n_full - (S - 1));
+  int k = 0;
+  for (; k < n_tight; ++k) {
+    sync_tiles(S - 2 >= 2 ? 2 : S - 2);
+    const int tn = t_lo + k + S - 1;
+    const int sn = (k + S - 1) % S;
+    unsigned char* kst = Kst + sn * K_BYTES;
+    unsigned char* vst = Vst + sn * V_BYTES;
+#pragma unroll
+    for (int n = 0; n < K_OPS; ++n) {
+      const int p = tn * NK + k_row[n];
+      const bf16_bits* src = Kp + ctab[(p >> bsh) - cb0] + (long long)((p & bsm) * D + k_col[n]);
+      __builtin_amdgcn_global_load_lds(src, kst + (wave + NWAVE * n) * 1024, 16, 0, 0);
+    }
+#pragma unroll
+    for (int n = 0; n < V_OPS; ++n) {
+      const int p = tn * NK + v_key[n];
+      const bf16_bits* src = Vp + ctab[(p >> bsh) - cb0] + (long long)(v_row[n] * bs + (p & bsm));
+      __builtin_amdgcn_global_load_lds(src, vst + (wave + NWAVE * n) * 1024, 16, 0, 0);
+    }
+    compute_tile(k % S, t_lo + k, false);
+  }
+  for (; k < nuse; ++k) {
+    const int ahead = min(S - 2, nuse - 1 - k);
+    sync_tiles(ahead >= 2 ? 2 : ahead);
+    if (k + S - 1 < nuse) {
+      issue_k(tile_at(k + S - 1), (k + S - 1) % S);
+      issue_v(tile_at(k + S - 1), (k + S - 1) % S);
+    }
+    const int t = tile_at(k);
+    compute_tile(k % S, t, !dense_full(t));
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -701,9 +765,9 @@ __global__ void __launch_bounds__(256, 1) attn_mfma_kernel(AttnArgs a) {
     l_run[qb] += __shfl_xor(l_run[qb], 32);
   }
   if constexpr (WK > 1) {
-    float* xm = reinterpret_cast<float*>(smem);  // [4][QW]
-    float* xl = xm + 4 * QW;                     // [4][QW]
-    float* xo = xl + 4 * QW;                     // [4][QW][D]
+    float* xm = reinterpret_cast<float*>(smem);  // [NWAVE][QW]
+    float* xl = xm + NWAVE * QW;                 // [NWAVE][QW]
+    float* xo = xl + NWAVE * QW;                 // [NWAVE][QW][D]
     if (wk > 0) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
@@ -833,7 +897,7 @@ static hipError_t launch_mfma_cfg(const AttnArgs& a, size_t lds, hipStream_t st)
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   const unsigned nwg = (unsigned)a.B * a.Hkv * a.n_qtiles * a.n_splits;
-  hipLaunchKernelGGL(fn, dim3(nwg), dim3(256), lds, st, a);
+  hipLaunchKernelGGL(fn, dim3(nwg), dim3(WQ * WK * 64), lds, st, a);
   return hipGetLastError();
 }
 
@@ -844,9 +908,9 @@ static hipError_t launch_mfma_d(const AttnArgs& a, const AttnPlan& p, hipStream_
     if (p.stages == 4) return launch_mfma_cfg<D, 32, 2, 2, 32, 4>(a, p.lds_bytes, st);
     return launch_mfma_cfg<D, 32, 2, 2, 32, 2>(a, p.lds_bytes, st);
   }
-  if (p.stages == 4) return launch_mfma_cfg<D, 32, 4, 1, 64, 4>(a, p.lds_bytes, st);
-  if (p.stages == 3) return launch_mfma_cfg<D, 32, 4, 1, 64, 3>(a, p.lds_bytes, st);
-  return launch_mfma_cfg<D, 32, 4, 1, 64, 2>(a, p.lds_bytes, st);
+  if (p.stages == 4) return launch_mfma_cfg<D, 32, 4, 2, 32, 4>(a, p.lds_bytes, st);
+  if (p.stages == 3) return launch_mfma_cfg<D, 32, 4, 2, 32, 3>(a, p.lds_bytes, st);
+  return launch_mfma_cfg<D, 32, 4, 2, 32, 2>(a, p.lds_bytes, st);
 }
 
 hipError_t launch_attn_mfma(const AttnArgs& a, const AttnPlan& p, hipStream_t st) {

@@ -57,7 +57,9 @@ static AttnPlan plan_attn(const sd_shape* s, int ksel, bool sparse) {
   } else if (M <= 64) {
     p.WQ = 2; p.WK = 2; p.QW = 32; p.KW = 32;
   } else {
-    p.WQ = 4; p.WK = 1; p.QW = 32; p.KW = 64;
+    // eight wavefronts: four 32-row query slices x two 32-key slices, two
+    // wavefronts per SIMD so one's MFMAs overlap the other's softmax
+    p.WQ = 4; p.WK = 2; p.QW = 32; p.KW = 32;
   }
   p.NK = p.KW * p.WK;
   p.rows = p.WQ * p.QW;
@@ -96,21 +98,21 @@ static AttnPlan plan_attn(const sd_shape* s, int ksel, bool sparse) {
   }
   p.anc_lds_words = (int)anc_need;
   extras += 8 * anc_need;
-  // deepest ring that fits: 4 or 3 stages for the wide tile, 4 or 2 for the
-  // middle one, 2 for the key-sliced one
+  // deepest ring that fits: 4, 3 or 2 stages for the wide tile, 4 or 2 for
+  // two key slices, 2 for four key slices
   const int cand[3] = {4, 3, 2};
   p.stages = 0;
   for (int c : cand) {
     if (p.WQ == 1 && c != 2) continue;
     if (p.WQ == 2 && c == 3) continue;
-    const size_t merge = p.WK > 1 ? (size_t)4 * (p.QW * p.D + 2 * p.QW) * 4 : 0;
+    const size_t merge = p.WK > 1 ? (size_t)p.WQ * p.WK * (p.QW * p.D + 2 * p.QW) * 4 : 0;
     if (std::max(c * stage, merge) + extras <= kLdsLimit) {
       p.stages = c;
       break;
     }
   }
   if (p.stages == 0) p.stages = 2;   // reported as SD_UNSUPPORTED by the LDS check
-  const size_t merge = p.WK > 1 ? (size_t)4 * (p.QW * p.D + 2 * p.QW) * 4 : 0;
+  const size_t merge = p.WK > 1 ? (size_t)p.WQ * p.WK * (p.QW * p.D + 2 * p.QW) * 4 : 0;
   size_t lds = std::max(p.stages * stage, merge) + extras;
   p.lds_bytes = align_up(lds, 16);
   const size_t nrows = (size_t)s->B * s->T * s->Hq;
