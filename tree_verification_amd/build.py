@@ -49,7 +49,9 @@ def build(verbose=False):
             sys.stderr.write(err)
     objs = [o for o, _ in results]
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
+    # -z defs: every symbol must resolve (a kernel whose host stub was not
+    # emitted shows up here rather than at load time)
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-Wl,-z,defs", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n%s" % r.stderr)

@@ -466,7 +466,10 @@ __global__ void __launch_bounds__(WQ * WK * 64) attn_mfma_kernel(AttnArgs a) {
   }
 
   // Issue the loads of tile t's K (issue_k) or V^T (issue_v) into ring slot
-  // `slot`.  Every thread issues the same number of DMA operations.
+  // `slot`.  Every thread issues the same number of DMA operations.  The LDS
+  // DMA builtin is always given a named pointer variable: handed an array
+  // element directly, the host compilation pass silently drops the kernel's
+  // launch stub (the link check in the build catches that).
   auto dense_full = [&](int t) { return t < nct && !sparse && t * NK + NK <= ctx; };
   auto issue_k = [&](int t, int slot) __attribute__((always_inline)) {
     unsigned char* kst = Kst + slot * K_BYTES;
@@ -524,6 +527,8 @@ __global__ void __launch_bounds__(WQ * WK * 64) attn_mfma_kernel(AttnArgs a) {
   };
 
   // ---- per-lane softmax state ----------------------------------------------
+  // l_run: this lane's share of its column's sum of p (summed over the four
+  // lanes of the column at the end).
   float m_run[QB], l_run[QB];
   f32x4 o[QB][DB];
 #pragma unroll
@@ -613,7 +618,13 @@ __global__ void __launch_bounds__(WQ * WK * 64) attn_mfma_kernel(AttnArgs a) {
   // by more than 2^kLazy, so p <= 2^kLazy and the accumulators are rarely
   // rescaled.
   const float c = a.scale_log2;
-  auto row_max = [&](const STile& s, float (&ms)[QB]) __attribute__((always_inline)) {
+  // The reference max m_run of a query column only has to bound the column's
+  // scores to within 2^kLazy.  Each lane checks its own scores; only when some
+  // lane exceeds the bound is the exact column max formed (across the four
+  // lanes holding the column) and m_run raised, rescaling o and l.
+  auto softmax_bound = [&](const STile& s) __attribute__((always_inline)) {
+    float lm[QB];
+    bool any = false;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       float mx = -INFINITY;
@@ -621,20 +632,18 @@ __global__ void __launch_bounds__(WQ * WK * 64) attn_mfma_kernel(AttnArgs a) {
       for (int e = 0; e < 2 * KG; ++e)
 #pragma unroll
         for (int j = 0; j < 4; ++j) mx = fmaxf(mx, s[qb][e][j]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      ms[qb] = mx * c;
+      lm[qb] = mx;
+      any |= mx * c > m_run[qb] + kLazy;
     }
-  };
-  auto rescale = [&](const float (&ms)[QB]) __attribute__((always_inline)) {
-    bool any = false;
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) any |= ms[qb] > m_run[qb] + kLazy;
     if (__builtin_amdgcn_ballot_w64(any)) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        const bool raise = ms[qb] > m_run[qb] + kLazy;
-        const float mn = raise ? ms[qb] : m_run[qb];
+        float mx = lm[qb];
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float ms = mx * c;
+        const bool raise = ms > m_run[qb] + kLazy;
+        const float mn = raise ? ms : m_run[qb];
         const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - mn);
         m_run[qb] = mn;
         l_run[qb] *= alpha;
@@ -647,7 +656,6 @@ __global__ void __launch_bounds__(WQ * WK * 64) attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       const float nm = -m_run[qb];
-      float lsum = 0.f;
 #pragma unroll
       for (int kg = 0; kg < KG; ++kg) {
         bf16x8 pk;
@@ -657,14 +665,13 @@ __global__ void __launch_bounds__(WQ * WK * 64) attn_mfma_kernel(AttnArgs a) {
           for (int j = 0; j < 4; j += 2) {
             const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][2 * kg + half][j], c, nm));
             const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][2 * kg + half][j + 1], c, nm));
-            lsum += p0 + p1;
+            l_run[qb] += p0 + p1;
             const bf16x2 pp = __builtin_convertvector((f32x2){p0, p1}, bf16x2);
             pk[4 * half + j] = pp[0];
             pk[4 * half + j + 1] = pp[1];
           }
         pf[qb][kg] = pk;
       }
-      l_run[qb] += lsum;
     }
   };
   // O^T += V^T P^T for the tile in ring slot `slot`.
@@ -685,22 +692,8 @@ __global__ void __launch_bounds__(WQ * WK * 64) attn_mfma_kernel(AttnArgs a) {
     }
   };
 
-  // One tile: scores, mask (unless the tile is a whole dense context tile),
-  // online softmax, P V.
-  auto compute_tile = [&](int slot, int t, bool masked) __attribute__((always_inline)) {
-    STile s;
-    qk(slot, s);
-    if (masked) mask_tile(t, s);
-    float ms[QB];
-    row_max(s, ms);
-    rescale(ms);
-    PTile pf;
-    exp_tile(s, pf);
-    pv(slot, pf);
-  };
-  auto sync_tiles = [&](int vm) __attribute__((always_inline)) {
-    if (vm == 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * OPS));
-    else if (vm == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(OPS));
+  auto sync_tiles = [&](bool exact) __attribute__((always_inline)) {
+    if (exact) __builtin_amdgcn_s_waitcnt(vmcnt_imm((S - 2) * OPS));
     else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __builtin_amdgcn_s_waitcnt(lgkmcnt_imm(0));
     asm volatile("" ::: "memory");
@@ -708,13 +701,19 @@ __global__ void __launch_bounds__(WQ * WK * 64) attn_mfma_kernel(AttnArgs a) {
     asm volatile("" ::: "memory");
   };
 
-  // ---- main loop: S-stage ring, tile k + S - 1 issued while tile k computes --
-  // Every thread issues the same DMA operations per tile, so tile k has landed
-  // once at most the operations of the (up to S - 2) tiles issued after it are
-  // outstanding.  The leading whole dense context tiles run in a tight loop
-  // whose prefetches are whole dense tiles too; the remaining tiles (context
-  // tail, tree tiles, sparse tiles) run in the general loop.  The set-up loads
-  // are drained first.
+  // ---- main loop --------------------------------------------------------------
+  // K and V^T have rings of S slots each.  Tile k's scores are computed one
+  // iteration ahead, so iteration k reads K(k + 1) and V(k): it runs the score
+  // MFMAs of tile k + 1 beside the softmax of tile k, then tile k's P V.  It
+  // then issues K(k + S) into K(k)'s slot (last read in iteration k - 1) and
+  // V(k + S - 1) into V(k - 1)'s slot.  Every thread issues the same DMA
+  // operations, so K(k + 1) and V(k), issued together in iteration
+  // k + 1 - S, have landed once at most the (S - 2) later iterations'
+  // operations are outstanding; near the end that count is not exact and
+  // everything is drained instead.  The leading whole dense context tiles run
+  // in a tight loop (an even number of iterations whose prefetches are whole
+  // dense tiles too); the rest (context tail, tree tiles, sparse tiles) in the
+  // general loop.  The set-up loads are drained first.
   __builtin_amdgcn_s_waitcnt(0);
 #pragma unroll
   for (int k = 0; k < S - 1; ++k)
@@ -722,38 +721,95 @@ __global__ void __launch_bounds__(WQ * WK * 64) attn_mfma_kernel(AttnArgs a) {
       issue_k(tile_at(k), k);
       issue_v(tile_at(k), k);
     }
+  if (S - 1 < nuse) issue_k(tile_at(S - 1), S - 1);
+  STile sa, sb;
+  PTile pf;
+  if (nuse > 0) {
+    // K(0) has landed once at most the (S - 1) * OPS operations issued after
+    // it (V(0), tiles 1 .. S - 2, K(S - 1)) are outstanding.
+    sync_tiles(false);
+    qk(0, sa);
+  }
   const int n_full = sparse ? 0 : max(0, min(t_hi, ctx / NK) - t_lo);
-  const int n_tight = max(0, n_full - (S - 1));
-  int k = 0;
-  for (; k < n_tight; ++k) {
-    sync_tiles(S - 2 >= 2 ? 2 : S - 2);
-    const int tn = t_lo + k + S - 1;
-    const int sn = (k + S - 1) % S;
-    unsigned char* kst = Kst + sn * K_BYTES;
-    unsigned char* vst = Vst + sn * V_BYTES;
+  const int n_tight = max(0, n_full - S) & ~1;
+  // DMA sources of K(tk) and V(tk - 1) for a tight step, formed one step
+  // ahead so the block-table reads are off the issue path.
+  // The 64 / CK K rows one wave-operation copies lie in one page, so that
+  // operation's page base is wave-uniform: it is formed on the scalar unit from
+  // the block table (entries out of range were flagged in the prologue and read
+  // as block 0), and each lane adds a fixed byte offset.
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  uint32_t koff[K_OPS];
+#pragma unroll
+  for (int n = 0; n < K_OPS; ++n) {
+    const int r0 = (64 * (wave_u + NWAVE * n)) / CK;
+    koff[n] = (uint32_t)(((k_row[n] - r0) * D + k_col[n]) * 2);
+  }
+  const unsigned char* kpage[K_OPS];
+  const bf16_bits* vsrc[V_OPS];
+  // the block table read through the constant address space: uniform reads
+  // become scalar loads
+  typedef const __attribute__((address_space(4))) int32_t* const_i32p;
+  const const_i32p table_c = (const_i32p)(table);
+  auto tight_sources = [&](int tk) __attribute__((always_inline)) {
 #pragma unroll
     for (int n = 0; n < K_OPS; ++n) {
-      const int p = tn * NK + k_row[n];
-      const bf16_bits* src = Kp + ctab[(p >> bsh) - cb0] + (long long)((p & bsm) * D + k_col[n]);
-      __builtin_amdgcn_global_load_lds(src, kst + (wave + NWAVE * n) * 1024, 16, 0, 0);
+      const int p0 = tk * NK + (64 * (wave_u + NWAVE * n)) / CK;
+      int phys = table_c[p0 >> bsh];
+      phys = (phys < 0 || phys >= a.num_blocks) ? 0 : phys;
+      kpage[n] = reinterpret_cast<const unsigned char*>(
+          Kp + (phys * blk_elems + head_off + (long long)((p0 & bsm) * D)));
     }
 #pragma unroll
     for (int n = 0; n < V_OPS; ++n) {
-      const int p = tn * NK + v_key[n];
-      const bf16_bits* src = Vp + ctab[(p >> bsh) - cb0] + (long long)(v_row[n] * bs + (p & bsm));
-      __builtin_amdgcn_global_load_lds(src, vst + (wave + NWAVE * n) * 1024, 16, 0, 0);
+      const int p = (tk - 1) * NK + v_key[n];
+      vsrc[n] = Vp + ctab[(p >> bsh) - cb0] + (long long)(v_row[n] * bs + (p & bsm));
     }
-    compute_tile(k % S, t_lo + k, false);
-  }
-  for (; k < nuse; ++k) {
-    const int ahead = min(S - 2, nuse - 1 - k);
-    sync_tiles(ahead >= 2 ? 2 : ahead);
-    if (k + S - 1 < nuse) {
-      issue_k(tile_at(k + S - 1), (k + S - 1) % S);
-      issue_v(tile_at(k + S - 1), (k + S - 1) % S);
+  };
+  auto tight_step = [&](int k, STile& sc, STile& sn) __attribute__((always_inline)) {
+    sync_tiles(true);
+    {
+      unsigned char* kst = Kst + (k % S) * K_BYTES;
+#pragma unroll
+      for (int n = 0; n < K_OPS; ++n)
+      {
+        const unsigned char* src = kpage[n] + koff[n];  // (a named pointer: see issue_k)
+        __builtin_amdgcn_global_load_lds(src, kst + (wave + NWAVE * n) * 1024, 16, 0, 0);
+      }
+      unsigned char* vst = Vst + ((k + S - 1) % S) * V_BYTES;
+#pragma unroll
+      for (int n = 0; n < V_OPS; ++n)
+      {
+        const bf16_bits* src = vsrc[n];
+        __builtin_amdgcn_global_load_lds(src, vst + (wave + NWAVE * n) * 1024, 16, 0, 0);
+      }
     }
+    if (k + 1 < n_tight) tight_sources(t_lo + k + 1 + S);
+    softmax_bound(sc);
+    qk((k + 1) % S, sn);
+    exp_tile(sc, pf);
+    pv(k % S, pf);
+  };
+  auto general_step = [&](int k, STile& sc, STile& sn) __attribute__((always_inline)) {
+    sync_tiles(k + S - 1 < nuse);
+    if (k + S < nuse) issue_k(tile_at(k + S), k % S);
+    if (k + S - 1 < nuse) issue_v(tile_at(k + S - 1), (k + S - 1) % S);
     const int t = tile_at(k);
-    compute_tile(k % S, t, !dense_full(t));
+    if (!dense_full(t)) mask_tile(t, sc);
+    softmax_bound(sc);
+    if (k + 1 < nuse) qk((k + 1) % S, sn);
+    exp_tile(sc, pf);
+    pv(k % S, pf);
+  };
+  int k = 0;
+  if (n_tight > 0) tight_sources(t_lo + S);
+  for (; k < n_tight; k += 2) {
+    tight_step(k, sa, sb);
+    tight_step(k + 1, sb, sa);
+  }
+  for (; k < nuse; k += 2) {
+    general_step(k, sa, sb);
+    if (k + 1 < nuse) general_step(k + 1, sb, sa);
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
