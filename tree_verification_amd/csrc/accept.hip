@@ -38,6 +38,17 @@ constexpr int kMaxP = 16;
 constexpr int kMaxKid = 64;          // children whose test scalars are prefetched
 constexpr unsigned kSpinLimit = 1u << 20;
 
+// Workgroup barrier for data exchanged through LDS.  __syncthreads() would
+// also wait for every outstanding global load (on this architecture a
+// workgroup release waits for vmcnt(0)), serialising the row prefetches into
+// the first barrier after them.
+__device__ __forceinline__ void lds_sync() {
+  __builtin_amdgcn_s_waitcnt(lgkmcnt_imm(0));
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 __device__ __forceinline__ double wave_sum_d(double v) {
   for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
   return v;
@@ -88,7 +99,11 @@ __device__ __forceinline__ void load8(const E* row, int y0, int V, bool vec, flo
     for (int c = 0; c < NC; ++c) { __VA_ARGS__ }           \
   }
 
-template <typename LT, bool CACHED>
+enum AcceptMode { kGreedy = 0, kRejection = 1, kTarget = 2 };
+
+// One kernel per (logit type, register cache, rule), so each holds only the
+// code of its rule.
+template <typename LT, bool CACHED, int MODE>
 __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
   constexpr bool kBF = sizeof(LT) == 2;
   static_assert(!CACHED || kBF, "only bf16 rows are cached");
@@ -98,6 +113,7 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
   __shared__ float kid_l[kMaxKid], kid_q[kMaxKid], kid_u[kMaxKid];
   __shared__ int wcnt[kAW];
   __shared__ double red_d[kAW];
+  __shared__ double red4[kAW][4];
   __shared__ float red_f[kAW];
   __shared__ int red_i[kAW];
   __shared__ double mass[kMaxP];    // per-slice mass of the distribution to draw from
@@ -107,7 +123,15 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
   __shared__ int s_flag, s_to, s_first, s_last, s_x;
 
   const int P = a.P;
-  const int b = blockIdx.x / P, wg = blockIdx.x % P;
+  // Workgroups are dispatched round-robin over the 8 XCDs; when the grid
+  // allows, the P workgroups of a sequence are placed on one XCD so their
+  // exchanges meet in one L2.
+  int L = blockIdx.x;
+  {
+    const int G = gridDim.x, n = G >> 3;
+    if ((G & 7) == 0 && n % P == 0) L = (L & 7) * n + (L >> 3);
+  }
+  const int b = L / P, wg = L % P;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int T = a.T, V = a.V;
   const int bt = a.tree_stride ? b : 0;
@@ -131,9 +155,9 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
     s_flag = 0;
     s_to = 0;
   }
-  __syncthreads();
+  lds_sync();
   if (bad) atomicOr(&s_flag, bad);
-  __syncthreads();
+  lds_sync();
   if (wg == 0)
     for (int n = tid; n < T; n += kAT) path[n] = -1;
   if (s_flag) {
@@ -148,7 +172,7 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
   const int sl0 = min(wg * a.SL, V), sl1 = min(sl0 + a.SL, V);
   const int NC = a.NC;
   const bool vec = (V & 7) == 0;
-  const bool mss = a.tau > 0.f && a.draft != nullptr;
+  constexpr bool mss = MODE == kRejection;
   const float c2 = a.tau > 0.f ? 1.4426950408889634f / a.tau : 0.f;
   const double invtau_d = a.tau > 0.f ? 1.0 / (double)a.tau : 0.0;
   auto y0_of = [&](int c) { return sl0 + c * kChunk + tid * 8; };
@@ -165,7 +189,7 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
   // fences are needed: each value travels in a single atomic word.
   int nbar = 0;
   auto exchange = [&](uint32_t v0, uint32_t v1) {
-    __syncthreads();
+    lds_sync();
     ++nbar;
     if (P == 1) {
       if (tid == 0) {
@@ -196,16 +220,16 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
         xv[tid][1] = (uint32_t)w1;
       }
     }
-    __syncthreads();
+    lds_sync();
   };
   auto xf = [&](int j, int k) { return __uint_as_float(xv[j][k]); };
 
   // ---- workgroup reduction of a float64 sum -------------------------------------
   auto wg_sum = [&](double v) -> double {
     v = wave_sum_d(v);
-    __syncthreads();
+    lds_sync();
     if (lane == 0) red_d[wave] = v;
-    __syncthreads();
+    lds_sync();
     double t = 0.0;
     for (int w = 0; w < kAW; ++w) t += red_d[w];
     return t;
@@ -219,13 +243,13 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
       const bool f = n < T && s_par[n] == cur;
       const unsigned long long bal = __ballot(f);
       if (lane == 0) wcnt[wave] = __popcll(bal);
-      __syncthreads();
+      lds_sync();
       int off = nk;
       for (int w = 0; w < wave; ++w) off += wcnt[w];
       if (f) kids[off + __popcll(bal & ((1ull << lane) - 1ull))] = n;
       int tot = 0;
       for (int w = 0; w < kAW; ++w) tot += wcnt[w];
-      __syncthreads();
+      lds_sync();
       nk += tot;
     }
     return nk;
@@ -289,10 +313,13 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
   };
 
   // Inverse-CDF draw: slices' masses in mass[0..P); threshold u * total.  The
-  // workgroup owning the crossing rescans its slice with `wf(c, w8)` and
-  // returns the token (other workgroups return -1).
+  // workgroup owning the crossing finds it in its slice, four chunks at a
+  // time: each thread sums its 8 weights `wf(c, w8)` of each chunk, a scan over
+  // (chunk, thread) positions gives each thread the mass before its
+  // elements, the first thread whose range passes the threshold scans its 8
+  // weights.  Other workgroups return -1.
   auto draw = [&](float u, auto wf) -> int {
-    __syncthreads();
+    lds_sync();
     double tot = 0.0;
     for (int j = 0; j < P; ++j) tot += mass[j];
     const double thr = (double)u * tot;
@@ -312,44 +339,81 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
       for (int j = 0; j < pick; ++j) before += mass[j];
     }
     if (wg != pick) return -1;
-    if (tid == 0) {
-      s_x = -1;
-      s_last = -1;
-    }
+    if (tid == 0) s_last = -1;
+    // weights of chunk c; with CACHED the chunk index must be a constant for
+    // the register cache, so c is matched against the unrolled candidates
+    auto wfc = [&](int c, double* w8) {
+      if constexpr (CACHED) {
+#pragma unroll
+        for (int j = 0; j < kMaxCh; ++j)
+          if (j == c) wf(j, w8);
+      } else {
+        wf(c, w8);
+      }
+    };
     double rn = before;
-    FOR_CHUNKS(c,
-      double w8[8];
-      wf(c, w8);
-      double ls = 0.0;
-      _Pragma("unroll")
-      for (int e = 0; e < 8; ++e) ls += w8[e];
-      double inc = ls;
-      for (int off = 1; off < 64; off <<= 1) {
-        const double o = __shfl_up(inc, off);
-        if (lane >= off) inc += o;
+    // CACHED slices have at most four chunks: one group
+    for (int c0 = 0; c0 < (CACHED ? 1 : NC); c0 += 4) {
+      double t[4], inc[4];
+      int lp_pos = -1;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        t[j] = 0.0;
+        if (c0 + j < NC) {
+          double w8[8];
+          if constexpr (CACHED) wf(j, w8);
+          else wf(c0 + j, w8);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            t[j] += w8[e];
+            if (w8[e] > 0.0) lp_pos = y0_of(c0 + j) + e;
+          }
+        }
+        inc[j] = t[j];
       }
-      __syncthreads();
-      if (lane == 63) red_d[wave] = inc;
-      if (tid == 0) s_first = kAT;
-      __syncthreads();
-      double woff = 0.0, ctot = 0.0;
-      for (int w = 0; w < kAW; ++w) {
-        if (w < wave) woff += red_d[w];
-        ctot += red_d[w];
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const double o = __shfl_up(inc[j], off);
+          if (lane >= off) inc[j] += o;
+        }
+      if (lane == 63)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) red4[wave][j] = inc[j];
+      if (tid == 0) s_first = 1 << 30;
+      for (int off = 32; off >= 1; off >>= 1) lp_pos = max(lp_pos, __shfl_xor(lp_pos, off));
+      if (lane == 0 && lp_pos >= 0) atomicMax(&s_last, lp_pos);
+      lds_sync();
+      double gtot = 0.0, cum = rn;
+      int key = 1 << 30;
+      double excl_hit = 0.0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        double woff = 0.0, ctot = 0.0;
+        for (int w = 0; w < kAW; ++w) {
+          if (w < wave) woff += red4[w][j];
+          ctot += red4[w][j];
+        }
+        const double excl = cum + woff + inc[j] - t[j];
+        if (key == (1 << 30) && t[j] > 0.0 && excl + t[j] > thr) {
+          key = j * kAT + tid;
+          excl_hit = excl;
+        }
+        cum += ctot;
+        gtot += ctot;
       }
-      const double excl = rn + woff + inc - ls;
-      if (ls > 0.0 && excl + ls > thr) atomicMin(&s_first, tid);
-      if (ls > 0.0) {
-        int lp = 0;
-        for (int e = 0; e < 8; ++e)
-          if (w8[e] > 0.0) lp = e;
-        atomicMax(&s_last, y0_of(c) + lp);
-      }
-      __syncthreads();
+      int kmin = key;
+      for (int off = 32; off >= 1; off >>= 1) kmin = min(kmin, __shfl_xor(kmin, off));
+      if (lane == 0 && kmin < (1 << 30)) atomicMin(&s_first, kmin);
+      lds_sync();
       const int first = s_first;
-      if (first < kAT) {
-        if (tid == first) {
-          double r2 = excl;
+      if (first < (1 << 30)) {
+        if (key == first) {
+          const int c = c0 + first / kAT;
+          double w8[8];
+          wfc(c, w8);
+          double r2 = excl_hit;
           int pk = -1, lp = -1;
           for (int e = 0; e < 8; ++e) {
             if (w8[e] > 0.0) lp = e;
@@ -358,12 +422,12 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
           }
           s_x = y0_of(c) + (pk >= 0 ? pk : lp);
         }
-        __syncthreads();
+        lds_sync();
         return s_x;
       }
-      rn += ctot;
-    )
-    __syncthreads();
+      rn += gtot;
+    }
+    lds_sync();
     return s_last;
   };
 
@@ -385,7 +449,7 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
       ku = a.unif[((size_t)b * T + node) * 2 + 0];
     }
     if (!have_row) load_row(row, lc);
-    if (mss) {
+    if constexpr (mss) {
       qrow = a.draft + ((size_t)b * T + cur) * V;
       if constexpr (CACHED) {
 #pragma unroll
@@ -401,14 +465,9 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
       }
     }
     if (nk > 0) load_row(row_of(kids[0]), pfc);
-    if (kid_lane) {
-      kid_l[tid] = kl;
-      kid_q[tid] = kq;
-      kid_u[tid] = ku;
-    }
     int nxt = -1;
     bool stop = false;
-    if (a.tau == 0.f) {
+    if constexpr (MODE == kGreedy) {
       // argmax, lowest id among equal maxima
       float bv = -INFINITY;
       int bi = V;
@@ -431,12 +490,12 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
           bi = oi;
         }
       }
-      __syncthreads();
+      lds_sync();
       if (lane == 0) {
         red_f[wave] = bv;
         red_i[wave] = bi;
       }
-      __syncthreads();
+      lds_sync();
       bv = red_f[0];
       bi = red_i[0];
       for (int w = 1; w < kAW; ++w)
@@ -493,18 +552,25 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
                (om == -INFINITY ? 0.0 : os * (double)__builtin_amdgcn_exp2f((om - mn) * c2));
         mt = mn;
       }
-      __syncthreads();
+      lds_sync();
       if (lane == 0) {
         red_f[wave] = mt;
         red_d[wave] = st;
       }
-      __syncthreads();
+      lds_sync();
       float mw = red_f[0];
       for (int w = 1; w < kAW; ++w) mw = fmaxf(mw, red_f[w]);
       double sw = 0.0;
       if (mw > -INFINITY)
         for (int w = 0; w < kAW; ++w)
           if (red_f[w] > -INFINITY) sw += red_d[w] * (double)__builtin_amdgcn_exp2f((red_f[w] - mw) * c2);
+      // the children's test scalars reach LDS only now: their loads were in
+      // flight during the statistics pass and the exchange's wait
+      if (kid_lane) {
+        kid_l[tid] = kl;
+        kid_q[tid] = kq;
+        kid_u[tid] = ku;
+      }
       exchange(__float_as_uint(mw), __float_as_uint((float)sw));
       float m = -INFINITY;
       for (int j = 0; j < P; ++j) m = fmaxf(m, xf(j, 0));
@@ -512,7 +578,7 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
         const float mj = xf(tid, 0);
         mass[tid] = mj == -INFINITY ? 0.0 : (double)xf(tid, 1) * (double)__builtin_amdgcn_exp2f((mj - m) * c2);
       }
-      __syncthreads();
+      lds_sync();
       double z0 = 0.0;
       for (int j = 0; j < P; ++j) z0 += mass[j];
       auto ew8 = [&](int c, double* w8) {
@@ -522,7 +588,7 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
         for (int e = 0; e < 8; ++e)
           w8[e] = v[e] == -INFINITY ? 0.0 : (double)__builtin_amdgcn_exp2f((v[e] - m) * c2);
       };
-      if (!mss) {
+      if constexpr (!mss) {
         const float u = a.unif[((size_t)b * T + cur) * 2 + 1];
         const int x = draw(u, ew8);
         exchange((uint32_t)(x + 1), 0u);   // only the drawing workgroup has x >= 0
@@ -539,50 +605,90 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
         }
       } else {
         int nrej = 0;
-        // residual after `upto` rejections, elementwise; zrej[j] is the j-th normaliser
-        // (multiplying by the reciprocals: a relative difference of ~1e-16
-        // from dividing, far inside the decision tolerance)
+        // Residual after `upto` rejections for one token: r <- max(r - q, 0) /
+        // Z_j for each rejection j whose mass Z_j was positive (zero mass
+        // leaves r unchanged), multiplying by the reciprocals zinv[j].  The
+        // cached path below applies the same operations element by element.
         auto resid = [&](double r0, double qy, int upto) -> double {
           double r = r0;
           for (int j = 0; j < upto; ++j)
-            if (zinv[j] > 0.0) r = fmax(r - qy, 0.0) * zinv[j];  // zero mass: unchanged
+            if (zinv[j] > 0.0) r = fmax(r - qy, 0.0) * zinv[j];
           return r;
         };
         const double iz0 = 1.0 / z0;
+        // p(y) / z0 in the arithmetic the tests use: fp32 exp2 of the scaled
+        // difference, then float64
+        auto p_of = [&](float l) -> double {
+          return l == -INFINITY ? 0.0 : (double)__builtin_amdgcn_exp2f((l - m) * c2) * iz0;
+        };
+        // CACHED: this thread's elements of the current residual, in float64
+        double rr[CACHED ? kMaxCh : 1][8];
+        if constexpr (CACHED) {
+          FOR_CHUNKS(cc,
+            float v[8];
+            logits8(cc, v);
+            _Pragma("unroll")
+            for (int e = 0; e < 8; ++e) rr[cc][e] = p_of(v[e]);
+          )
+        }
         for (int c = 0; c < nk && nrej < kMaxRej; ++c) {
           const int node = kids[c];
           const int x = s_tok[node];
-          const double lx = c < kMaxKid ? (double)kid_l[c] : (double)Elem<LT>::load(row, x);
+          const float lx = c < kMaxKid ? kid_l[c] : Elem<LT>::load(row, x);
           const double qx = c < kMaxKid ? (double)kid_q[c] : (double)qrow[x];
           const double u = c < kMaxKid ? (double)kid_u[c] : (double)a.unif[((size_t)b * T + node) * 2];
-          const double rx = resid(exp((lx - (double)m) * invtau_d) / z0, qx, nrej);
+          const double rx = resid(p_of(lx), qx, nrej);
           if (u * qx < rx) {
             nxt = c;
             break;
           }
-          // rejected: this slice's mass of max(r - q, 0)
+          // rejected: this slice's mass of max(r - q, 0), exchanged in full
+          // float64 precision
           double pz = 0.0;
-          FOR_CHUNKS(cc,
-            double w8[8];
-            float q8[8];
-            ew8(cc, w8);
-            q8_of(cc, q8);
-            _Pragma("unroll")
-            for (int e = 0; e < 8; ++e) {
-              const double qy = (double)q8[e];
-              pz += fmax(resid(w8[e] * iz0, qy, nrej) - qy, 0.0);
-            }
-          )
+          if constexpr (CACHED) {
+            FOR_CHUNKS(cc,
+              float q8[8];
+              q8_of(cc, q8);
+              _Pragma("unroll")
+              for (int e = 0; e < 8; ++e) pz += fmax(rr[cc][e] - (double)q8[e], 0.0);
+            )
+          } else {
+            FOR_CHUNKS(cc,
+              float v[8];
+              float q8[8];
+              logits8(cc, v);
+              q8_of(cc, q8);
+              _Pragma("unroll")
+              for (int e = 0; e < 8; ++e) {
+                const double qy = (double)q8[e];
+                pz += fmax(resid(p_of(v[e]), qy, nrej) - qy, 0.0);
+              }
+            )
+          }
           pz = wg_sum(pz);
-          exchange(__float_as_uint((float)pz), 0u);
+          const unsigned long long pzb = (unsigned long long)__double_as_longlong(pz);
+          exchange((uint32_t)pzb, (uint32_t)(pzb >> 32));
           double z = 0.0;
-          for (int j = 0; j < P; ++j) z += (double)xf(j, 0);
-          if (z > 0.0 && tid < P) mass[tid] = (double)xf(tid, 0);
+          for (int j = 0; j < P; ++j)
+            z += __longlong_as_double((long long)(((unsigned long long)xv[j][1] << 32) | xv[j][0]));
+          if (z > 0.0 && tid < P)
+            mass[tid] = __longlong_as_double((long long)(((unsigned long long)xv[tid][1] << 32) | xv[tid][0]));
+          const double zi = z > 0.0 ? 1.0 / z : 0.0;
           if (tid == 0) {
             zrej[nrej] = z;
-            zinv[nrej] = z > 0.0 ? 1.0 / z : 0.0;
+            zinv[nrej] = zi;
           }
-          __syncthreads();
+          if constexpr (CACHED) {
+            if (z > 0.0) {
+              FOR_CHUNKS(cc,
+                float q8[8];
+                q8_of(cc, q8);
+                _Pragma("unroll")
+                for (int e = 0; e < 8; ++e) rr[cc][e] = fmax(rr[cc][e] - (double)q8[e], 0.0) * zi;
+              )
+            }
+          }
+          lds_sync();
           ++nrej;
         }
         if (nxt < 0) {
@@ -594,11 +700,17 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
           for (int j = 0; j < nr; ++j)
             if (zrej[j] > 0.0) units = zrej[j];
           auto rw8 = [&](int c, double* w8) {
-            float q8[8];
-            q8_of(c, q8);
-            ew8(c, w8);
+            if constexpr (CACHED) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) w8[e] = resid(w8[e] * iz0, (double)q8[e], nr) * units;
+              for (int e = 0; e < 8; ++e) w8[e] = rr[c][e] * units;
+            } else {
+              float v[8];
+              float q8[8];
+              logits8(c, v);
+              q8_of(c, q8);
+#pragma unroll
+              for (int e = 0; e < 8; ++e) w8[e] = resid(p_of(v[e]), (double)q8[e], nr) * units;
+            }
           };
           const int x = draw(u, rw8);
           if (x >= 0 && tid == 0) a.bonus[b] = x;
@@ -619,15 +731,15 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
         have_row = true;
       }
     }
-    __syncthreads();
+    lds_sync();
   }
   if (wg == 0 && tid == 0) a.path_len[b] = plen;
   if (P > 1) {
     // the last workgroup of the sequence to leave clears the slots, so the
     // next call starts from barrier number 1 again
-    __syncthreads();
+    lds_sync();
     if (tid == 0) s_flag = atomicAdd(done, 1u) == (unsigned)P - 1;
-    __syncthreads();
+    lds_sync();
     if (s_flag) {
       for (int j = tid; j < 2 * kMaxP * 2; j += kAT)
         __hip_atomic_store(slots + j, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -645,10 +757,17 @@ int accept_wgs(int B, int V) {
   return P > 1 ? P : 1;
 }
 
+template <int MODE>
+static const void* accept_fn(const AcceptArgs& a) {
+  if (a.logits_f32) return reinterpret_cast<const void*>(accept_kernel<float, false, MODE>);
+  if (a.NC <= kMaxCh) return reinterpret_cast<const void*>(accept_kernel<bf16_bits, true, MODE>);
+  return reinterpret_cast<const void*>(accept_kernel<bf16_bits, false, MODE>);
+}
+
 hipError_t launch_accept(const AcceptArgs& a, hipStream_t st) {
-  const void* fn = a.logits_f32 ? reinterpret_cast<const void*>(accept_kernel<float, false>)
-                   : a.NC <= kMaxCh ? reinterpret_cast<const void*>(accept_kernel<bf16_bits, true>)
-                                    : reinterpret_cast<const void*>(accept_kernel<bf16_bits, false>);
+  const void* fn = a.tau == 0.f ? accept_fn<kGreedy>(a)
+                   : a.draft != nullptr ? accept_fn<kRejection>(a)
+                                        : accept_fn<kTarget>(a);
   const dim3 grid((unsigned)a.B * a.P), block(kAT);
   // B * P <= 256: with one workgroup per CU every workgroup of the grid is
   // resident at once, which the cross-workgroup waits rely on (they are
