@@ -262,22 +262,18 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
   float qc[kMaxCh][8];
   const LT* row = row_of(0);
   const float* qrow = nullptr;
+  // CACHED kernels run only when V % 8 == 0, so a chunk starting inside the
+  // slice is whole.  Every cached chunk is loaded unconditionally (a chunk
+  // outside the slice reads the row's first 8 values, which are never used):
+  // a branch around the load would make its merge wait for the data at once.
+  auto cached_y = [&](int c) {
+    const int y0 = y0_of(c);
+    return (c < NC && y0 < sl1) ? y0 : 0;
+  };
   auto load_row = [&](const LT* r, uint4* dst) {
     if constexpr (CACHED) {
 #pragma unroll
-      for (int c = 0; c < kMaxCh; ++c) {
-        const int y0 = y0_of(c);
-        if (c < NC && y0 < sl1) {
-          if (vec && y0 + 8 <= V) {
-            dst[c] = *reinterpret_cast<const uint4*>(r + y0);
-          } else {
-            uint32_t w[4] = {0, 0, 0, 0};
-            for (int e = 0; e < 8; ++e)
-              if (y0 + e < V) w[e >> 1] |= (uint32_t)r[y0 + e] << (16 * (e & 1));
-            dst[c] = make_uint4(w[0], w[1], w[2], w[3]);
-          }
-        }
-      }
+      for (int c = 0; c < kMaxCh; ++c) dst[c] = *reinterpret_cast<const uint4*>(r + cached_y(c));
     }
   };
   auto logits8 = [&](int c, float* v) {
@@ -439,12 +435,15 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
     row = row_of(cur);
     // Issue this node's loads together: the scalars of the child tests, the
     // row (unless prefetched), the draft row, and the first child's row.
-    float kl = 0.f, kq = 0.f, ku = 0.f;
+    // (the logit is kept as loaded and converted only when it is stored, so
+    // nothing waits for these loads before the statistics pass)
+    LT kl_raw = LT(0);
+    float kq = 0.f, ku = 0.f;
     const bool kid_lane = mss && tid < min(nk, kMaxKid);
     if (kid_lane) {
       const int node = kids[tid];
       const int x = s_tok[node];
-      kl = Elem<LT>::load(row, x);
+      kl_raw = row[x];
       kq = a.draft[((size_t)b * T + cur) * V + x];
       ku = a.unif[((size_t)b * T + node) * 2 + 0];
     }
@@ -452,15 +451,15 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
     if constexpr (mss) {
       qrow = a.draft + ((size_t)b * T + cur) * V;
       if constexpr (CACHED) {
+        // (chunks outside the slice hold unused draft values; every use
+        // there meets a zero residual)
 #pragma unroll
         for (int c = 0; c < kMaxCh; ++c) {
-          const int y0 = y0_of(c);
-          if (c < NC && y0 < sl1) {
-            load8<float>(qrow, y0, V, vec, 0.f, qc[c]);
-          } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) qc[c][e] = 0.f;
-          }
+          const int yq = cached_y(c);
+          const float4 u0 = *reinterpret_cast<const float4*>(qrow + yq);
+          const float4 u1 = *reinterpret_cast<const float4*>(qrow + yq + 4);
+          qc[c][0] = u0.x; qc[c][1] = u0.y; qc[c][2] = u0.z; qc[c][3] = u0.w;
+          qc[c][4] = u1.x; qc[c][5] = u1.y; qc[c][6] = u1.z; qc[c][7] = u1.w;
         }
       }
     }
@@ -567,7 +566,8 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
       // the children's test scalars reach LDS only now: their loads were in
       // flight during the statistics pass and the exchange's wait
       if (kid_lane) {
-        kid_l[tid] = kl;
+        if constexpr (kBF) kid_l[tid] = bf16_to_f32(kl_raw);
+        else kid_l[tid] = kl_raw;
         kid_q[tid] = kq;
         kid_u[tid] = ku;
       }
@@ -760,7 +760,8 @@ int accept_wgs(int B, int V) {
 template <int MODE>
 static const void* accept_fn(const AcceptArgs& a) {
   if (a.logits_f32) return reinterpret_cast<const void*>(accept_kernel<float, false, MODE>);
-  if (a.NC <= kMaxCh) return reinterpret_cast<const void*>(accept_kernel<bf16_bits, true, MODE>);
+  if (a.NC <= kMaxCh && (a.V & 7) == 0)
+    return reinterpret_cast<const void*>(accept_kernel<bf16_bits, true, MODE>);
   return reinterpret_cast<const void*>(accept_kernel<bf16_bits, false, MODE>);
 }
 
