@@ -17,13 +17,20 @@
 
 namespace sdtree {
 
-// One wavefront per (b, block, KV head): lane l owns D / 64 consecutive dims.
+// Block means.  A (b, block, KV head) unit is served by LPU lanes, each
+// owning one 16-byte column chunk (EPL consecutive dims) of the block's rows:
+// it walks the block's valid tokens in position order, 8 rows in flight, so
+// every dim's sum is the sequential one.  A wavefront serves 64 / LPU units.
 template <typename E, int D>
 __global__ void __launch_bounds__(256) block_mean_kernel(TopkArgs a) {
 #pragma clang fp contract(off)
-  constexpr int DPL = D / 64;
+  constexpr int EPL = 16 / (int)sizeof(E);      // dims per lane
+  constexpr int LPU = D / EPL;                   // lanes per unit
+  constexpr int UPW = 64 / LPU;                  // units per wavefront
+  static_assert(LPU * EPL == D && UPW * LPU == 64, "lane split");
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const long long unit = (long long)blockIdx.x * 4 + wave;
+  const int sub = lane / LPU, col = lane % LPU;
+  const long long unit = ((long long)blockIdx.x * 4 + wave) * UPW + sub;
   const long long nunits = (long long)a.B * a.nbmax * a.Hkv;
   if (unit >= nunits) return;
   const int g = (int)(unit % a.Hkv);
@@ -31,82 +38,142 @@ __global__ void __launch_bounds__(256) block_mean_kernel(TopkArgs a) {
   const int b = (int)(unit / ((long long)a.Hkv * a.nbmax));
   const int ctx = a.ctx[b];
   if (ctx < 0 || (long long)ctx > (long long)a.max_blocks * a.bs) {
-    if (n == 0 && g == 0 && lane == 0) set_status(a.status, SD_ERR_CAPACITY);
+    if (n == 0 && g == 0 && col == 0) set_status(a.status, SD_ERR_CAPACITY);
     return;
   }
   const int nblk = (ctx + a.bs - 1) / a.bs;
   if (n >= nblk) return;
   const int blk = a.table[(size_t)b * a.max_blocks + n];
-  float* out = a.means + (((size_t)b * a.nbmax + n) * a.Hkv + g) * D + lane * DPL;
+  float* out = a.means + (((size_t)b * a.nbmax + n) * a.Hkv + g) * D + col * EPL;
   if (blk < 0 || blk >= a.num_blocks) {
-    if (lane == 0) set_status(a.status, SD_ERR_BLOCK);
-    for (int e = 0; e < DPL; ++e) out[e] = 0.f;
+    if (col == 0) set_status(a.status, SD_ERR_BLOCK);
+    for (int e = 0; e < EPL; ++e) out[e] = 0.f;
     return;
   }
   const int valid = min(a.bs, ctx - n * a.bs);
-  const E* base = reinterpret_cast<const E*>(a.k) + (((size_t)blk * a.Hkv + g) * a.bs) * D + lane * DPL;
-  float s[DPL];
-  for (int e = 0; e < DPL; ++e) s[e] = 0.f;
+  const uint4* base = reinterpret_cast<const uint4*>(
+      reinterpret_cast<const E*>(a.k) + (((size_t)blk * a.Hkv + g) * a.bs) * D) + col;
+  constexpr int RS = D * (int)sizeof(E) / 16;    // uint4 per row
+  float s[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) s[e] = 0.f;
+  auto add = [&](const uint4& u) {
+    if constexpr (sizeof(E) == 2) {
+      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) s[e] = s[e] + bf16_to_f32((bf16_bits)(w[e >> 1] >> (16 * (e & 1))));
+    } else {
+      s[0] = s[0] + __uint_as_float(u.x);
+      s[1] = s[1] + __uint_as_float(u.y);
+      s[2] = s[2] + __uint_as_float(u.z);
+      s[3] = s[3] + __uint_as_float(u.w);
+    }
+  };
   int t = 0;
   for (; t + 8 <= valid; t += 8) {
-    float x[8][DPL];
+    uint4 x[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
+    for (int u = 0; u < 8; ++u) x[u] = base[(size_t)(t + u) * RS];
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) x[u][e] = Elem<E>::load(base, (size_t)(t + u) * D + e);
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
-#pragma unroll
-      for (int e = 0; e < DPL; ++e) s[e] = s[e] + x[u][e];
+    for (int u = 0; u < 8; ++u) add(x[u]);
   }
-  for (; t < valid; ++t)
-    for (int e = 0; e < DPL; ++e) s[e] = s[e] + Elem<E>::load(base, (size_t)t * D + e);
+  for (; t < valid; ++t) add(base[(size_t)t * RS]);
   const float fv = (float)valid;
-  for (int e = 0; e < DPL; ++e) out[e] = __fdiv_rn(s[e], fv);
+  float r[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) r[e] = __fdiv_rn(s[e], fv);
+  if constexpr (EPL == 8) {
+    reinterpret_cast<float4*>(out)[0] = make_float4(r[0], r[1], r[2], r[3]);
+    reinterpret_cast<float4*>(out)[1] = make_float4(r[4], r[5], r[6], r[7]);
+  } else {
+    reinterpret_cast<float4*>(out)[0] = make_float4(r[0], r[1], r[2], r[3]);
+  }
 }
 
-// Workgroup per (b, g, chunk of 64 blocks).  Each group of 16 lanes computes
-// one score: lane d' holds dims d' + 16 e, folds them in-lane down to width 16,
-// then four xor steps finish the halving tree (bit-identical to it, since the
-// two operands of every addition are the same).
+// Scores.  Workgroup per (b, g, chunk of 64 blocks); the query rows of the KV
+// group are staged in LDS 32 at a time, lane d' of a 16-lane group finding
+// its dims d' + 16 e contiguous.  Each group takes one block at a time: lane
+// d' holds the block mean's dims d' + 16 e, forms the products with a row and
+// folds them in-lane down to width 16; four row rotations (by 8, 4, 2, 1
+// lanes) then finish the halving tree for lane 0, which adds exactly the
+// operands the tree pairs.  Scores are staged in LDS and written as
+// contiguous row segments.
+__device__ __forceinline__ float row_ror_add(float v, int n) {
+  // lane i of each 16-lane row receives lane (i + n) % 16
+  int r;
+  switch (n) {
+    case 8: r = __builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xf, 0xf, false); break;
+    case 4: r = __builtin_amdgcn_mov_dpp(__float_as_int(v), 0x124, 0xf, 0xf, false); break;
+    case 2: r = __builtin_amdgcn_mov_dpp(__float_as_int(v), 0x122, 0xf, 0xf, false); break;
+    default: r = __builtin_amdgcn_mov_dpp(__float_as_int(v), 0x121, 0xf, 0xf, false); break;
+  }
+  return v + __int_as_float(r);
+}
 template <typename E, int D>
 __global__ void __launch_bounds__(256) block_score_kernel(TopkArgs a) {
 #pragma clang fp contract(off)
   constexpr int EL = D / 16;
   constexpr int NBC = 64;
+  constexpr int RC = 32;                     // query rows per LDS stage
+  __shared__ __align__(16) float qs[RC][D];   // [row][lane d'][e] = q[row][d' + 16 e]
+  __shared__ float ss[RC][NBC + 1];
   const int chunk = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int ctx = a.ctx[b];
   if (ctx < 0 || (long long)ctx > (long long)a.max_blocks * a.bs) return;
   const int nblk = (ctx + a.bs - 1) / a.bs;
   const int n0 = chunk * NBC;
   if (n0 >= nblk) return;
+  const int nbc = min(NBC, nblk - n0);
   const int tid = threadIdx.x;
   const int grp = tid >> 4, dl = tid & 15;
   const int R = a.T * a.G;  // query rows of this KV group
-  for (int nn = grp; nn < NBC; nn += 16) {
-    const int n = n0 + nn;
-    if (n >= nblk) break;
-    const float* mrow = a.means + (((size_t)b * a.nbmax + n) * a.Hkv + g) * D;
-    float m[EL];
+  for (int r0 = 0; r0 < R; r0 += RC) {
+    const int rc = min(RC, R - r0);
+    __syncthreads();
+    for (int idx = tid; idx < rc * D; idx += 256) {
+      const int rr = idx / D, d = idx % D;
+      const int r = r0 + rr;
+      const int i = r / a.G, h = g * a.G + r % a.G;
+      qs[rr][(d % 16) * EL + d / 16] =
+          Elem<E>::load(reinterpret_cast<const E*>(a.q), (((size_t)b * a.T + i) * a.Hq + h) * D + d);
+    }
+    __syncthreads();
+    for (int nn = grp; nn < nbc; nn += 16) {
+      const float* mrow = a.means + (((size_t)b * a.nbmax + n0 + nn) * a.Hkv + g) * D;
+      float m[EL];
 #pragma unroll
-    for (int e = 0; e < EL; ++e) m[e] = mrow[dl + 16 * e];
-    for (int r = 0; r < R; ++r) {
+      for (int e = 0; e < EL; ++e) m[e] = mrow[dl + 16 * e];
+      for (int rr = 0; rr < rc; ++rr) {
+        float v[EL];
+        const float4* qv = reinterpret_cast<const float4*>(&qs[rr][dl * EL]);
+#pragma unroll
+        for (int e4 = 0; e4 < EL / 4; ++e4) {
+          const float4 q4 = qv[e4];
+          v[4 * e4 + 0] = q4.x * m[4 * e4 + 0];
+          v[4 * e4 + 1] = q4.y * m[4 * e4 + 1];
+          v[4 * e4 + 2] = q4.z * m[4 * e4 + 2];
+          v[4 * e4 + 3] = q4.w * m[4 * e4 + 3];
+        }
+#pragma unroll
+        for (int hw = EL / 2; hw >= 1; hw >>= 1)
+#pragma unroll
+          for (int e = 0; e < hw; ++e) v[e] = v[e] + v[e + hw];
+        float sc = v[0];
+        sc = row_ror_add(sc, 8);
+        sc = row_ror_add(sc, 4);
+        sc = row_ror_add(sc, 2);
+        sc = row_ror_add(sc, 1);
+        if (dl == 0) ss[rr][nn] = sc;
+      }
+    }
+    __syncthreads();
+    for (int idx = tid; idx < rc * NBC; idx += 256) {
+      const int rr = idx / NBC, nn = idx % NBC;
+      if (nn >= nbc) continue;
+      const int r = r0 + rr;
       const int i = r / a.G, h = g * a.G + r % a.G;
       const size_t qrow = ((size_t)b * a.T + i) * a.Hq + h;
-      const E* qp = reinterpret_cast<const E*>(a.q) + qrow * D;
-      float v[EL];
-#pragma unroll
-      for (int e = 0; e < EL; ++e) v[e] = Elem<E>::load(qp, dl + 16 * e) * m[e];
-#pragma unroll
-      for (int hw = EL / 2; hw >= 1; hw >>= 1)
-#pragma unroll
-        for (int e = 0; e < hw; ++e) v[e] = v[e] + v[e + hw];
-      float s = v[0];
-      s = s + __shfl_xor(s, 8);
-      s = s + __shfl_xor(s, 4);
-      s = s + __shfl_xor(s, 2);
-      s = s + __shfl_xor(s, 1);
-      if (dl == 0) a.scores[qrow * a.nbmax + n] = s;
+      a.scores[qrow * a.nbmax + n0 + nn] = ss[rr][nn];
     }
   }
 }
@@ -118,14 +185,19 @@ __device__ __forceinline__ uint32_t score_key(float s) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// One workgroup per query row: radix-select the k-th largest key, then emit
-// every block above it plus the lowest-indexed blocks equal to it.
+// Selection: one wavefront per query row.  A radix select over 8-bit digits
+// finds the k-th largest key (per-wavefront histogram in LDS, suffix sums by a
+// lane scan); then every block above it and the first blocks equal to it are
+// emitted in ascending block order (ballot compaction).
+constexpr int kSelStage = 2048;  // scores per row staged in LDS (longer rows read global memory)
+
 __global__ void __launch_bounds__(256) block_select_kernel(TopkArgs a) {
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t s_prefix, s_krem;
-  __shared__ int wcnt_eq[4], wcnt_sel[4];
-  const long long row = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ uint32_t hist[4][256];
+  __shared__ uint32_t keys[4][kSelStage];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const long long row = (long long)blockIdx.x * 4 + wave;
+  const long long nrows = (long long)a.B * a.T * a.Hq;
+  if (row >= nrows) return;
   const int b = (int)(row / ((long long)a.T * a.Hq));
   int32_t* out = a.sel + row * a.topk;
   const int ctx = a.ctx[b];
@@ -133,73 +205,96 @@ __global__ void __launch_bounds__(256) block_select_kernel(TopkArgs a) {
   const int nb = ok ? (ctx + a.bs - 1) / a.bs : 0;
   const float* sc = a.scores + row * a.nbmax;
   if (nb <= a.topk) {
-    for (int e = tid; e < a.topk; e += 256) out[e] = e < nb ? e : -1;
+    for (int e = lane; e < a.topk; e += 64) out[e] = e < nb ? e : -1;
     return;
   }
-  uint32_t prefix = 0, mask = 0, krem = a.topk;
+  uint32_t* h = hist[wave];
+  // the row's keys, staged once when they fit
+  const bool staged = nb <= kSelStage;
+  uint32_t* kw = keys[wave];
+  if (staged)
+    for (int y = lane; y < nb; y += 64) kw[y] = score_key(sc[y]);
+  auto key_of = [&](int y) -> uint32_t { return staged ? kw[y] : score_key(sc[y]); };
+  uint32_t prefix = 0, mask = 0, krem = (uint32_t)a.topk;
   for (int shift = 24; shift >= 0; shift -= 8) {
-    hist[tid] = 0;
-    __syncthreads();
-    for (int y = tid; y < nb; y += 256) {
-      const uint32_t u = score_key(sc[y]);
-      if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) h[lane * 4 + i] = 0u;
+    __builtin_amdgcn_wave_barrier();
+    for (int y = lane; y < nb; y += 64) {
+      const uint32_t u = key_of(y);
+      if ((u & mask) == prefix) atomicAdd(&h[(u >> shift) & 255u], 1u);
     }
-    __syncthreads();
-    if (tid == 0) {
-      uint32_t above = 0;
-      int d = 255;
-      for (; d > 0; --d) {
-        if (above + hist[d] >= krem) break;
-        above += hist[d];
+    __builtin_amdgcn_wave_barrier();
+    // lane l holds bins 4l .. 4l + 3; x = count of keys in bins >= 4l
+    uint32_t hb[4], lt = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      hb[i] = h[lane * 4 + i];
+      lt += hb[i];
+    }
+    uint32_t x = lt;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint32_t y = __shfl_down(x, off);
+      if (lane + off < 64) x += y;
+    }
+    // bin d = 4 lane + i holds the k-th largest when the keys in bins above
+    // it number fewer than krem and with it at least krem
+    uint32_t above = x - lt;
+    int dsel = -1;
+    uint32_t asel = 0;
+#pragma unroll
+    for (int i = 3; i >= 0; --i) {
+      if (dsel < 0 && above < krem && above + hb[i] >= krem) {
+        dsel = lane * 4 + i;
+        asel = above;
       }
-      s_prefix = prefix | ((uint32_t)d << shift);
-      s_krem = krem - above;
+      above += hb[i];
     }
-    __syncthreads();
-    prefix = s_prefix;
-    krem = s_krem;
+    const unsigned long long bal = __ballot(dsel >= 0);
+    const int src = __ffsll((long long)bal) - 1;
+    const int d = __shfl(dsel, src);
+    const uint32_t ab = __shfl(asel, src);
+    prefix |= (uint32_t)d << shift;
     mask |= 255u << shift;
-    __syncthreads();
+    krem -= ab;
+    __builtin_amdgcn_wave_barrier();
   }
-  // prefix is now the k-th largest key; take everything above it and the first
-  // krem blocks equal to it, in ascending block order.
+  // prefix is the k-th largest key; krem of the keys equal to it are taken,
+  // lowest block first.
   int eq_before = 0, sel_before = 0;
-  for (int base = 0; base < nb; base += 256) {
-    const int y = base + tid;
-    const uint32_t u = y < nb ? score_key(sc[y]) : 0u;
+  const unsigned long long below = (1ull << lane) - 1ull;
+  for (int base = 0; base < nb; base += 64) {
+    const int y = base + lane;
+    const uint32_t u = y < nb ? key_of(y) : 0u;
     const bool eq = y < nb && u == prefix;
     const unsigned long long beq = __ballot(eq);
-    if (lane == 0) wcnt_eq[wave] = __popcll(beq);
-    __syncthreads();
-    int eq_rank = eq_before + __popcll(beq & ((1ull << lane) - 1ull));
-    for (int w = 0; w < wave; ++w) eq_rank += wcnt_eq[w];
+    const int eq_rank = eq_before + __popcll(beq & below);
     const bool take = y < nb && (u > prefix || (eq && eq_rank < (int)krem));
     const unsigned long long bsel = __ballot(take);
-    if (lane == 0) wcnt_sel[wave] = __popcll(bsel);
-    __syncthreads();
-    int pos = sel_before + __popcll(bsel & ((1ull << lane) - 1ull));
-    for (int w = 0; w < wave; ++w) pos += wcnt_sel[w];
+    const int pos = sel_before + __popcll(bsel & below);
     if (take && pos < a.topk) out[pos] = y;
-    for (int w = 0; w < 4; ++w) {
-      eq_before += wcnt_eq[w];
-      sel_before += wcnt_sel[w];
-    }
-    __syncthreads();
+    eq_before += __popcll(beq);
+    sel_before += __popcll(bsel);
   }
-  for (int e = sel_before + tid; e < a.topk; e += 256) out[e] = -1;
+  for (int e = sel_before + lane; e < a.topk; e += 64) out[e] = -1;
 }
 
 template <typename E, int D>
 static hipError_t launch_topk_t(const TopkArgs& a, hipStream_t st) {
+  constexpr int UPW = 64 / (D / (16 / (int)sizeof(E)));
   const long long units = (long long)a.B * a.nbmax * a.Hkv;
-  hipLaunchKernelGGL((block_mean_kernel<E, D>), dim3((unsigned)((units + 3) / 4)), dim3(256), 0, st, a);
+  const long long per_wg = 4LL * UPW;
+  hipLaunchKernelGGL((block_mean_kernel<E, D>), dim3((unsigned)((units + per_wg - 1) / per_wg)), dim3(256), 0,
+                     st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   dim3 g2((a.nbmax + 63) / 64, a.Hkv, a.B);
   hipLaunchKernelGGL((block_score_kernel<E, D>), g2, dim3(256), 0, st, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(block_select_kernel, dim3((unsigned)((long long)a.B * a.T * a.Hq)), dim3(256), 0, st, a);
+  const long long rows = (long long)a.B * a.T * a.Hq;
+  hipLaunchKernelGGL(block_select_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
