@@ -148,7 +148,8 @@ sd_status sd_accept(const sd_accept_shape* shape, const void* target_logits,
  * sd_accept produces), which makes the in-place copy safe.  k_pages, v_pages
  * and ctx_lens are modified.  A sequence whose path or table fails validation
  * is left untouched and a sticky bit is set in ws (>= sd_workspace_bytes(
- * SD_CALL_COMMIT, shape, 0) bytes; only its status word is used).
+ * SD_CALL_COMMIT, shape, 0) bytes: the status word and one completion counter
+ * per sequence, which every call leaves at zero).
  *   path      int32 [B, T] as produced by sd_accept; path_len int32 [B].
  */
 sd_status sd_kv_commit(const sd_shape* shape, void* k_pages, void* v_pages,

@@ -71,7 +71,8 @@ def test_workspace_sizes():
     assert L.sd_workspace_bytes(1, ctypes.byref(s), 65) == 0
     assert L.sd_workspace_bytes(3, ctypes.byref(s), 32) >= 16 * 260 * 8 * 128 * 4
     assert L.sd_workspace_bytes(3, ctypes.byref(s), 0) == 0
-    assert L.sd_workspace_bytes(4, ctypes.byref(s), 0) == 256
+    # commit: status header plus one completion counter per sequence
+    assert L.sd_workspace_bytes(4, ctypes.byref(s), 0) == 256 + 256
     a = _lib.SdAcceptShape(16, 64, 128256, 1, 64)
     # 16 workgroups per sequence: barrier state for each of the 16 sequences
     assert L.sd_workspace_bytes(2, ctypes.byref(a), 0) == 256 + 16 * 1024
@@ -101,7 +102,7 @@ def test_commit_and_topk_reject_bad_arguments():
     assert L.sd_kv_commit(ctypes.byref(_shape(Hq=7)), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 256,
                           None) == 2
     assert L.sd_kv_commit(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 256, None) == 1
-    assert L.sd_kv_commit(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 8, None) == 5
+    assert L.sd_kv_commit(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 256, None) == 5
     assert L.sd_topk_blocks(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, 0, FAKE, FAKE, 1 << 40, None) == 1
     assert L.sd_topk_blocks(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, 4, FAKE, FAKE, 10, None) == 5
     assert L.sd_device_status(None, None, None) == 1

@@ -134,6 +134,7 @@ struct CommitArgs {
   const int32_t* path;
   const int32_t* path_len;
   uint32_t* status;
+  unsigned* counters;   // one per sequence, zero between calls
   int B, T, Hkv, D, bs, max_blocks, num_blocks, esize;
 };
 

@@ -126,6 +126,9 @@ static AttnPlan plan_attn(const sd_shape* s, int ksel, bool sparse) {
   return p;
 }
 
+// Commit scratch: the status header and one completion counter per sequence.
+static size_t commit_ws(const sd_shape* s) { return kWsHeader + align_up((size_t)s->B * 4, 256); }
+
 static size_t topk_ws(const sd_shape* s, size_t* means_off, size_t* scores_off) {
   const size_t nbmax = (size_t)s->max_blocks;
   const size_t mo = kWsHeader;
@@ -179,7 +182,7 @@ size_t sd_workspace_bytes(int32_t call_id, const void* shape, int32_t extra) {
   }
   if (call_id == SD_CALL_COMMIT) {
     const sd_shape* s = static_cast<const sd_shape*>(shape);
-    return check_shape(s) == SD_OK ? kWsHeader : 0;
+    return check_shape(s) == SD_OK ? commit_ws(s) : 0;
   }
   if (call_id == SD_CALL_TOPK) {
     const sd_shape* s = static_cast<const sd_shape*>(shape);
@@ -277,7 +280,7 @@ sd_status sd_kv_commit(const sd_shape* shape, void* k_pages, void* v_pages,
   if (st != SD_OK) return st;
   if (!k_pages || !v_pages || !block_table || !ctx_lens || !path || !path_len || !ws)
     return SD_INVALID_ARG;
-  if (ws_bytes < kWsHeader) return SD_CAPACITY;
+  if (ws_bytes < commit_ws(shape)) return SD_CAPACITY;
   CommitArgs a;
   memset(&a, 0, sizeof(a));
   a.k = k_pages; a.v = v_pages; a.table = block_table; a.ctx = ctx_lens; a.path = path;
@@ -286,6 +289,7 @@ sd_status sd_kv_commit(const sd_shape* shape, void* k_pages, void* v_pages,
   a.max_blocks = shape->max_blocks; a.num_blocks = shape->num_blocks;
   a.esize = shape->dtype == SD_F32 ? 4 : 2;
   a.status = static_cast<uint32_t*>(ws);
+  a.counters = reinterpret_cast<unsigned*>(static_cast<unsigned char*>(ws) + kWsHeader);
   return hip_status(launch_commit(a, static_cast<hipStream_t>(stream)));
 }
 
