@@ -13,6 +13,8 @@
 //                       and shared by every query row of a KV group, online
 //                       softmax in registers, split context with partials
 //   attn_combine_kernel merges split partials into the normalised output
+#include <type_traits>
+
 #include "common.h"
 
 namespace sdtree {
@@ -730,7 +732,16 @@ __global__ void __launch_bounds__(WQ * WK * 64) attn_mfma_kernel(AttnArgs a) {
     sync_tiles(false);
     qk(0, sa);
   }
-  const int n_full = sparse ? 0 : max(0, min(t_hi, ctx / NK) - t_lo);
+  // Whole tiles: dense context tiles inside ctx; sparse tiles made only of
+  // whole selected blocks (the union is ascending, so only its last block can
+  // be the partial block at the end of the context).
+  int n_full;
+  if (!sparse) {
+    n_full = max(0, min(t_hi, ctx / NK) - t_lo);
+  } else {
+    const int n_whole = nU - ((nU > 0 && U[nU - 1] == nblk_ctx - 1 && (ctx & bsm) != 0) ? 1 : 0);
+    n_full = max(0, min(t_hi, (int)(((long long)n_whole << bsh) / NK)) - t_lo);
+  }
   const int n_tight = max(0, n_full - S) & ~1;
   // DMA sources of K(tk) and V(tk - 1) for a tight step, formed one step
   // ahead so the block-table reads are off the issue path.
@@ -751,22 +762,47 @@ __global__ void __launch_bounds__(WQ * WK * 64) attn_mfma_kernel(AttnArgs a) {
   // become scalar loads
   typedef const __attribute__((address_space(4))) int32_t* const_i32p;
   const const_i32p table_c = (const_i32p)(table);
-  auto tight_sources = [&](int tk) __attribute__((always_inline)) {
+  // (sparse tiles index the union of selected blocks: virtual key vi lies in
+  // union block vi >> bsh, whose validated physical id is Uphys[vi >> bsh])
+  auto tight_sources = [&](auto sp_tag, int tk) __attribute__((always_inline)) {
+    constexpr bool SP = decltype(sp_tag)::value;
 #pragma unroll
     for (int n = 0; n < K_OPS; ++n) {
       const int p0 = tk * NK + (64 * (wave_u + NWAVE * n)) / CK;
-      int phys = table_c[p0 >> bsh];
-      phys = (phys < 0 || phys >= a.num_blocks) ? 0 : phys;
+      int phys;
+      if constexpr (!SP) {
+        phys = table_c[p0 >> bsh];
+        phys = (phys < 0 || phys >= a.num_blocks) ? 0 : phys;
+      } else {
+        phys = __builtin_amdgcn_readfirstlane(Uphys[p0 >> bsh]);
+      }
       kpage[n] = reinterpret_cast<const unsigned char*>(
           Kp + (phys * blk_elems + head_off + (long long)((p0 & bsm) * D)));
     }
 #pragma unroll
     for (int n = 0; n < V_OPS; ++n) {
       const int p = (tk - 1) * NK + v_key[n];
-      vsrc[n] = Vp + ctab[(p >> bsh) - cb0] + (long long)(v_row[n] * bs + (p & bsm));
+      const long long boff = SP ? (long long)Uphys[p >> bsh] * blk_elems + head_off : ctab[(p >> bsh) - cb0];
+      vsrc[n] = Vp + boff + (long long)(v_row[n] * bs + (p & bsm));
     }
   };
-  auto tight_step = [&](int k, STile& sc, STile& sn) __attribute__((always_inline)) {
+  // Mask of a whole sparse tile: a row sees an 8-key chunk when it selected
+  // the chunk's block.
+  auto sparse_mask = [&](int t, STile& sc) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kg = 0; kg < KG; ++kg) {
+      const int e = (t * NK + kbase + 32 * kg + 8 * lg) >> bsh;
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const bool vis = node[qb] >= 0 && ((rowbits[rloc[qb] * UW + (e >> 5)] >> (e & 31)) & 1u);
+        if (!vis)
+#pragma unroll
+          for (int half = 0; half < 2; ++half) sc[qb][2 * kg + half] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+      }
+    }
+  };
+  auto tight_step = [&](auto sp_tag, int k, STile& sc, STile& sn) __attribute__((always_inline)) {
+    constexpr bool SP = decltype(sp_tag)::value;
     sync_tiles(true);
     {
       unsigned char* kst = Kst + (k % S) * K_BYTES;
@@ -784,7 +820,8 @@ __global__ void __launch_bounds__(WQ * WK * 64) attn_mfma_kernel(AttnArgs a) {
         __builtin_amdgcn_global_load_lds(src, vst + (wave + NWAVE * n) * 1024, 16, 0, 0);
       }
     }
-    if (k + 1 < n_tight) tight_sources(t_lo + k + 1 + S);
+    if (k + 1 < n_tight) tight_sources(sp_tag, t_lo + k + 1 + S);
+    if constexpr (SP) sparse_mask(t_lo + k, sc);
     softmax_bound(sc);
     qk((k + 1) % S, sn);
     exp_tile(sc, pf);
@@ -802,10 +839,21 @@ __global__ void __launch_bounds__(WQ * WK * 64) attn_mfma_kernel(AttnArgs a) {
     pv(k % S, pf);
   };
   int k = 0;
-  if (n_tight > 0) tight_sources(t_lo + S);
-  for (; k < n_tight; k += 2) {
-    tight_step(k, sa, sb);
-    tight_step(k + 1, sb, sa);
+  // (two copies of the loop: dense and sparse, each specialised)
+  if (!sparse) {
+    const std::integral_constant<bool, false> dense_tag;
+    if (n_tight > 0) tight_sources(dense_tag, t_lo + S);
+    for (; k < n_tight; k += 2) {
+      tight_step(dense_tag, k, sa, sb);
+      tight_step(dense_tag, k + 1, sb, sa);
+    }
+  } else {
+    const std::integral_constant<bool, true> sparse_tag;
+    if (n_tight > 0) tight_sources(sparse_tag, t_lo + S);
+    for (; k < n_tight; k += 2) {
+      tight_step(sparse_tag, k, sa, sb);
+      tight_step(sparse_tag, k + 1, sb, sa);
+    }
   }
   for (; k < nuse; k += 2) {
     general_step(k, sa, sb);
