@@ -384,8 +384,11 @@ __global__ void __launch_bounds__(WQ * WK * 64) attn_mfma_kernel(AttnArgs a) {
   // ---- tile range of this split, usable tiles ------------------------------
   const int nct = !cap_ok ? 0 : (sparse ? ((nU << bsh) + NK - 1) / NK : (ctx + NK - 1) / NK);
   const int ntot = cap_ok ? nct + n_tt : 0;
-  const int t_lo = split * a.tps;
-  const int t_hi = min(t_lo + a.tps, ntot);
+  // The sequence's actual tiles are spread evenly over the splits (the plan's
+  // tiles per split bound this share, so the LDS block tables still fit).
+  const int tps_here = (ntot + a.n_splits - 1) / a.n_splits;
+  const int t_lo = split * tps_here;
+  const int t_hi = min(t_lo + tps_here, ntot);
   const int n_ctx_here = max(0, min(t_hi, nct) - t_lo);
   if (tid == 0) {
     int n = 0;
