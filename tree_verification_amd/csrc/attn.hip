@@ -579,6 +579,36 @@ __global__ void __launch_bounds__(WQ * WK * 64) attn_mfma_kernel(AttnArgs a) {
     }
   };
 
+  typedef bf16x8 KFrag[KG][2][DS];
+  auto load_k = [&](int slot, KFrag& kf) __attribute__((always_inline)) {
+    const unsigned char* Kt = Kst + slot * K_BYTES;
+#pragma unroll
+    for (int kg = 0; kg < KG; ++kg)
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int key = kbase + 32 * kg + 8 * (l16 >> 2) + 4 * half + (l16 & 3);
+#pragma unroll
+        for (int ds = 0; ds < DS; ++ds)
+          kf[kg][half][ds] = *reinterpret_cast<const bf16x8*>(
+              Kt + key * (D * 2) + (((ds * 4 + lg) ^ kswz(key)) * 16));
+      }
+  };
+  auto qk_regs = [&](const KFrag& kf, STile& s) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kg = 0; kg < KG; ++kg)
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) s[qb][2 * kg + half] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ds = 0; ds < DS; ++ds)
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb)
+            s[qb][2 * kg + half] =
+                __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kg][half][ds], qf[qb][ds], s[qb][2 * kg + half], 0, 0, 0);
+      }
+  };
+
   // Masks the scores of tile t that a query column may not see.
   auto mask_tile = [&](int t, STile& s) __attribute__((always_inline)) {
 #pragma unroll
@@ -679,22 +709,33 @@ __global__ void __launch_bounds__(WQ * WK * 64) attn_mfma_kernel(AttnArgs a) {
       }
     }
   };
-  // O^T += V^T P^T for the tile in ring slot `slot`.
-  auto pv = [&](int slot, const PTile& pf) __attribute__((always_inline)) {
+  // O^T += V^T P^T: the V^T fragments of the tile in ring slot `slot` are
+  // read into registers (load_v), then multiplied (pv_regs).
+  typedef bf16x8 VFrag[KG][DB];
+  auto load_v = [&](int slot, VFrag& vf) __attribute__((always_inline)) {
     const unsigned char* Vt = Vst + slot * V_BYTES;
 #pragma unroll
-    for (int kg = 0; kg < KG; ++kg) {
+    for (int kg = 0; kg < KG; ++kg)
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         const int d = db * 16 + l16;
         const int cc = (kbase + 32 * kg + 8 * lg) >> 3;
-        const bf16x8 va =
-            *reinterpret_cast<const bf16x8*>(Vt + d * (NK * 2) + ((cc ^ vswz(d)) * 16));
+        vf[kg][db] = *reinterpret_cast<const bf16x8*>(Vt + d * (NK * 2) + ((cc ^ vswz(d)) * 16));
+      }
+  };
+  auto pv_regs = [&](const VFrag& vf, const PTile& pf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kg = 0; kg < KG; ++kg)
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
-          o[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pf[qb][kg], o[qb][db], 0, 0, 0);
-      }
-    }
+          o[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[kg][db], pf[qb][kg], o[qb][db], 0, 0, 0);
+  };
+  auto pv = [&](int slot, const PTile& pf) __attribute__((always_inline)) {
+    VFrag vf;
+    load_v(slot, vf);
+    pv_regs(vf, pf);
   };
 
   auto sync_tiles = [&](bool exact) __attribute__((always_inline)) {
@@ -826,9 +867,17 @@ __global__ void __launch_bounds__(WQ * WK * 64) attn_mfma_kernel(AttnArgs a) {
     if (k + 1 < n_tight) tight_sources(sp_tag, t_lo + k + 1 + S);
     if constexpr (SP) sparse_mask(t_lo + k, sc);
     softmax_bound(sc);
-    qk((k + 1) % S, sn);
+    // tile k's V^T fragments are read before the score MFMAs, so their LDS
+    // latency is covered; the scheduling barrier keeps the compiler from
+    // sinking the reads to their first use
+    KFrag kf;
+    load_k((k + 1) % S, kf);
+    VFrag vf;
+    load_v(k % S, vf);
+    __builtin_amdgcn_sched_barrier(0);
+    qk_regs(kf, sn);
     exp_tile(sc, pf);
-    pv(k % S, pf);
+    pv_regs(vf, pf);
   };
   auto general_step = [&](int k, STile& sc, STile& sn) __attribute__((always_inline)) {
     sync_tiles(k + S - 1 < nuse);
