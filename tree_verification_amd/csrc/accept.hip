@@ -34,7 +34,7 @@ constexpr int kChunk = kAT * 8;       // tokens per chunk
 constexpr int kMaxCh = 4;             // chunks kept in registers
 constexpr int kMaxT = kMaxTreeNodes;
 constexpr int kMaxRej = 64;
-constexpr int kMaxP = 16;
+constexpr int kMaxP = 16;             // (the slice butterflies span 16 lanes)
 constexpr int kMaxKid = 64;          // children whose test scalars are prefetched
 constexpr unsigned kSpinLimit = 1u << 20;
 
@@ -119,7 +119,7 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
   __shared__ double mass[kMaxP];    // per-slice mass of the distribution to draw from
   __shared__ double zrej[kMaxRej];  // residual normalisers at the current node
   __shared__ double zinv[kMaxRej];  // their reciprocals (0 when the mass was 0)
-  __shared__ uint32_t xv[kMaxP][2];
+  __shared__ __align__(8) uint32_t xv[kMaxP][2];
   __shared__ int s_flag, s_to, s_first, s_last, s_x;
 
   const int P = a.P;
@@ -223,6 +223,16 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
     lds_sync();
   };
   auto xf = [&](int j, int k) { return __uint_as_float(xv[j][k]); };
+  // All P exchanged pairs read into registers together (one LDS wait rather
+  // than one per slot); slots j >= P read as (fill0, fill1).
+  auto read_pairs = [&](uint32_t* x0, uint32_t* x1, uint32_t fill0, uint32_t fill1) {
+#pragma unroll
+    for (int j = 0; j < kMaxP; ++j) {
+      const uint2 w = *reinterpret_cast<const uint2*>(&xv[j][0]);
+      x0[j] = j < P ? w.x : fill0;
+      x1[j] = j < P ? w.y : fill1;
+    }
+  };
 
   // ---- workgroup reduction of a float64 sum -------------------------------------
   auto wg_sum = [&](double v) -> double {
@@ -284,19 +294,30 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
       return;
     }
     if constexpr (CACHED) {
-      const uint4 u = lc[c];
+      // (the empty asm keeps each conversion where it is written: the
+      // compiler would otherwise hoist the residual passes' conversions out
+      // of the test loop, in front of the first test)
+      // (V % 8 == 0 here, so a chunk starting inside the slice is whole)
+      uint4 u = lc[c];
+      asm volatile("" : "+v"(u.x), "+v"(u.y), "+v"(u.z), "+v"(u.w));
       const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        v[e] = y0 + e < V ? bf16_to_f32((bf16_bits)(w[e >> 1] >> (16 * (e & 1)))) : -INFINITY;
+      for (int e = 0; e < 8; ++e) v[e] = bf16_to_f32((bf16_bits)(w[e >> 1] >> (16 * (e & 1))));
     } else {
       load8<LT>(row, y0, V, vec, -INFINITY, v);
     }
   };
   auto q8_of = [&](int c, float* q8) {
     if constexpr (CACHED) {
+      // (the empty asm keeps each use where it is written: hoisted out of
+      // the test loop, the use would wait for the draft row before the first
+      // test)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) q8[e] = qc[c][e];
+      for (int e = 0; e < 8; ++e) {
+        float q = qc[c][e];
+        asm volatile("" : "+v"(q));
+        q8[e] = q;
+      }
     } else {
       const int y0 = y0_of(c);
       if (y0 < sl1) {
@@ -437,11 +458,14 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
     // row (unless prefetched), the draft row, and the first child's row.
     // (the logit is kept as loaded and converted only when it is stored, so
     // nothing waits for these loads before the statistics pass)
+    // (every thread loads, lanes past the children reading node 0's values:
+    // a branch around the loads would make its merge wait for them)
     LT kl_raw = LT(0);
     float kq = 0.f, ku = 0.f;
     const bool kid_lane = mss && tid < min(nk, kMaxKid);
-    if (kid_lane) {
-      const int node = kids[tid];
+    if constexpr (mss) {
+      const int kid = kids[tid < kMaxKid ? tid : 0];
+      const int node = kid_lane ? kid : 0;
       const int x = s_tok[node];
       kl_raw = row[x];
       kq = a.draft[((size_t)b * T + cur) * V + x];
@@ -505,12 +529,17 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
       exchange(__float_as_uint(bv), (uint32_t)bi);
       float gv = -INFINITY;
       int gi = V;
-      for (int j = 0; j < P; ++j) {
-        const float v = xf(j, 0);
-        const int i = (int)xv[j][1];
-        if (v > gv || (v == gv && i < gi)) {
-          gv = v;
-          gi = i;
+      {
+        uint32_t x0[kMaxP], x1[kMaxP];
+        read_pairs(x0, x1, __float_as_uint(-INFINITY), (uint32_t)V);
+#pragma unroll
+        for (int j = 0; j < kMaxP; ++j) {
+          const float v = __uint_as_float(x0[j]);
+          const int i = (int)x1[j];
+          if (v > gv || (v == gv && i < gi)) {
+            gv = v;
+            gi = i;
+          }
         }
       }
       for (int c = 0; c < nk; ++c)
@@ -572,15 +601,25 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
         kid_u[tid] = ku;
       }
       exchange(__float_as_uint(mw), __float_as_uint((float)sw));
-      float m = -INFINITY;
-      for (int j = 0; j < P; ++j) m = fmaxf(m, xf(j, 0));
-      if (tid < P) {
-        const float mj = xf(tid, 0);
-        mass[tid] = mj == -INFINITY ? 0.0 : (double)xf(tid, 1) * (double)__builtin_amdgcn_exp2f((mj - m) * c2);
+      // Slice j's (max, mass) sits in lane j % 16 of every wavefront; the
+      // global max and the masses' sum are formed by butterflies over those
+      // 16 lanes, which leave the same value in every lane (each step adds a
+      // pair of values in either order).  mass[] is read only by the draw.
+      float m;
+      double z0;
+      {
+        const int j = lane & 15;
+        const float mj = j < P ? xf(j, 0) : -INFINITY;
+        const float sj = j < P ? xf(j, 1) : 0.f;
+        m = mj;
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));
+        const double mass_j = mj == -INFINITY ? 0.0 : (double)sj * (double)__builtin_amdgcn_exp2f((mj - m) * c2);
+        z0 = mass_j;
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1) z0 += __shfl_xor(z0, off);
+        if (tid < P) mass[tid] = mass_j;
       }
-      lds_sync();
-      double z0 = 0.0;
-      for (int j = 0; j < P; ++j) z0 += mass[j];
       auto ew8 = [&](int c, double* w8) {
         float v[8];
         logits8(c, v);
@@ -593,7 +632,12 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
         const int x = draw(u, ew8);
         exchange((uint32_t)(x + 1), 0u);   // only the drawing workgroup has x >= 0
         int xs = -1;
-        for (int j = 0; j < P; ++j) xs = max(xs, (int)xv[j][0] - 1);
+        {
+          uint32_t x0[kMaxP], x1[kMaxP];
+          read_pairs(x0, x1, 0u, 0u);
+#pragma unroll
+          for (int j = 0; j < kMaxP; ++j) xs = max(xs, (int)x0[j] - 1);
+        }
         for (int c = 0; c < nk; ++c)
           if (s_tok[kids[c]] == xs) {
             nxt = c;
@@ -621,22 +665,39 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
         auto p_of = [&](float l) -> double {
           return l == -INFINITY ? 0.0 : (double)__builtin_amdgcn_exp2f((l - m) * c2) * iz0;
         };
-        // CACHED: this thread's elements of the current residual, in float64
+        // CACHED: this thread's elements of the current residual, in float64,
+        // formed at the first rejection (a first child accepted at once never
+        // needs them)
         double rr[CACHED ? kMaxCh : 1][8];
-        if constexpr (CACHED) {
-          FOR_CHUNKS(cc,
-            float v[8];
-            logits8(cc, v);
-            _Pragma("unroll")
-            for (int e = 0; e < 8; ++e) rr[cc][e] = p_of(v[e]);
-          )
-        }
+        auto init_rr = [&]() {
+          if constexpr (CACHED) {
+            FOR_CHUNKS(cc,
+              float v[8];
+              logits8(cc, v);
+              _Pragma("unroll")
+              for (int e = 0; e < 8; ++e) rr[cc][e] = p_of(v[e]);
+            )
+          }
+        };
         for (int c = 0; c < nk && nrej < kMaxRej; ++c) {
-          const int node = kids[c];
-          const int x = s_tok[node];
-          const float lx = c < kMaxKid ? kid_l[c] : Elem<LT>::load(row, x);
-          const double qx = c < kMaxKid ? (double)kid_q[c] : (double)qrow[x];
-          const double u = c < kMaxKid ? (double)kid_u[c] : (double)a.unif[((size_t)b * T + node) * 2];
+          if (c > 0 && c % kMaxKid == 0) {
+            // the next batch of children's test scalars (wide nodes only);
+            // these loads are waited for here, off the common path
+            lds_sync();
+            const int cc = c + tid;
+            if (tid < kMaxKid && cc < nk) {
+              const int node = kids[cc];
+              const int x = s_tok[node];
+              kid_l[tid] = Elem<LT>::load(row, x);
+              kid_q[tid] = qrow[x];
+              kid_u[tid] = a.unif[((size_t)b * T + node) * 2];
+            }
+            lds_sync();
+          }
+          const int ci = c % kMaxKid;
+          const float lx = kid_l[ci];
+          const double qx = (double)kid_q[ci];
+          const double u = (double)kid_u[ci];
           const double rx = resid(p_of(lx), qx, nrej);
           if (u * qx < rx) {
             nxt = c;
@@ -646,6 +707,7 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
           // float64 precision
           double pz = 0.0;
           if constexpr (CACHED) {
+            if (nrej == 0) init_rr();
             FOR_CHUNKS(cc,
               float q8[8];
               q8_of(cc, q8);
@@ -668,9 +730,14 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
           pz = wg_sum(pz);
           const unsigned long long pzb = (unsigned long long)__double_as_longlong(pz);
           exchange((uint32_t)pzb, (uint32_t)(pzb >> 32));
-          double z = 0.0;
-          for (int j = 0; j < P; ++j)
-            z += __longlong_as_double((long long)(((unsigned long long)xv[j][1] << 32) | xv[j][0]));
+          double z;
+          {
+            // butterfly over the 16 slices, as for z0
+            const int j = lane & 15;
+            z = j < P ? __longlong_as_double((long long)(((unsigned long long)xv[j][1] << 32) | xv[j][0])) : 0.0;
+#pragma unroll
+            for (int off = 1; off < 16; off <<= 1) z += __shfl_xor(z, off);
+          }
           if (z > 0.0 && tid < P)
             mass[tid] = __longlong_as_double((long long)(((unsigned long long)xv[tid][1] << 32) | xv[tid][0]));
           const double zi = z > 0.0 ? 1.0 / z : 0.0;
@@ -692,6 +759,7 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
           ++nrej;
         }
         if (nxt < 0) {
+          if (nrej == 0) init_rr();   // a leaf: the draw is from p itself
           const float u = a.unif[((size_t)b * T + cur) * 2 + 1];
           const int nr = nrej;
           // weights in the units of mass[]: the residual times the normaliser of
