@@ -24,6 +24,8 @@
 // (the likeliest next node).  An inverse-CDF draw picks the slice holding the crossing point
 // from the per-slice masses and only that workgroup rescans its slice.  Sums
 // are float64; the probability a test is taken on is recomputed in float64.
+#include <type_traits>
+
 #include "common.h"
 
 namespace sdtree {
@@ -49,8 +51,51 @@ __device__ __forceinline__ void lds_sync() {
   asm volatile("" ::: "memory");
 }
 
+// Cross-lane moves through DPP (no LDS round trip).  dpp_*<CTRL, ROWS>(old, v)
+// returns v of the lane CTRL selects, or `old` in rows outside ROWS.
+// Row-local reductions use: swap neighbours (quad_perm 1,0,3,2), swap pairs
+// (quad_perm 2,3,0,1), mirror within 8 lanes, mirror within 16 lanes -- after
+// these a 16-lane row holds its total in every lane, and since each step
+// combines a pair of values in either order, every lane holds the same bits.
+// Broadcasting lane 15 of each row into the next row (rows 1, 3) and lane 31
+// into rows 2, 3 then leaves the wavefront's total in lane 63.
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+constexpr int kDppBcast15 = 0x142, kDppBcast31 = 0x143;
+template <int CTRL, int ROWS>
+__device__ __forceinline__ int dpp_i(int old, int v) {
+  return __builtin_amdgcn_update_dpp(old, v, CTRL, ROWS, 0xF, false);
+}
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_f(float old, float v) {
+  return __int_as_float(dpp_i<CTRL, ROWS>(__float_as_int(old), __float_as_int(v)));
+}
+template <int CTRL, int ROWS>
+__device__ __forceinline__ double dpp_d(double old, double v) {
+  const long long o = __double_as_longlong(old), x = __double_as_longlong(v);
+  const int lo = dpp_i<CTRL, ROWS>((int)o, (int)x);
+  const int hi = dpp_i<CTRL, ROWS>((int)(o >> 32), (int)(x >> 32));
+  return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
+}
+// Reduce a value of type X over each 16-lane row with comb(a, b) (commutative);
+// with WAVE, go on to leave the wavefront's total in lane 63 (`id` is the
+// identity of comb, taken by lanes outside the broadcast rows).
+template <bool WAVE, typename X, typename Mv, typename Comb>
+__device__ __forceinline__ X dpp_reduce(X v, X id, Mv mv, Comb comb) {
+  v = comb(v, mv(std::integral_constant<int, kDppXor1>(), std::integral_constant<int, 0xF>(), id, v));
+  v = comb(v, mv(std::integral_constant<int, kDppXor2>(), std::integral_constant<int, 0xF>(), id, v));
+  v = comb(v, mv(std::integral_constant<int, kDppHalfMirror>(), std::integral_constant<int, 0xF>(), id, v));
+  v = comb(v, mv(std::integral_constant<int, kDppMirror>(), std::integral_constant<int, 0xF>(), id, v));
+  if constexpr (WAVE) {
+    v = comb(v, mv(std::integral_constant<int, kDppBcast15>(), std::integral_constant<int, 0xA>(), id, v));
+    v = comb(v, mv(std::integral_constant<int, kDppBcast31>(), std::integral_constant<int, 0xC>(), id, v));
+  }
+  return v;
+}
+
+// float64 sum over the wavefront, in lane 63
 __device__ __forceinline__ double wave_sum_d(double v) {
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  auto mv = [](auto c, auto r, double old, double x) { return dpp_d<decltype(c)::value, decltype(r)::value>(old, x); };
+  return dpp_reduce<true>(v, 0.0, mv, [](double x, double y) { return x + y; });
   return v;
 }
 
@@ -238,7 +283,7 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
   auto wg_sum = [&](double v) -> double {
     v = wave_sum_d(v);
     lds_sync();
-    if (lane == 0) red_d[wave] = v;
+    if (lane == 63) red_d[wave] = v;
     lds_sync();
     double t = 0.0;
     for (int w = 0; w < kAW; ++w) t += red_d[w];
@@ -505,16 +550,19 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
             bi = y0 + e;
           }
       )
-      for (int off = 32; off >= 1; off >>= 1) {
-        const float ov = __shfl_xor(bv, off);
-        const int oi = __shfl_xor(bi, off);
-        if (ov > bv || (ov == bv && oi < bi)) {
-          bv = ov;
-          bi = oi;
-        }
+      {
+        struct VI { float v; int i; };
+        auto mv = [&](auto c, auto r, VI old, VI x) {
+          return VI{dpp_f<decltype(c)::value, decltype(r)::value>(old.v, x.v),
+                    dpp_i<decltype(c)::value, decltype(r)::value>(old.i, x.i)};
+        };
+        auto comb = [](VI x, VI y) { return (y.v > x.v || (y.v == x.v && y.i < x.i)) ? y : x; };
+        const VI t = dpp_reduce<true>(VI{bv, bi}, VI{-INFINITY, V}, mv, comb);
+        bv = t.v;
+        bi = t.i;
       }
       lds_sync();
-      if (lane == 0) {
+      if (lane == 63) {
         red_f[wave] = bv;
         red_i[wave] = bi;
       }
@@ -564,24 +612,32 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
         for (int e = 1; e < 8; ++e) cm = fmaxf(cm, v[e]);
         if (cm > -INFINITY) {
           const float mn = fmaxf(mt, cm);
-          double add = 0.0;
+          double w[8];
           _Pragma("unroll")
-          for (int e = 0; e < 8; ++e) add += (double)__builtin_amdgcn_exp2f((v[e] - mn) * c2);
+          for (int e = 0; e < 8; ++e) w[e] = (double)__builtin_amdgcn_exp2f((v[e] - mn) * c2);
+          const double add = ((w[0] + w[1]) + (w[2] + w[3])) + ((w[4] + w[5]) + (w[6] + w[7]));
           st = (mt == -INFINITY ? 0.0 : st * (double)__builtin_amdgcn_exp2f((mt - mn) * c2)) + add;
           mt = mn;
         }
       )
-      for (int off = 32; off >= 1; off >>= 1) {
-        const float om = __shfl_xor(mt, off);
-        const double os = __shfl_xor(st, off);
-        const float mn = fmaxf(mt, om);
-        if (mn > -INFINITY)
-          st = (mt == -INFINITY ? 0.0 : st * (double)__builtin_amdgcn_exp2f((mt - mn) * c2)) +
-               (om == -INFINITY ? 0.0 : os * (double)__builtin_amdgcn_exp2f((om - mn) * c2));
-        mt = mn;
+      {
+        struct MS { float m; double s; };
+        auto mv = [&](auto c, auto r, MS old, MS x) {
+          return MS{dpp_f<decltype(c)::value, decltype(r)::value>(old.m, x.m),
+                    dpp_d<decltype(c)::value, decltype(r)::value>(old.s, x.s)};
+        };
+        auto comb = [&](MS x, MS y) {
+          const float mn = fmaxf(x.m, y.m);
+          if (mn == -INFINITY) return MS{mn, 0.0};
+          return MS{mn, (x.m == -INFINITY ? 0.0 : x.s * (double)__builtin_amdgcn_exp2f((x.m - mn) * c2)) +
+                            (y.m == -INFINITY ? 0.0 : y.s * (double)__builtin_amdgcn_exp2f((y.m - mn) * c2))};
+        };
+        const MS t = dpp_reduce<true>(MS{mt, st}, MS{-INFINITY, 0.0}, mv, comb);
+        mt = t.m;
+        st = t.s;
       }
       lds_sync();
-      if (lane == 0) {
+      if (lane == 63) {
         red_f[wave] = mt;
         red_d[wave] = st;
       }
@@ -611,13 +667,11 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
         const int j = lane & 15;
         const float mj = j < P ? xf(j, 0) : -INFINITY;
         const float sj = j < P ? xf(j, 1) : 0.f;
-        m = mj;
-#pragma unroll
-        for (int off = 1; off < 16; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));
+        auto mvf = [](auto c, auto r, float old, float x) { return dpp_f<decltype(c)::value, decltype(r)::value>(old, x); };
+        auto mvd = [](auto c, auto r, double old, double x) { return dpp_d<decltype(c)::value, decltype(r)::value>(old, x); };
+        m = dpp_reduce<false>(mj, -INFINITY, mvf, [](float x, float y) { return fmaxf(x, y); });
         const double mass_j = mj == -INFINITY ? 0.0 : (double)sj * (double)__builtin_amdgcn_exp2f((mj - m) * c2);
-        z0 = mass_j;
-#pragma unroll
-        for (int off = 1; off < 16; off <<= 1) z0 += __shfl_xor(z0, off);
+        z0 = dpp_reduce<false>(mass_j, 0.0, mvd, [](double x, double y) { return x + y; });
         if (tid < P) mass[tid] = mass_j;
       }
       auto ew8 = [&](int c, double* w8) {
@@ -735,8 +789,8 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
             // butterfly over the 16 slices, as for z0
             const int j = lane & 15;
             z = j < P ? __longlong_as_double((long long)(((unsigned long long)xv[j][1] << 32) | xv[j][0])) : 0.0;
-#pragma unroll
-            for (int off = 1; off < 16; off <<= 1) z += __shfl_xor(z, off);
+            auto mvd = [](auto c, auto r, double old, double x) { return dpp_d<decltype(c)::value, decltype(r)::value>(old, x); };
+            z = dpp_reduce<false>(z, 0.0, mvd, [](double x, double y) { return x + y; });
           }
           if (z > 0.0 && tid < P)
             mass[tid] = __longlong_as_double((long long)(((unsigned long long)xv[tid][1] << 32) | xv[tid][0]));
