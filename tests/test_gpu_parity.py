@@ -50,6 +50,32 @@ def test_attention_small_full_compare(name):
     check_attention(gpu, ref, c.dtype, name)
 
 
+# Shapes whose (sequence, KV head, 256-row query tile) count fills the chip
+# without a context split: the bf16 path then runs its 256-row workgroups over
+# 32-key tiles (ragged contexts, a ragged tree tail, a deep best-first tree
+# whose far tree tiles are skipped).
+WIDE_TILE = {
+    "tree64": ("llama3_8b_tree64", dict(B=32, ctx_lo=61, ctx_hi=190)),
+    "tree200": ("llama3_8b_tree64", dict(B=32, T=200, ctx_lo=40, ctx_hi=97)),
+    "bestfirst1024": ("specexec_70b_tree2048", dict(T=1024, ctx_lo=77, ctx_hi=77, V=700)),
+}
+
+
+@pytest.mark.parametrize("case", sorted(WIDE_TILE))
+def test_attention_wide_query_tile(case):
+    name, over = WIDE_TILE[case]
+    c = small_variant(name, **over)
+    M = c.T * (c.Hq // c.Hkv)
+    assert c.dtype == "bf16" and c.D == 128 and M > 128 and c.B * c.Hkv * ((M + 255) // 256) >= 256
+    _say("attention wide query tile %s" % case)
+    x = make_inputs(c)
+    d = to_device(x)
+    gpu = _run_attn(x, d)
+    ref = oracle.attention_dense(x.q, x.k_pages, x.v_pages, x.block_table, x.ctx_lens,
+                                 x.tree_parent, c.bs, c.dtype)
+    check_attention(gpu, ref, c.dtype, case)
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("case", ["T1", "ctx0", "shared_tree", "forest", "ragged_tail", "gqa1",
                                   "d64", "chain_deep", "wide_T"])

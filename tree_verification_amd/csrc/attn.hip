@@ -205,7 +205,9 @@ __global__ void __launch_bounds__(WQ * WK * 64) attn_mfma_kernel(AttnArgs a) {
   auto kswz = [](int r) -> int {
     return CK == 16 ? ((r & 3) | ((r >> 1) & 12)) : (((r >> 1) & 1) | (((r >> 3) & 3) << 1));
   };
-  auto vswz = [](int d) -> int { return CV == 16 ? (d & 15) : ((d >> 1) & 7); };
+  auto vswz = [](int d) -> int {
+    return CV == 16 ? (d & 15) : CV == 8 ? ((d >> 1) & 7) : ((d >> 2) & 3);
+  };
 
   extern __shared__ __align__(16) unsigned char smem[];
   unsigned char* Kst = smem;                                 // [S][K_BYTES]
@@ -282,6 +284,16 @@ __global__ void __launch_bounds__(WQ * WK * 64) attn_mfma_kernel(AttnArgs a) {
   int* s_par = reinterpret_cast<int*>(smem);
   static_assert(2 * (K_BYTES + V_BYTES) >= 4 * kMaxTreeNodes, "parents fit the ring");
   const int nn = i_hi - i_lo + 1;
+  // flag the tree tiles (NK nodes each) that a nonzero ancestor word touches
+  auto flag_word = [&](int w, uint64_t acc) {
+    if constexpr (NK >= 64) {
+      tflag[(w * 64) / NK] = 1;
+    } else {
+#pragma unroll
+      for (int h = 0; h < 64 / NK; ++h)
+        if ((acc >> (h * NK)) & ((1ull << NK) - 1ull)) tflag[(w * 64) / NK + h] = 1;
+    }
+  };
   if (tid < 128) tflag[tid] = 0;
   if (tid == 0) s_err = 0;
   for (int j = tid; j <= i_hi; j += NT) s_par[j] = a.parent[(size_t)bt * T + j];
@@ -296,7 +308,7 @@ __global__ void __launch_bounds__(WQ * WK * 64) attn_mfma_kernel(AttnArgs a) {
       const int w = n >> 6;
       if (w != cur_w) {
         row[cur_w] = acc;
-        tflag[(cur_w * 64) / NK] = 1;
+        flag_word(cur_w, acc);
         cur_w = w;
         acc = 0;
       }
@@ -307,7 +319,7 @@ __global__ void __launch_bounds__(WQ * WK * 64) attn_mfma_kernel(AttnArgs a) {
       n = par;
     }
     row[cur_w] = acc;
-    tflag[(cur_w * 64) / NK] = 1;
+    flag_word(cur_w, acc);
   }
 
   // ---- sparse: union of the blocks selected by this workgroup's rows -----
@@ -867,9 +879,9 @@ __global__ void __launch_bounds__(WQ * WK * 64) attn_mfma_kernel(AttnArgs a) {
     if (k + 1 < n_tight) tight_sources(sp_tag, t_lo + k + 1 + S);
     if constexpr (SP) sparse_mask(t_lo + k, sc);
     softmax_bound(sc);
-    // tile k's V^T fragments are read before the score MFMAs, so their LDS
-    // latency is covered; the scheduling barrier keeps the compiler from
-    // sinking the reads to their first use
+    // the K fragments of tile k + 1 and the V^T fragments of tile k are read
+    // before any MFMA, so their LDS latency is covered; the scheduling
+    // barrier keeps the compiler from sinking the reads to their first use
     KFrag kf;
     load_k((k + 1) % S, kf);
     VFrag vf;
@@ -1059,6 +1071,12 @@ static hipError_t launch_mfma_cfg(const AttnArgs& a, size_t lds, hipStream_t st)
 
 template <int D>
 static hipError_t launch_mfma_d(const AttnArgs& a, const AttnPlan& p, hipStream_t st) {
+  if constexpr (D == 128) {
+    if (p.WQ == 8) {
+      if (p.stages == 8) return launch_mfma_cfg<D, 32, 8, 1, 32, 8>(a, p.lds_bytes, st);
+      return launch_mfma_cfg<D, 32, 8, 1, 32, 4>(a, p.lds_bytes, st);
+    }
+  }
   if (p.WQ == 1) return launch_mfma_cfg<D, 32, 1, 4, 32, 2>(a, p.lds_bytes, st);
   if (p.WQ == 2) {
     if (p.stages == 4) return launch_mfma_cfg<D, 32, 2, 2, 32, 4>(a, p.lds_bytes, st);

@@ -56,10 +56,18 @@ static AttnPlan plan_attn(const sd_shape* s, int ksel, bool sparse) {
     p.WQ = 1; p.WK = 4; p.QW = 32; p.KW = 32;
   } else if (M <= 64) {
     p.WQ = 2; p.WK = 2; p.QW = 32; p.KW = 32;
-  } else {
+  } else if (M <= 128 || p.D != 128 || (long long)s->B * s->Hkv * ((M + 255) / 256) < 256) {
     // eight wavefronts: four 32-row query slices x two 32-key slices, two
     // wavefronts per SIMD so one's MFMAs overlap the other's softmax
     p.WQ = 4; p.WK = 2; p.QW = 32; p.KW = 32;
+  } else {
+    // eight wavefronts of 32 query rows each over 32-key tiles: one workgroup
+    // streams a (sequence, KV head)'s keys once for 256 query rows, halving
+    // the L2-to-LDS traffic of many query tiles.  Taken when it fills the
+    // chip without splitting the context (a split's partials and their merge
+    // cost more than the halved traffic saves), and for D = 128 (a 32-key K
+    // tile is then one 16-byte load per thread).
+    p.WQ = 8; p.WK = 1; p.QW = 32; p.KW = 32;
   }
   p.NK = p.KW * p.WK;
   p.rows = p.WQ * p.QW;
@@ -100,9 +108,11 @@ static AttnPlan plan_attn(const sd_shape* s, int ksel, bool sparse) {
   extras += 8 * anc_need;
   // deepest ring that fits: 4, 3 or 2 stages for the wide tile, 4 or 2 for
   // two key slices, 2 for four key slices
-  const int cand[3] = {4, 3, 2};
+  const int cand[5] = {8, 4, 3, 2, 0};
   p.stages = 0;
   for (int c : cand) {
+    if (c == 0) break;
+    if (p.WQ == 8 ? (c != 8 && c != 4) : c == 8) continue;
     if (p.WQ == 1 && c != 2) continue;
     if (p.WQ == 2 && c == 3) continue;
     const size_t merge = p.WK > 1 ? (size_t)p.WQ * p.WK * (p.QW * p.D + 2 * p.QW) * 4 : 0;
@@ -111,7 +121,7 @@ static AttnPlan plan_attn(const sd_shape* s, int ksel, bool sparse) {
       break;
     }
   }
-  if (p.stages == 0) p.stages = 2;   // reported as SD_UNSUPPORTED by the LDS check
+  if (p.stages == 0) p.stages = p.WQ == 8 ? 4 : 2;   // reported as SD_UNSUPPORTED by the LDS check
   const size_t merge = p.WK > 1 ? (size_t)p.WQ * p.WK * (p.QW * p.D + 2 * p.QW) * 4 : 0;
   size_t lds = std::max(p.stages * stage, merge) + extras;
   p.lds_bytes = align_up(lds, 16);
