@@ -605,11 +605,13 @@ __global__ void __launch_bounds__(WQ * WK * 64) attn_mfma_kernel(AttnArgs a) {
               Kt + key * (D * 2) + (((ds * 4 + lg) ^ kswz(key)) * 16));
       }
   };
-  auto qk_regs = [&](const KFrag& kf, STile& s) __attribute__((always_inline)) {
+  // (halves: a bit mask of the 16-row key halves to compute)
+  auto qk_regs = [&](const KFrag& kf, STile& s, int halves = 3) __attribute__((always_inline)) {
 #pragma unroll
     for (int kg = 0; kg < KG; ++kg)
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
+        if (!((halves >> half) & 1)) continue;
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) s[qb][2 * kg + half] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -882,12 +884,20 @@ __global__ void __launch_bounds__(WQ * WK * 64) attn_mfma_kernel(AttnArgs a) {
     // the K fragments of tile k + 1 and the V^T fragments of tile k are read
     // before any MFMA, so their LDS latency is covered; the scheduling
     // barrier keeps the compiler from sinking the reads to their first use
+    // The next step's block-table reads are scalar loads, which return out of
+    // order; waited for here, they leave only the in-order fragment reads
+    // pending.  At most 15 of those are outstanding at a time (the counter's
+    // range), so each MFMA waits for just its own operands: the K fragments,
+    // the first key half's scores, then the V^T fragments.
+    __builtin_amdgcn_s_waitcnt(lgkmcnt_imm(0));
     KFrag kf;
     load_k((k + 1) % S, kf);
+    __builtin_amdgcn_sched_barrier(0);
+    qk_regs(kf, sn, 1);
     VFrag vf;
     load_v(k % S, vf);
     __builtin_amdgcn_sched_barrier(0);
-    qk_regs(kf, sn);
+    qk_regs(kf, sn, 2);
     exp_tile(sc, pf);
     pv_regs(vf, pf);
   };
