@@ -7,7 +7,10 @@ One step is one verification pass over one batch: tree-masked attention
 walk (sd_accept) and the commit of the accepted paths (sd_kv_commit); the
 sparse workload first selects blocks (sd_topk_blocks) and attends sparsely.
 The context lengths are restored after each commit (a 4-byte-per-sequence
-device copy inside the step) so every step does the same work.
+device copy inside the step) so every step does the same work.  The K/V
+pages are held in several copies (--kv-copies, default 2) and consecutive
+steps use different ones, so a step cannot find the previous step's K/V in
+the 256 MB last-level cache.
 
 Prints one JSON line: verified tree tokens/s (B * T per step) over the timed
 steps, the attention call against the HBM or MFMA roofline (algorithmic
@@ -38,6 +41,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--kv-copies", type=int, default=2,
+                    help="K/V page copies, used by consecutive steps in turn")
     ap.add_argument("--workload", default="llama3_8b_tree64")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -220,7 +225,7 @@ class HipEvent:
 
 
 class Workload:
-    def __init__(self, name):
+    def __init__(self, name, kv_copies=1):
         import torch
         import tree_verification_amd as tva
         from synth import CONFIGS, make_inputs
@@ -235,6 +240,8 @@ class Workload:
                 return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
             return torch.from_numpy(a).cuda()
         self.q, self.k, self.v = dev(x.q), dev(x.k_pages), dev(x.v_pages)
+        self.kvs = [(self.k, self.v)] + [(self.k.clone(), self.v.clone()) for _ in range(kv_copies - 1)]
+        self.n_steps = 0
         self.table, self.ctx = dev(x.block_table), dev(x.ctx_lens)
         self.ctx0 = self.ctx.clone()
         self.parent, self.token = dev(x.tree_parent), dev(x.tree_token)
@@ -256,6 +263,8 @@ class Workload:
 
     def step(self, ev=None):
         tva = self.tva
+        self.k, self.v = self.kvs[self.n_steps % len(self.kvs)]
+        self.n_steps += 1
         if self.sel is not None:
             tva.topk_blocks(self.q, self.k, self.table, self.ctx, self.cfg.topk, sel=self.sel)
         if ev is not None:
@@ -364,7 +373,7 @@ def main():
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
-    w = Workload(args.workload)
+    w = Workload(args.workload, max(1, args.kv_copies))
     cfg = w.cfg
     for _ in range(args.warmup):
         w.step()
@@ -416,7 +425,8 @@ def main():
         "data": "synthetic (seeded; shapes of the workload, no datasets or weights)",
         "config": {"workload": cfg.name, "B": cfg.B, "T": cfg.T, "Hq": cfg.Hq, "Hkv": cfg.Hkv,
                    "D": cfg.D, "ctx": [cfg.ctx_lo, cfg.ctx_hi], "block": cfg.bs, "V": cfg.V,
-                   "accept": cfg.mode, "temperature": w.tau, "topk": cfg.topk or None},
+                   "accept": cfg.mode, "temperature": w.tau, "topk": cfg.topk or None,
+                   "kv_copies": len(w.kvs)},
         "roofline": dict(roof, kernel="sd_tree_verify_attn (tree-masked attention kernel)",
                          attention_us=round(attn_s * 1e6, 2), bytes_per_call=int(bytes_),
                          flops_per_call=int(flops)),
