@@ -130,41 +130,87 @@ __global__ void __launch_bounds__(256) block_score_kernel(TopkArgs a) {
   for (int r0 = 0; r0 < R; r0 += RC) {
     const int rc = min(RC, R - r0);
     __syncthreads();
-    for (int idx = tid; idx < rc * D; idx += 256) {
-      const int rr = idx / D, d = idx % D;
-      const int r = r0 + rr;
+    // 8-dim chunks, all of a thread's loads issued before any is used
+    constexpr int NCH = RC * D / 8 / 256;     // chunks per thread
+    float qv8[NCH][8];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int idx = tid + 256 * c;
+      const int rr = idx / (D / 8), d0 = (idx % (D / 8)) * 8;
+      const int r = r0 + min(rr, rc - 1);
       const int i = r / a.G, h = g * a.G + r % a.G;
-      qs[rr][(d % 16) * EL + d / 16] =
-          Elem<E>::load(reinterpret_cast<const E*>(a.q), (((size_t)b * a.T + i) * a.Hq + h) * D + d);
+      const E* src = reinterpret_cast<const E*>(a.q) + (((size_t)b * a.T + i) * a.Hq + h) * D + d0;
+      if constexpr (sizeof(E) == 2) {
+        const uint4 u = *reinterpret_cast<const uint4*>(src);
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qv8[c][e] = bf16_to_f32((bf16_bits)(w[e >> 1] >> (16 * (e & 1))));
+      } else {
+        const float4 u0 = reinterpret_cast<const float4*>(src)[0], u1 = reinterpret_cast<const float4*>(src)[1];
+        qv8[c][0] = u0.x; qv8[c][1] = u0.y; qv8[c][2] = u0.z; qv8[c][3] = u0.w;
+        qv8[c][4] = u1.x; qv8[c][5] = u1.y; qv8[c][6] = u1.z; qv8[c][7] = u1.w;
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int idx = tid + 256 * c;
+      const int rr = idx / (D / 8), d0 = (idx % (D / 8)) * 8;
+      if (rr < rc)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qs[rr][((d0 + e) % 16) * EL + (d0 + e) / 16] = qv8[c][e];
     }
     __syncthreads();
-    for (int nn = grp; nn < nbc; nn += 16) {
-      const float* mrow = a.means + (((size_t)b * a.nbmax + n0 + nn) * a.Hkv + g) * D;
-      float m[EL];
+    // this group's NBG blocks (grp, grp + 16, ...) against two rows at a time:
+    // 2 NBG independent dot products in flight per lane
+    constexpr int NBG = NBC / 16;
+    float m[NBG][EL];
 #pragma unroll
-      for (int e = 0; e < EL; ++e) m[e] = mrow[dl + 16 * e];
-      for (int rr = 0; rr < rc; ++rr) {
-        float v[EL];
-        const float4* qv = reinterpret_cast<const float4*>(&qs[rr][dl * EL]);
+    for (int j = 0; j < NBG; ++j) {
+      const int nn = grp + 16 * j;
+      const float* mrow = a.means + (((size_t)b * a.nbmax + n0 + min(nn, nbc - 1)) * a.Hkv + g) * D;
+#pragma unroll
+      for (int e = 0; e < EL; ++e) m[j][e] = mrow[dl + 16 * e];
+    }
+    for (int rr0 = 0; rr0 < rc; rr0 += 2) {
+      float q[2][EL];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const float4* qv = reinterpret_cast<const float4*>(&qs[min(rr0 + u, rc - 1)][dl * EL]);
 #pragma unroll
         for (int e4 = 0; e4 < EL / 4; ++e4) {
           const float4 q4 = qv[e4];
-          v[4 * e4 + 0] = q4.x * m[4 * e4 + 0];
-          v[4 * e4 + 1] = q4.y * m[4 * e4 + 1];
-          v[4 * e4 + 2] = q4.z * m[4 * e4 + 2];
-          v[4 * e4 + 3] = q4.w * m[4 * e4 + 3];
+          q[u][4 * e4 + 0] = q4.x;
+          q[u][4 * e4 + 1] = q4.y;
+          q[u][4 * e4 + 2] = q4.z;
+          q[u][4 * e4 + 3] = q4.w;
+        }
+      }
+      float sc[NBG][2];
+#pragma unroll
+      for (int j = 0; j < NBG; ++j)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          float v[EL];
+#pragma unroll
+          for (int e = 0; e < EL; ++e) v[e] = q[u][e] * m[j][e];
+#pragma unroll
+          for (int hw = EL / 2; hw >= 1; hw >>= 1)
+#pragma unroll
+            for (int e = 0; e < hw; ++e) v[e] = v[e] + v[e + hw];
+          sc[j][u] = v[0];
         }
 #pragma unroll
-        for (int hw = EL / 2; hw >= 1; hw >>= 1)
+      for (int n = 8; n >= 1; n >>= 1)
 #pragma unroll
-          for (int e = 0; e < hw; ++e) v[e] = v[e] + v[e + hw];
-        float sc = v[0];
-        sc = row_ror_add(sc, 8);
-        sc = row_ror_add(sc, 4);
-        sc = row_ror_add(sc, 2);
-        sc = row_ror_add(sc, 1);
-        if (dl == 0) ss[rr][nn] = sc;
-      }
+        for (int j = 0; j < NBG; ++j)
+#pragma unroll
+          for (int u = 0; u < 2; ++u) sc[j][u] = row_ror_add(sc[j][u], n);
+      if (dl == 0)
+#pragma unroll
+        for (int j = 0; j < NBG; ++j)
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+            if (grp + 16 * j < nbc && rr0 + u < rc) ss[rr0 + u][grp + 16 * j] = sc[j][u];
     }
     __syncthreads();
     for (int idx = tid; idx < rc * NBC; idx += 256) {
@@ -212,8 +258,22 @@ __global__ void __launch_bounds__(256) block_select_kernel(TopkArgs a) {
   // the row's keys, staged once when they fit
   const bool staged = nb <= kSelStage;
   uint32_t* kw = keys[wave];
-  if (staged)
-    for (int y = lane; y < nb; y += 64) kw[y] = score_key(sc[y]);
+  if (staged) {
+    // 16 loads per lane in flight at a time
+    for (int y0 = 0; y0 < nb; y0 += 64 * 16) {
+      float v[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int y = y0 + lane + 64 * u;
+        v[u] = sc[y < nb ? y : 0];
+      }
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int y = y0 + lane + 64 * u;
+        if (y < nb) kw[y] = score_key(v[u]);
+      }
+    }
+  }
   auto key_of = [&](int y) -> uint32_t { return staged ? kw[y] : score_key(sc[y]); };
   uint32_t prefix = 0, mask = 0, krem = (uint32_t)a.topk;
   for (int shift = 24; shift >= 0; shift -= 8) {
