@@ -19,7 +19,7 @@ namespace sdtree {
 
 // Block means.  A (b, block, KV head) unit is served by LPU lanes, each
 // owning one 16-byte column chunk (EPL consecutive dims) of the block's rows:
-// it walks the block's valid tokens in position order, 8 rows in flight, so
+// it walks the block's valid tokens in position order, 16 rows in flight, so
 // every dim's sum is the sequential one.  A wavefront serves 64 / LPU units.
 template <typename E, int D>
 __global__ void __launch_bounds__(256) block_mean_kernel(TopkArgs a) {
@@ -69,13 +69,14 @@ __global__ void __launch_bounds__(256) block_mean_kernel(TopkArgs a) {
       s[3] = s[3] + __uint_as_float(u.w);
     }
   };
+  constexpr int RIF = 16;   // rows in flight
   int t = 0;
-  for (; t + 8 <= valid; t += 8) {
-    uint4 x[8];
+  for (; t + RIF <= valid; t += RIF) {
+    uint4 x[RIF];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) x[u] = base[(size_t)(t + u) * RS];
+    for (int u = 0; u < RIF; ++u) x[u] = base[(size_t)(t + u) * RS];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) add(x[u]);
+    for (int u = 0; u < RIF; ++u) add(x[u]);
   }
   for (; t < valid; ++t) add(base[(size_t)t * RS]);
   const float fv = (float)valid;
