@@ -59,16 +59,16 @@ __global__ void __launch_bounds__(256) anc_mask_kernel(const int32_t* __restrict
 }
 
 // ---------------------------------------------------------------------------
-// float32 attention, one wavefront per query row (b, i, h).  Keys are walked
+// float32 attention, one workgroup per query row (b, i, h).  Keys are walked
 // 64 at a time in a virtual order: dense = positions [0, ctx) then the tree
 // slots ctx + j; sparse = the ksel * bs slots of the row's selected blocks,
 // then the tree slots.  Tree slot j is visible when j is an ancestor of i.
+// The four wavefronts take every fourth 64-key chunk, each with its own
+// online softmax, and merge their (max, sum, output) states at the end.
 template <typename E, int D>
 __global__ void __launch_bounds__(256) attn_valu_kernel(AttnArgs a) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const long long row = (long long)blockIdx.x * 4 + wave;
-  const long long nrows = (long long)a.B * a.T * a.Hq;
-  if (row >= nrows) return;
+  const long long row = blockIdx.x;
   const int h = (int)(row % a.Hq);
   const int i = (int)((row / a.Hq) % a.T);
   const int b = (int)(row / ((long long)a.Hq * a.T));
@@ -92,7 +92,7 @@ __global__ void __launch_bounds__(256) attn_valu_kernel(AttnArgs a) {
   const long long n_keys = n_ctx_keys + a.T;
   float m = -1e30f, l = 0.f, o[DL];
   for (int k = 0; k < DL; ++k) o[k] = 0.f;
-  for (long long c0 = 0; c0 < n_keys; c0 += 64) {
+  for (long long c0 = 64LL * wave; c0 < n_keys; c0 += 256) {
     // lane <-> key c0 + lane: position, visibility, score
     const long long kidx = c0 + lane;
     long long pos = -1;
@@ -136,18 +136,49 @@ __global__ void __launch_bounds__(256) attn_valu_kernel(AttnArgs a) {
     l = l * alpha + ps;
     m = mn;
     for (int k = 0; k < DL; ++k) o[k] *= alpha;
-    // lanes now own output dims: accumulate the 64 keys' values
+    // lanes now own output dims: accumulate the 64 keys' values, eight keys'
+    // loads in flight at a time (a key that is not visible reads element 0
+    // and contributes zero)
     const int vlo = (int)(vbase & 0xffffffffll), vhi = (int)(vbase >> 32);
-    for (int kk = 0; kk < 64; ++kk) {
-      const float w = __shfl(p, kk);
-      const long long base = ((long long)__shfl(vhi, kk) << 32) | (unsigned)__shfl(vlo, kk);
-      if (base >= 0) {
-        for (int k = 0; k < DL; ++k) o[k] += w * Elem<E>::load(V, base + (size_t)(lane + 64 * k) * a.bs);
+    for (int k0 = 0; k0 < 64; k0 += 8) {
+      float w[8], v[8][DL];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const long long base = ((long long)__shfl(vhi, k0 + u) << 32) | (unsigned)__shfl(vlo, k0 + u);
+        const bool vis = base >= 0;
+        w[u] = vis ? __shfl(p, k0 + u) : 0.f;
+        const long long bb = vis ? base : 0;
+#pragma unroll
+        for (int k = 0; k < DL; ++k) {
+          const float x = Elem<E>::load(V, bb + (size_t)(lane + 64 * k) * a.bs);
+          v[u][k] = vis ? x : 0.f;
+        }
       }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int k = 0; k < DL; ++k) o[k] += w[u] * v[u][k];
     }
   }
-  const float inv = l > 0.f ? 1.f / l : 0.f;
-  for (int k = 0; k < DL; ++k) Elem<E>::store(out, row * D + lane + 64 * k, o[k] * inv);
+  __shared__ float xm[4], xl[4], xo[4][D];
+  if (lane == 0) {
+    xm[wave] = m;
+    xl[wave] = l;
+  }
+  for (int k = 0; k < DL; ++k) xo[wave][lane + 64 * k] = o[k];
+  __syncthreads();
+  if (wave != 0) return;
+  float mt = xm[0];
+  for (int w = 1; w < 4; ++w) mt = fmaxf(mt, xm[w]);
+  float lt = 0.f, ot[DL];
+  for (int k = 0; k < DL; ++k) ot[k] = 0.f;
+  for (int w = 0; w < 4; ++w) {
+    const float f = exp2f(xm[w] - mt);
+    lt += xl[w] * f;
+    for (int k = 0; k < DL; ++k) ot[k] += xo[w][lane + 64 * k] * f;
+  }
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  for (int k = 0; k < DL; ++k) Elem<E>::store(out, row * D + lane + 64 * k, ot[k] * inv);
 }
 
 // ---------------------------------------------------------------------------
@@ -1056,7 +1087,7 @@ hipError_t launch_anc_mask(const int32_t* parent, int T, int W64, int n_trees, u
 template <int D>
 static hipError_t launch_valu_d(const AttnArgs& a, bool f32, hipStream_t st) {
   const long long nrows = (long long)a.B * a.T * a.Hq;
-  dim3 grid((unsigned)((nrows + 3) / 4));
+  dim3 grid((unsigned)nrows);
   if (f32)
     hipLaunchKernelGGL((attn_valu_kernel<float, D>), grid, dim3(256), 0, st, a);
   else
