@@ -19,11 +19,12 @@
 // partial through barrier-tagged atomic slots in the workspace (bounded spin;
 // B * P <= 256 workgroups, one per CU, are all resident); every workgroup then
 // reduces the P partials in the same order and takes the same decision.  At
-// each node the loads that the walk will need are issued together: the
-// test scalars of the children, the draft row, and the first child's logits
-// (the likeliest next node).  An inverse-CDF draw picks the slice holding the crossing point
-// from the per-slice masses and only that workgroup rescans its slice.  Sums
-// are float64; the probability a test is taken on is recomputed in float64.
+// each node the loads that the walk will need are issued together: the test
+// scalars of the children, the draft row and, after the statistics exchange,
+// the first child's logits (the likeliest next node).  An inverse-CDF draw
+// picks the slice holding the crossing point from the per-slice masses and
+// only that workgroup rescans its slice.  Sums are float64; the probability a
+// test is taken on is recomputed in float64.
 #include <type_traits>
 
 #include "common.h"
@@ -532,7 +533,12 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
         }
       }
     }
-    if (nk > 0) load_row(row_of(kids[0]), pfc);
+    // (greedy prefetches the first child's row now; the other rules after
+    // the statistics exchange, whose polling loads would otherwise wait for
+    // it: vector loads return in order)
+    if constexpr (MODE == kGreedy) {
+      if (nk > 0) load_row(row_of(kids[0]), pfc);
+    }
     int nxt = -1;
     bool stop = false;
     if constexpr (MODE == kGreedy) {
@@ -657,6 +663,7 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
         kid_u[tid] = ku;
       }
       exchange(__float_as_uint(mw), __float_as_uint((float)sw));
+      if (nk > 0) load_row(row_of(kids[0]), pfc);
       // Slice j's (max, mass) sits in lane j % 16 of every wavefront; the
       // global max and the masses' sum are formed by butterflies over those
       // 16 lanes, which leave the same value in every lane (each step adds a
