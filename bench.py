@@ -1,6 +1,7 @@
 """Benchmark of the tree-verification pass on one MI355X.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload llama3_8b_tree64]
+    python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--settle-ms 200]
+                    [--workload llama3_8b_tree64]
 
 One step is one verification pass over one batch: tree-masked attention
 (sd_tree_verify_attn, which also builds the ancestor masks), the acceptance
@@ -15,7 +16,11 @@ the 256 MB last-level cache.
 Prints one JSON line: verified tree tokens/s (B * T per step) over the timed
 steps, the attention call against the HBM or MFMA roofline (algorithmic
 bytes or FLOPs per call / event-timed call duration), and the CPU oracle
-timed on a bounded sample of the same workload.
+timed on a bounded sample of the same workload.  The attention call of every
+10th timed step (--event-every) is bracketed by HIP events: an event record
+leaves the GPU idle for a few microseconds, so bracketing every call would
+add that idle time to every step.  Before the warmup steps, untimed steps
+run for --settle-ms so the GPU has left its idle clocks.
 """
 import argparse
 import hashlib
@@ -39,8 +44,15 @@ METRIC = "verified tree tokens/s + achieved HBM GB/s (or MFMA %) of tree-verify,
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--settle-ms", type=float, default=200.0,
+                    help="before the warmup steps, run untimed steps for this long so the "
+                         "GPU leaves its idle clocks (a step is ~0.15 ms; without this the "
+                         "first tens of milliseconds of steps run up to 10%% slower)")
+    ap.add_argument("--event-every", type=int, default=10,
+                    help="bracket the attention call of every N-th timed step with HIP events "
+                         "(each event record adds a few microseconds of idle GPU time to its step)")
     ap.add_argument("--kv-copies", type=int, default=2,
                     help="K/V page copies, used by consecutive steps in turn")
     ap.add_argument("--workload", default="llama3_8b_tree64")
@@ -153,6 +165,17 @@ def _counter_means(path, counter):
     return {k: sum(v) / len(v) for k, v in acc.items()}
 
 
+def _calibration_kib(path, counter):
+    """Mean counter value of the calibration copies: the last three copy
+    dispatches of the run (bench.py issues them after everything else; the
+    K/V page copies made at set-up launch the same kernel with the same grid)."""
+    import csv
+    vals = [(int(r["Dispatch_Id"]), float(r["Counter_Value"])) for r in csv.DictReader(open(path))
+            if r["Counter_Name"] == counter and "copyBuffer" in r["Kernel_Name"]]
+    last = [v for _, v in sorted(vals)[-3:]]
+    return sum(last) / len(last)
+
+
 def write_traffic(workload, fetch_csv, write_csv, copy_mib):
     """HBM bytes per attention call: FETCH_SIZE and WRITE_SIZE of the attention
     kernels (KiB per dispatch), each scaled by the ratio of the known size of
@@ -163,8 +186,7 @@ def write_traffic(workload, fetch_csv, write_csv, copy_mib):
     total = 0.0
     for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         means = _counter_means(path, counter)
-        copies = [v for (n, _), v in means.items() if "copyBuffer" in n]
-        cal = max(copies)          # the largest copy is the calibration copy
+        cal = _calibration_kib(path, counter)
         scale = copy_bytes / (cal * 1024.0)
         attn = {n: v for (n, _), v in means.items()
                 if "attn_mfma_kernel" in n or "attn_combine_kernel" in n}
@@ -375,17 +397,25 @@ def main():
     torch.cuda.set_device(0)
     w = Workload(args.workload, max(1, args.kv_copies))
     cfg = w.cfg
+    settle_steps = 0
+    t_end = time.perf_counter() + args.settle_ms * 1e-3
+    while time.perf_counter() < t_end:
+        for _ in range(10):
+            w.step()
+        settle_steps += 10
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         w.step()
     torch.cuda.synchronize()
-    evs = [(HipEvent(), HipEvent()) for _ in range(args.steps)]
+    every = max(1, args.event_every)
+    evs = {k: (HipEvent(), HipEvent()) for k in range(0, args.steps, every)}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
-        w.step(evs[k])
+        w.step(evs.get(k))
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    attn_s = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e-3
+    attn_s = float(np.mean([a.elapsed_time(b) for a, b in evs.values()])) * 1e-3
     step_s = (t1 - t0) / args.steps
     status = w.tva.device_status()
     assert status == 0, "device status bits set: %#x" % status
@@ -417,6 +447,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_steps": settle_steps,
         "ms_per_step": round(step_s * 1e3, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -428,7 +459,8 @@ def main():
                    "accept": cfg.mode, "temperature": w.tau, "topk": cfg.topk or None,
                    "kv_copies": len(w.kvs)},
         "roofline": dict(roof, kernel="sd_tree_verify_attn (tree-masked attention kernel)",
-                         attention_us=round(attn_s * 1e6, 2), bytes_per_call=int(bytes_),
+                         attention_us=round(attn_s * 1e6, 2), timed_calls=len(evs),
+                         bytes_per_call=int(bytes_),
                          flops_per_call=int(flops)),
         "cpu_baseline": cpu,
         "accepted_tokens_per_s": round(float(plen.sum()) / step_s, 1),

@@ -8,7 +8,7 @@
 //
 // Kernels:
 //   anc_mask_kernel     ancestor bitmask per node, anc(i) = anc(parent(i)) | bit(i)
-//   attn_valu_kernel    one wavefront per query row, float32 math (fp32 inputs)
+//   attn_valu_kernel    one workgroup per query row, float32 math (fp32 inputs)
 //   attn_mfma_kernel    bf16 MFMA flash-style kernel: K / V^T tiles staged in LDS
 //                       and shared by every query row of a KV group, online
 //                       softmax in registers, split context with partials
