@@ -606,10 +606,49 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
         stop = true;
       }
     } else {
-      // statistics of this slice in one pass: running max and the mass
-      // relative to it, merged across lanes and waves
+      // statistics of this slice: its max and the mass relative to it,
+      // merged across lanes and waves (in lane 63 of each wave)
       float mt = -INFINITY;
       double st = 0.0;
+      if constexpr (CACHED) {
+        // The slice is in registers: the wave's max first (a float
+        // reduction), then every weight relative to it at once, so no step
+        // of the sum waits on a rescale.
+        float v[kMaxCh][8];
+        float cm[kMaxCh];
+#pragma unroll
+        for (int c = 0; c < kMaxCh; ++c) {
+          if (c < NC) {
+            logits8(c, v[c]);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[c][e] = -INFINITY;
+          }
+          cm[c] = fmaxf(fmaxf(fmaxf(v[c][0], v[c][1]), fmaxf(v[c][2], v[c][3])),
+                        fmaxf(fmaxf(v[c][4], v[c][5]), fmaxf(v[c][6], v[c][7])));
+        }
+        float lm = cm[0];
+#pragma unroll
+        for (int c = 1; c < kMaxCh; ++c) lm = fmaxf(lm, cm[c]);
+        auto mvf = [](auto c, auto r, float old, float x) { return dpp_f<decltype(c)::value, decltype(r)::value>(old, x); };
+        lm = dpp_reduce<true>(lm, -INFINITY, mvf, [](float x, float y) { return fmaxf(x, y); });
+        mt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lm), 63));   // (the reduction ends in lane 63)
+        double ls = 0.0;
+        if (mt > -INFINITY) {
+          double cs[kMaxCh];
+#pragma unroll
+          for (int c = 0; c < kMaxCh; ++c) {
+            double w[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) w[e] = (double)__builtin_amdgcn_exp2f((v[c][e] - mt) * c2);
+            cs[c] = ((w[0] + w[1]) + (w[2] + w[3])) + ((w[4] + w[5]) + (w[6] + w[7]));
+          }
+          ls = cs[0];
+#pragma unroll
+          for (int c = 1; c < kMaxCh; ++c) ls += cs[c];
+        }
+        st = wave_sum_d(ls);
+      } else {
       FOR_CHUNKS(c,
         float v[8];
         logits8(c, v);
@@ -641,6 +680,7 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
         const MS t = dpp_reduce<true>(MS{mt, st}, MS{-INFINITY, 0.0}, mv, comb);
         mt = t.m;
         st = t.s;
+      }
       }
       lds_sync();
       if (lane == 63) {

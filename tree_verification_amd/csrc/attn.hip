@@ -817,8 +817,18 @@ __global__ void __launch_bounds__(WQ * WK * 64) attn_mfma_kernel(AttnArgs a) {
   PTile pf;
   if (nuse > 0) {
     // K(0) has landed once at most the (S - 1) * OPS operations issued after
-    // it (V(0), tiles 1 .. S - 2, K(S - 1)) are outstanding.
-    sync_tiles(false);
+    // it (V(0), tiles 1 .. S - 2, K(S - 1)) are outstanding; with fewer than S
+    // usable tiles that count is not exact and everything is drained.  (A V^T
+    // tile assembled from plain loads waits for them, and with them for every
+    // operation before it, so the count stays a safe bound.)  Only K(0) is
+    // waited for: the rest of the first tiles land while tile 0's scores are
+    // formed.
+    if (nuse >= S) __builtin_amdgcn_s_waitcnt(vmcnt_imm((S - 1) * OPS));
+    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    __builtin_amdgcn_s_waitcnt(lgkmcnt_imm(0));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
     qk(0, sa);
   }
   // Whole tiles: dense context tiles inside ctx; sparse tiles made only of
