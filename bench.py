@@ -7,8 +7,9 @@ One step is one verification pass over one batch: tree-masked attention
 (sd_tree_verify_attn, which also builds the ancestor masks), the acceptance
 walk (sd_accept) and the commit of the accepted paths (sd_kv_commit); the
 sparse workload first selects blocks (sd_topk_blocks) and attends sparsely.
-The context lengths are restored after each commit (a 4-byte-per-sequence
-device copy inside the step) so every step does the same work.  The K/V
+Each timed step gets its own copy of the starting context lengths, made
+before the timed region, so every step does the same work and no restore
+copy runs between steps (the untimed steps restore them instead).  The K/V
 pages are held in several copies (--kv-copies, default 2) and consecutive
 steps use different ones, so a step cannot find the previous step's K/V in
 the 256 MB last-level cache.
@@ -279,25 +280,32 @@ class Workload:
         if cfg.topk:
             self.sel = torch.empty((B, T, cfg.Hq, cfg.topk), dtype=torch.int32, device="cuda")
 
-    def attention(self):
-        self.tva.tree_verify_attn(self.q, self.k, self.v, self.table, self.ctx, self.parent,
-                                  out=self.out, sel_blocks=self.sel)
+    def attention(self, ctx=None):
+        self.tva.tree_verify_attn(self.q, self.k, self.v, self.table, self.ctx if ctx is None else ctx,
+                                  self.parent, out=self.out, sel_blocks=self.sel)
 
-    def step(self, ev=None):
+    def step(self, ev=None, ctx=None):
+        """One pass.  With `ctx` (a fresh copy of the context lengths, which
+        the commit advances) nothing is restored afterwards; without it the
+        step runs on the workload's own lengths and restores them."""
         tva = self.tva
+        restore = ctx is None
+        if restore:
+            ctx = self.ctx
         self.k, self.v = self.kvs[self.n_steps % len(self.kvs)]
         self.n_steps += 1
         if self.sel is not None:
-            tva.topk_blocks(self.q, self.k, self.table, self.ctx, self.cfg.topk, sel=self.sel)
+            tva.topk_blocks(self.q, self.k, self.table, ctx, self.cfg.topk, sel=self.sel)
         if ev is not None:
             ev[0].record()
-        self.attention()
+        self.attention(ctx)
         if ev is not None:
             ev[1].record()
         tva.accept(self.logits, self.draft, self.parent, self.token, self.unif, self.tau,
                    path=self.path, path_len=self.plen, bonus=self.bonus)
-        tva.kv_commit(self.k, self.v, self.table, self.ctx, self.path, self.plen)
-        self.ctx.copy_(self.ctx0)
+        tva.kv_commit(self.k, self.v, self.table, ctx, self.path, self.plen)
+        if restore:
+            ctx.copy_(self.ctx0)
 
 
 def time_calls(w, reps=10):
@@ -409,10 +417,13 @@ def main():
     torch.cuda.synchronize()
     every = max(1, args.event_every)
     evs = {k: (HipEvent(), HipEvent()) for k in range(0, args.steps, every)}
+    # each timed step gets its own copy of the context lengths (its commit
+    # advances them), so no restore runs inside the timed region
+    ctxs = [w.ctx0.clone() for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
-        w.step(evs.get(k))
+        w.step(evs.get(k), ctxs[k])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     attn_s = float(np.mean([a.elapsed_time(b) for a, b in evs.values()])) * 1e-3
