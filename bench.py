@@ -4,9 +4,11 @@
                     [--workload llama3_8b_tree64]
 
 One step is one verification pass over one batch: tree-masked attention
-(sd_tree_verify_attn, which also builds the ancestor masks), the acceptance
-walk (sd_accept) and the commit of the accepted paths (sd_kv_commit); the
-sparse workload first selects blocks (sd_topk_blocks) and attends sparsely.
+(sd_tree_verify_attn, which also builds the ancestor masks), then the
+acceptance walk and the commit of the accepted paths in one launch
+(sd_accept_commit, which gives the results of sd_accept then sd_kv_commit);
+the sparse workload first selects blocks (sd_topk_blocks) and attends
+sparsely.
 Each timed step gets its own copy of the starting context lengths, made
 before the timed region, so every step does the same work and no restore
 copy runs between steps (the untimed steps restore them instead).  The K/V
@@ -301,9 +303,10 @@ class Workload:
         self.attention(ctx)
         if ev is not None:
             ev[1].record()
-        tva.accept(self.logits, self.draft, self.parent, self.token, self.unif, self.tau,
-                   path=self.path, path_len=self.plen, bonus=self.bonus)
-        tva.kv_commit(self.k, self.v, self.table, ctx, self.path, self.plen)
+        # the acceptance walk and the commit of its paths, in one launch
+        tva.accept_commit(self.logits, self.draft, self.parent, self.token, self.unif, self.tau,
+                          self.k, self.v, self.table, ctx,
+                          path=self.path, path_len=self.plen, bonus=self.bonus)
         if restore:
             ctx.copy_(self.ctx0)
 
@@ -332,6 +335,12 @@ def time_calls(w, reps=10):
         tva.kv_commit(w.k, w.v, w.table, w.ctx, w.path, w.plen)
         w.ctx.copy_(w.ctx0)
     res["commit_plus_restore_us"] = loop(commit)
+
+    def accept_commit():
+        tva.accept_commit(w.logits, w.draft, w.parent, w.token, w.unif, w.tau, w.k, w.v, w.table, w.ctx,
+                          path=w.path, path_len=w.plen, bonus=w.bonus)
+        w.ctx.copy_(w.ctx0)
+    res["accept_commit_plus_restore_us"] = loop(accept_commit)
     if w.sel is not None:
         res["topk_us"] = loop(lambda: tva.topk_blocks(w.q, w.k, w.table, w.ctx, w.cfg.topk, sel=w.sel))
     return {k: round(v, 1) for k, v in res.items()}

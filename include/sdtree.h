@@ -10,6 +10,7 @@
  *   sd_accept            the acceptance walk (greedy, rejection sampling, or
  *                        sampling from the target at each node);
  *   sd_kv_commit         the accepted root path becomes committed context;
+ *   sd_accept_commit     sd_accept then sd_kv_commit, in one launch;
  *   sd_topk_blocks       top-k KV blocks per query for sparse verification.
  *
  * Conventions shared by every call
@@ -155,6 +156,27 @@ sd_status sd_accept(const sd_accept_shape* shape, const void* target_logits,
 sd_status sd_kv_commit(const sd_shape* shape, void* k_pages, void* v_pages,
                        const int32_t* block_table, int32_t* ctx_lens, const int32_t* path,
                        const int32_t* path_len, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * sd_accept followed by sd_kv_commit of the accepted paths, in one launch:
+ * the acceptance kernel commits each sequence's path once its walk has ended,
+ * so the path never leaves the device between the two steps.  Results are
+ * those of the two calls in sequence: path, path_len and bonus as sd_accept;
+ * k_pages, v_pages and ctx_lens as sd_kv_commit given that path.  Arguments
+ * are those of the two calls; `kv_shape` describes the paged cache and is
+ * checked as for sd_kv_commit, and its B and T must equal `shape`'s.  Data
+ * errors of either half set their sticky bits in `ws`
+ * (>= sd_workspace_bytes(SD_CALL_ACCEPT, shape, 0)); a sequence whose tree
+ * fails validation gets path_len 0 and commits nothing, and one whose slots
+ * [ctx, ctx + T) fail the commit's checks keeps its cache and length.
+ */
+sd_status sd_accept_commit(const sd_accept_shape* shape, const sd_shape* kv_shape,
+                           const void* target_logits, const float* draft_probs,
+                           const int32_t* tree_parent, const int32_t* tree_token,
+                           const float* uniforms, float temperature, int32_t* path,
+                           int32_t* path_len, int32_t* bonus, void* k_pages, void* v_pages,
+                           const int32_t* block_table, int32_t* ctx_lens, void* ws,
+                           size_t ws_bytes, void* stream);
 
 /*
  * Top-k context blocks per query (sparse-verification page, "Methodology":

@@ -17,7 +17,7 @@ def setup_module():
 
 def test_exports_every_declared_function():
     names = _lib.declared_functions()
-    assert len(names) == 7
+    assert len(names) == 8
     for n in names:
         assert hasattr(L, n), n
 
@@ -95,6 +95,23 @@ def test_accept_rejects_bad_arguments():
     assert call(ok, tau=float("nan")) == 1
     assert call(ok, unif=None) == 1
     assert call(ok, ws=100) == 5
+
+
+def test_accept_commit_rejects_bad_arguments():
+    def call(shape, kv, tau=0.8, kpages=FAKE, ws=256):
+        return L.sd_accept_commit(ctypes.byref(shape), None if kv is None else ctypes.byref(kv), FAKE,
+                                  FAKE, FAKE, FAKE, FAKE, tau, FAKE, FAKE, FAKE, kpages, FAKE, FAKE,
+                                  FAKE, FAKE, ws, None)
+    ok = _lib.SdAcceptShape(2, 8, 100, 1, 8)
+    kv = _shape(B=2, T=8, Hq=8, tree_stride=8)
+    assert call(ok, None) == 1                        # no cache shape
+    assert call(ok, _shape(B=3, T=8, Hq=8, tree_stride=8)) == 2      # B differs
+    assert call(ok, _shape(B=2, T=9, Hq=8, tree_stride=9)) == 2      # T differs
+    assert call(ok, _shape(B=2, T=8, Hq=8, tree_stride=8, D=96)) == 4
+    assert call(ok, kv, kpages=None) == 1
+    assert call(_lib.SdAcceptShape(2, 8, 100, 5, 8), kv) == 3
+    assert call(ok, kv, tau=-1.0) == 1
+    assert call(ok, kv, ws=100) == 5
 
 
 def test_commit_and_topk_reject_bad_arguments():

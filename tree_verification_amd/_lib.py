@@ -64,6 +64,8 @@ def lib():
         "sd_accept": [ctypes.POINTER(SdAcceptShape), _P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P,
                       _P, sz, _P],
         "sd_kv_commit": [ctypes.POINTER(SdShape), _P, _P, _P, _P, _P, _P, _P, sz, _P],
+        "sd_accept_commit": [ctypes.POINTER(SdAcceptShape), ctypes.POINTER(SdShape), _P, _P, _P, _P, _P,
+                             ctypes.c_float, _P, _P, _P, _P, _P, _P, _P, _P, sz, _P],
         "sd_topk_blocks": [ctypes.POINTER(SdShape), _P, _P, _P, _P, i32, _P, _P, sz, _P],
         "sd_device_status": [_P, _P, ctypes.POINTER(ctypes.c_uint32)],
         "sd_workspace_bytes": [i32, _P, i32],
@@ -179,6 +181,33 @@ def accept(target_logits, draft_probs, tree_parent, tree_token, uniforms, temper
         ctypes.byref(shape), _ptr(target_logits), _ptr(draft_probs), _ptr(tree_parent),
         _ptr(tree_token), _ptr(uniforms), float(temperature), _ptr(path), _ptr(path_len),
         _ptr(bonus), _ptr(ws), ws.numel(), _stream(dev)))
+    return path, path_len, bonus
+
+
+def accept_commit(target_logits, draft_probs, tree_parent, tree_token, uniforms, temperature,
+                  k_pages, v_pages, block_table, ctx_lens, path=None, path_len=None, bonus=None,
+                  ws=None):
+    """accept(...) then kv_commit(...) of its paths, in one launch (sd_accept_commit)."""
+    B, T, V = target_logits.shape
+    shape = SdAcceptShape(B, T, V, _dtype_code[target_logits.dtype],
+                          0 if tree_parent.shape[0] == 1 else T)
+    nb, Hkv, bs, D = k_pages.shape
+    kv_shape = SdShape(B, T, Hkv, Hkv, D, bs, block_table.shape[1], nb, _dtype_code[k_pages.dtype],
+                       T, 0.0)
+    dev = target_logits.device
+    if path is None:
+        path = torch.empty((B, T), dtype=torch.int32, device=dev)
+    if path_len is None:
+        path_len = torch.empty(B, dtype=torch.int32, device=dev)
+    if bonus is None:
+        bonus = torch.empty(B, dtype=torch.int32, device=dev)
+    need = workspace_bytes(SD_CALL_ACCEPT, shape)
+    ws = _WS.get(dev, need, SD_CALL_ACCEPT) if ws is None else ws
+    _check("sd_accept_commit", lib().sd_accept_commit(
+        ctypes.byref(shape), ctypes.byref(kv_shape), _ptr(target_logits), _ptr(draft_probs),
+        _ptr(tree_parent), _ptr(tree_token), _ptr(uniforms), float(temperature), _ptr(path),
+        _ptr(path_len), _ptr(bonus), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(ctx_lens),
+        _ptr(ws), ws.numel(), _stream(dev)))
     return path, path_len, bonus
 
 

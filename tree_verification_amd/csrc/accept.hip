@@ -39,6 +39,9 @@ constexpr int kMaxT = kMaxTreeNodes;
 constexpr int kMaxRej = 64;
 constexpr int kMaxP = 16;             // (the slice butterflies span 16 lanes)
 constexpr int kMaxKid = 64;          // children whose test scalars are prefetched
+constexpr int kCKRegs = 4;           // commit: 16-byte K chunks per thread per group
+constexpr int kCVRegs = 24;          // commit: V^T elements per thread per group
+constexpr int kMaxCBlk = kMaxT / 8 + 2;  // commit: blocks of the tree slots (bs >= 8)
 constexpr unsigned kSpinLimit = 1u << 20;
 
 // Workgroup barrier for data exchanged through LDS.  __syncthreads() would
@@ -187,6 +190,27 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
   unsigned long long* slots = reinterpret_cast<unsigned long long*>(a.sync + (size_t)b * kAccSeqBytes);
   unsigned* done = reinterpret_cast<unsigned*>(slots + 2 * kMaxP * 2);
 
+  // With a commit: the context length, and the block ids of the tree slots
+  // [ctx, ctx + T) staged and validated now, alongside the tree (the commit
+  // runs after the walk; see below).
+  const bool commit = a.cctx != nullptr;
+  const int c_ctx = commit ? a.cctx[b] : 0;
+  __shared__ int s_cblk[kMaxCBlk];
+  __shared__ int s_cerr;
+  uint32_t cbad = 0;
+  if (commit) {
+    if (c_ctx < 0 || (long long)c_ctx + T > (long long)a.cmax_blocks * a.cbs) {
+      cbad = SD_ERR_CAPACITY;
+    } else {
+      const int lo = c_ctx / a.cbs, nblk = (c_ctx + T - 1) / a.cbs - lo + 1;
+      const int32_t* ctable = a.ctable + (size_t)b * a.cmax_blocks + lo;
+      for (int n = tid; n < nblk; n += kAT) {
+        const int blk = ctable[n];
+        if (blk < 0 || blk >= a.cnum_blocks) cbad |= SD_ERR_BLOCK;
+        s_cblk[n] = blk;
+      }
+    }
+  }
   // The tree (kept in LDS) must be topologically ordered with valid tokens.
   int bad = 0;
   for (int n = tid; n < T; n += kAT) {
@@ -200,15 +224,92 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
   if (tid == 0) {
     s_flag = 0;
     s_to = 0;
+    s_cerr = 0;
   }
   lds_sync();
   if (bad) atomicOr(&s_flag, bad);
+  if (cbad) atomicOr(&s_cerr, (int)cbad);
   lds_sync();
+  const uint32_t cerr = (uint32_t)s_cerr;
   if (wg == 0)
     for (int n = tid; n < T; n += kAT) path[n] = -1;
+  // ---- commit of the accepted path (when asked for) --------------------------
+  // As a commit after the walk: positions ctx + j take the K/V of ctx + path[j]
+  // for j < plen, every KV head, then ctx grows by plen.  Validation as the
+  // commit (done above): the slots [ctx, ctx + T) must fit the table and their
+  // blocks be valid, else the sequence is left untouched and a sticky bit is
+  // set.
+  // Copies the path's entries of this workgroup's KV heads (g = wg, wg + P,
+  // ...) in groups: every thread loads its share of a group (16-byte K chunks,
+  // V^T elements), the workgroup waits for all of them, then stores.  Since
+  // path[j] >= j and the path increases, a group's destinations never overlap
+  // a later group's sources, so the copy is safe in place.  kids[] holds the
+  // path and s_cblk[] the block ids of slots [ctx, ctx + T).
+  auto commit_copy = [&](int L) {
+    const int D = a.cD, esize = a.cesize, bs = a.cbs, lo = c_ctx / bs;
+    const int rowb = D * esize;
+    const int kch = rowb / 16;                      // 16-byte chunks per K row
+    const int kstep = kAT / kch, vstep = kAT / D;
+    const int kcol = tid % kch, ku0 = tid / kch;
+    const int vcol = tid % D, vu0 = tid / D;
+    const int JG = min(kCKRegs * kstep, kCVRegs * vstep);
+    const long long blk_bytes = (long long)a.cHkv * bs * rowb;
+    unsigned char* K = static_cast<unsigned char*>(a.ck);
+    unsigned char* Vb = static_cast<unsigned char*>(a.cv);
+    const long long kc_off = (long long)kcol * 16;
+    const long long vc_off = (long long)vcol * bs * esize;
+    for (int g = wg; g < a.cHkv; g += P) {
+      const long long head_k = (long long)g * bs * rowb;
+      const long long head_v = (long long)g * D * bs * esize;
+      auto k_at = [&](int pos) {
+        return (long long)s_cblk[pos / bs - lo] * blk_bytes + head_k + (long long)(pos % bs) * rowb;
+      };
+      auto v_at = [&](int pos) {
+        return (long long)s_cblk[pos / bs - lo] * blk_bytes + head_v + (long long)(pos % bs) * esize;
+      };
+      for (int j0 = 0; j0 < L; j0 += JG) {
+        const int nj = min(JG, L - j0);
+        uint4 kr[kCKRegs];
+        uint32_t vr[kCVRegs];
+#pragma unroll
+        for (int r = 0; r < kCKRegs; ++r) {
+          const int jj = ku0 + r * kstep;
+          kr[r] = make_uint4(0, 0, 0, 0);
+          if (jj < nj && kids[j0 + jj] != j0 + jj)
+            kr[r] = *reinterpret_cast<const uint4*>(K + k_at(c_ctx + kids[j0 + jj]) + kc_off);
+        }
+#pragma unroll
+        for (int r = 0; r < kCVRegs; ++r) {
+          const int jj = vu0 + r * vstep;
+          vr[r] = 0;
+          if (jj < nj && kids[j0 + jj] != j0 + jj) {
+            const unsigned char* src = Vb + v_at(c_ctx + kids[j0 + jj]) + vc_off;
+            vr[r] = esize == 2 ? *reinterpret_cast<const uint16_t*>(src) : *reinterpret_cast<const uint32_t*>(src);
+          }
+        }
+        __syncthreads();   // every load of the group has landed before any store
+#pragma unroll
+        for (int r = 0; r < kCKRegs; ++r) {
+          const int jj = ku0 + r * kstep;
+          if (jj < nj && kids[j0 + jj] != j0 + jj)
+            *reinterpret_cast<uint4*>(K + k_at(c_ctx + j0 + jj) + kc_off) = kr[r];
+        }
+#pragma unroll
+        for (int r = 0; r < kCVRegs; ++r) {
+          const int jj = vu0 + r * vstep;
+          if (jj < nj && kids[j0 + jj] != j0 + jj) {
+            unsigned char* dst = Vb + v_at(c_ctx + j0 + jj) + vc_off;
+            if (esize == 2) *reinterpret_cast<uint16_t*>(dst) = (uint16_t)vr[r];
+            else *reinterpret_cast<uint32_t*>(dst) = vr[r];
+          }
+        }
+        __syncthreads();
+      }
+    }
+  };
   if (s_flag) {
     if (wg == 0 && tid == 0) {
-      set_status(a.status, (uint32_t)s_flag);
+      set_status(a.status, (uint32_t)s_flag | cerr);
       a.path_len[b] = 0;
       a.bonus[b] = -1;
     }
@@ -903,17 +1004,40 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
     lds_sync();
   }
   if (wg == 0 && tid == 0) a.path_len[b] = plen;
+  if (commit) {
+    if (cerr) {
+      if (wg == 0 && tid == 0) set_status(a.status, cerr);
+    } else {
+      // the path, rebuilt from its last node through the parents, in kids[]
+      lds_sync();
+      if (tid == 0) {
+        int n = cur;
+        for (int j = plen - 1; j >= 0; --j) {
+          kids[j] = n;
+          n = s_par[n];
+        }
+      }
+      lds_sync();
+      commit_copy(plen);
+    }
+  }
   if (P > 1) {
     // the last workgroup of the sequence to leave clears the slots, so the
-    // next call starts from barrier number 1 again
+    // next call starts from barrier number 1 again; with a commit it also
+    // writes the new context length (every workgroup read the old one first)
     lds_sync();
     if (tid == 0) s_flag = atomicAdd(done, 1u) == (unsigned)P - 1;
     lds_sync();
     if (s_flag) {
       for (int j = tid; j < 2 * kMaxP * 2; j += kAT)
         __hip_atomic_store(slots + j, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (tid == 0) __hip_atomic_store(done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (tid == 0) {
+        if (commit && !cerr) a.cctx[b] = c_ctx + plen;
+        __hip_atomic_store(done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
+  } else if (commit && !cerr && tid == 0) {
+    a.cctx[b] = c_ctx + plen;
   }
   if (tid == 0 && s_to) set_status(a.status, SD_ERR_TIMEOUT);
 }

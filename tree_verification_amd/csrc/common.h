@@ -119,6 +119,12 @@ struct AcceptArgs {
   uint32_t* status;
   unsigned char* sync;  // B * kAccSeqBytes, zero before the first call (P > 1 only)
   int P, SL, NC;        // workgroups per sequence, tokens per workgroup, 2048-token chunks
+  // commit of the accepted paths in the same launch (cctx == nullptr: none)
+  void* ck;
+  void* cv;
+  const int32_t* ctable;
+  int32_t* cctx;
+  int cHkv, cD, cbs, cmax_blocks, cnum_blocks, cesize;
 };
 
 int accept_wgs(int B, int V);

@@ -251,11 +251,13 @@ sd_status sd_tree_verify_attn(const sd_shape* shape, const void* q, const void* 
   return hip_status(launch_attn_mfma(a, p, hs));
 }
 
-sd_status sd_accept(const sd_accept_shape* shape, const void* target_logits,
-                    const float* draft_probs, const int32_t* tree_parent,
-                    const int32_t* tree_token, const float* uniforms, float temperature,
-                    int32_t* path, int32_t* path_len, int32_t* bonus, void* ws, size_t ws_bytes,
-                    void* stream) {
+// Checks the arguments of an acceptance call and fills its kernel arguments
+// (no commit).
+static sd_status accept_args(const sd_accept_shape* shape, const void* target_logits,
+                             const float* draft_probs, const int32_t* tree_parent,
+                             const int32_t* tree_token, const float* uniforms, float temperature,
+                             int32_t* path, int32_t* path_len, int32_t* bonus, void* ws,
+                             size_t ws_bytes, AcceptArgs* out) {
   if (!shape) return SD_INVALID_ARG;
   const sd_accept_shape& s = *shape;
   if (s.B < 1 || s.T < 1 || s.V < 1) return SD_BAD_SHAPE;
@@ -280,6 +282,42 @@ sd_status sd_accept(const sd_accept_shape* shape, const void* target_logits,
   a.P = accept_wgs(s.B, s.V);
   a.SL = (((s.V + a.P - 1) / a.P) + 7) / 8 * 8;
   a.NC = (a.SL + 2047) / 2048;
+  *out = a;
+  return SD_OK;
+}
+
+sd_status sd_accept(const sd_accept_shape* shape, const void* target_logits,
+                    const float* draft_probs, const int32_t* tree_parent,
+                    const int32_t* tree_token, const float* uniforms, float temperature,
+                    int32_t* path, int32_t* path_len, int32_t* bonus, void* ws, size_t ws_bytes,
+                    void* stream) {
+  AcceptArgs a;
+  const sd_status st = accept_args(shape, target_logits, draft_probs, tree_parent, tree_token,
+                                   uniforms, temperature, path, path_len, bonus, ws, ws_bytes, &a);
+  if (st != SD_OK) return st;
+  return hip_status(launch_accept(a, static_cast<hipStream_t>(stream)));
+}
+
+sd_status sd_accept_commit(const sd_accept_shape* shape, const sd_shape* kv_shape,
+                           const void* target_logits, const float* draft_probs,
+                           const int32_t* tree_parent, const int32_t* tree_token,
+                           const float* uniforms, float temperature, int32_t* path,
+                           int32_t* path_len, int32_t* bonus, void* k_pages, void* v_pages,
+                           const int32_t* block_table, int32_t* ctx_lens, void* ws,
+                           size_t ws_bytes, void* stream) {
+  if (!shape || !kv_shape) return SD_INVALID_ARG;
+  sd_status st = check_shape(kv_shape);
+  if (st != SD_OK) return st;
+  if (kv_shape->B != shape->B || kv_shape->T != shape->T) return SD_BAD_SHAPE;
+  if (!k_pages || !v_pages || !block_table || !ctx_lens) return SD_INVALID_ARG;
+  AcceptArgs a;
+  st = accept_args(shape, target_logits, draft_probs, tree_parent, tree_token, uniforms,
+                   temperature, path, path_len, bonus, ws, ws_bytes, &a);
+  if (st != SD_OK) return st;
+  a.ck = k_pages; a.cv = v_pages; a.ctable = block_table; a.cctx = ctx_lens;
+  a.cHkv = kv_shape->Hkv; a.cD = kv_shape->D; a.cbs = kv_shape->bs;
+  a.cmax_blocks = kv_shape->max_blocks; a.cnum_blocks = kv_shape->num_blocks;
+  a.cesize = kv_shape->dtype == SD_F32 ? 4 : 2;
   return hip_status(launch_accept(a, static_cast<hipStream_t>(stream)));
 }
 
