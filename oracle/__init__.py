@@ -30,5 +30,6 @@ from .tree import ancestor_matrix, children_of, root_path  # noqa: F401
 from .attention import attention_dense, attention_by_path  # noqa: F401
 from .accept import accept, invcdf  # noqa: F401
 from .commit import commit  # noqa: F401
-from .topk import block_means, block_scores, topk_blocks  # noqa: F401
+from .topk import (append_block_sums, block_means, block_scores, block_sums,  # noqa: F401
+                   means_from_sums, topk_blocks)
 from .codec import decode  # noqa: F401

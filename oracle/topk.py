@@ -15,10 +15,71 @@ Because the indices must match exactly, the float32 arithmetic is fixed:
           add element d + D/2 into d, then d + D/4, ..., then d + 1;
 * order = score descending, then block index ascending; keep the first k,
           emit them in ascending block order, pad with -1.
+
+Cached block sums (the selection read from per-block summaries kept as the
+context grows): `block_sums` is the numerator of the mean above, per
+physical block, and `append_block_sums` extends it by the positions a
+commit appended, continuing the same sequential sum; a mean formed from the
+kept sums is therefore the same float32 value as one formed from K.
 """
 import numpy as np
 
 from .codec import decode_f32
+
+
+def _block_sum(k_pages, blk, t0, t1, dtype, start=None):
+    """Sequential float32 sum of K rows t0 <= t < t1 of physical block blk
+    (all heads), continuing from `start` (else from +0)."""
+    Hkv, D = k_pages.shape[1], k_pages.shape[3]
+    s = np.zeros((Hkv, D), dtype=np.float32) if start is None else np.array(start, dtype=np.float32)
+    for t in range(t0, t1):
+        s = s + decode_f32(k_pages[blk, :, t, :], dtype)
+    return s
+
+
+def block_sums(k_pages, block_table, ctx_lens, bs, dtype):
+    """float32 [num_blocks, Hkv, D]: for every context block n < ceil(ctx_b / bs)
+    of every sequence, the sequential sum of its valid K rows at its physical
+    block; NaN for blocks no sequence holds as context."""
+    nb_phys, Hkv, _, D = k_pages.shape
+    out = np.full((nb_phys, Hkv, D), np.nan, dtype=np.float32)
+    for b in range(len(ctx_lens)):
+        ctx = int(ctx_lens[b])
+        for n in range((ctx + bs - 1) // bs):
+            blk = int(block_table[b, n])
+            out[blk] = _block_sum(k_pages, blk, 0, min(bs, ctx - n * bs), dtype)
+    return out
+
+
+def append_block_sums(sums, k_pages, block_table, ctx_new, n_new, bs, dtype):
+    """The sums after a commit appended n_new[b] positions ending at ctx_new[b]:
+    positions t in [ctx_new - n_new, ctx_new), in order, are added to their
+    block's sum; a block whose first position is among them starts from +0."""
+    out = np.array(sums, dtype=np.float32, copy=True)
+    for b in range(len(ctx_new)):
+        t = int(ctx_new[b]) - int(n_new[b])
+        while t < int(ctx_new[b]):
+            n, off = divmod(t, bs)
+            t1 = min((n + 1) * bs, int(ctx_new[b]))
+            blk = int(block_table[b, n])
+            out[blk] = _block_sum(k_pages, blk, off, off + (t1 - t), dtype,
+                                  start=None if off == 0 else out[blk])
+            t = t1
+    return out
+
+
+def means_from_sums(sums, block_table, ctx_lens, bs):
+    """float32 [B, nmax, Hkv, D] as block_means, from kept block sums."""
+    B = len(ctx_lens)
+    Hkv, D = sums.shape[1], sums.shape[2]
+    nb = [(int(c) + bs - 1) // bs for c in ctx_lens]
+    nmax = max(nb + [0])
+    out = np.full((B, nmax, Hkv, D), np.nan, dtype=np.float32)
+    for b in range(B):
+        ctx = int(ctx_lens[b])
+        for n in range(nb[b]):
+            out[b, n] = sums[int(block_table[b, n])] / np.float32(min(bs, ctx - n * bs))
+    return out
 
 
 def block_means(k_pages, block_table, ctx_lens, bs, dtype):

@@ -108,3 +108,63 @@ def test_planted_aligned_blocks_are_selected():
     sel = oracle.topk_blocks(qv[None, None, None], kp, table, np.array([nblk * bs], np.int32),
                              bs, 3, "f32")
     assert list(sel[0, 0, 0]) == planted
+
+
+def test_block_sums_exact_integers():
+    """Integer-valued keys: every float32 partial sum is exact, so each
+    block's sum equals the exact integer sum of its valid rows (closed form)."""
+    rng = np.random.default_rng(7)
+    bs = 4
+    q, kp, table, ctx, Kd = _int_case(rng, bs=bs)
+    sums = oracle.block_sums(kp, table, ctx, bs, "f32")
+    for b in range(2):
+        for n in range((ctx[b] + bs - 1) // bs):
+            lo, hi = n * bs, min(ctx[b], (n + 1) * bs)
+            want = Kd[b, :, lo:hi, :].astype(np.float64).sum(axis=1)
+            assert np.array_equal(sums[table[b, n]].astype(np.float64), want)
+    # blocks no sequence holds as context stay NaN
+    used = {int(table[b, n]) for b in range(2) for n in range((ctx[b] + bs - 1) // bs)}
+    for blk in range(kp.shape[0]):
+        if blk not in used:
+            assert np.isnan(sums[blk]).all()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_means_from_sums_equal_means(dtype):
+    """A mean formed from the kept sums is the very float32 value block_means
+    forms from K (same sequential sum, same single division)."""
+    rng = np.random.default_rng(11)
+    B, Hkv, D, bs = 3, 2, 8, 8
+    ctx = np.array([1, 17, 40], np.int32)
+    n = 48
+    Kd = rng.standard_normal((B, Hkv, n, D)).astype(np.float32)
+    if dtype == "bf16":
+        Kd = np.asarray(oracle.decode(f32_to_bf16_bits(Kd), "bf16"), np.float32)
+    kp, vp, table = paged_from_dense(Kd if dtype == "f32" else Kd, np.zeros_like(Kd), bs, rng)
+    if dtype == "bf16":
+        kp = f32_to_bf16_bits(kp)
+    sums = oracle.block_sums(kp, table, ctx, bs, dtype)
+    a = oracle.means_from_sums(sums, table, ctx, bs)
+    m = oracle.block_means(kp, table, ctx, bs, dtype)
+    assert np.array_equal(a.view(np.uint32), m.view(np.uint32))
+
+
+@pytest.mark.parametrize("ctx0,L", [(13, 5), (16, 8), (15, 1), (9, 0), (0, 3)])
+def test_append_block_sums_equals_rebuild(ctx0, L):
+    """Extending the sums by the positions a commit appended gives the sums
+    rebuilt from scratch at the new length, bit for bit: across a block
+    boundary, starting a new block, a single position, nothing, and an empty
+    context."""
+    rng = np.random.default_rng(ctx0 * 31 + L)
+    B, Hkv, D, bs = 2, 2, 8, 8
+    n = 40
+    Kd = rng.standard_normal((B, Hkv, n, D)).astype(np.float32)
+    kp, vp, table = paged_from_dense(Kd, np.zeros_like(Kd), bs, rng)
+    ctx = np.array([ctx0, ctx0 + 3], np.int32)
+    sums = oracle.block_sums(kp, table, ctx, bs, "f32")
+    plen = np.array([L, L], np.int32)
+    ctx_new = ctx + plen
+    got = oracle.append_block_sums(sums, kp, table, ctx_new, plen, bs, "f32")
+    want = oracle.block_sums(kp, table, ctx_new, bs, "f32")
+    live = ~np.isnan(want)
+    assert np.array_equal(got[live].view(np.uint32), want[live].view(np.uint32))
