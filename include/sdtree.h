@@ -11,7 +11,10 @@
  *                        sampling from the target at each node);
  *   sd_kv_commit         the accepted root path becomes committed context;
  *   sd_accept_commit     sd_accept then sd_kv_commit, in one launch;
- *   sd_topk_blocks       top-k KV blocks per query for sparse verification.
+ *   sd_topk_blocks       top-k KV blocks per query for sparse verification;
+ *   sd_block_sums, sd_block_sums_append, sd_topk_blocks_cached
+ *                        the same selection from per-block key sums kept as
+ *                        the context grows.
  *
  * Conventions shared by every call
  *   - Tensor arguments are DEVICE pointers owned by the caller.  The library
@@ -97,7 +100,7 @@ typedef struct sd_accept_shape {
   int32_t tree_stride;  /* 0 or T, as in sd_shape */
 } sd_accept_shape;
 
-enum { SD_CALL_ATTN = 1, SD_CALL_ACCEPT = 2, SD_CALL_TOPK = 3, SD_CALL_COMMIT = 4 };
+enum { SD_CALL_ATTN = 1, SD_CALL_ACCEPT = 2, SD_CALL_TOPK = 3, SD_CALL_COMMIT = 4, SD_CALL_BLOCK_SUMS = 5 };
 
 /*
  * Tree-masked grouped-query attention over the paged cache.
@@ -192,9 +195,45 @@ sd_status sd_topk_blocks(const sd_shape* shape, const void* q, const void* k_pag
                          const int32_t* block_table, const int32_t* ctx_lens, int32_t k,
                          int32_t* sel_blocks, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * Kept block key sums, so that top-k need not read K on every call (the
+ * sparse-verification page, "Methodology": the relevance score uses the
+ * mean-pooled key of each block; keeping the per-block sums as the context
+ * grows gives the same means without a scan of K).
+ *   block_sums  float32 [num_blocks, Hkv, D], indexed by PHYSICAL block; owned
+ *               by the caller.  A physical block shared by several sequences
+ *               must be a whole block in each.
+ * sd_block_sums: for every context block n < ceil(ctx_b / bs) of every
+ *   sequence, block_sums[block_table[b][n]][g][:] = the float32 sum of its valid
+ *   K rows, sequential in position order from +0.  Other entries are not
+ *   written.  ws >= sd_workspace_bytes(SD_CALL_BLOCK_SUMS, shape, 0).
+ * sd_block_sums_append: after a commit (ctx_lens already advanced), adds the
+ *   K rows of positions [ctx_b - n_new[b], ctx_b) to their blocks' sums in
+ *   position order; a block whose first position is among them starts from
+ *   +0.  With n_new = the commit's path_len, the sums stay equal to
+ *   sd_block_sums at the new lengths, bit for bit.  n_new[b] must lie in
+ *   [0, ctx_b]; a sequence with a bad count or a touched block out of range
+ *   is left unchanged and a sticky bit is set.
+ * sd_topk_blocks_cached: sd_topk_blocks with each mean formed as the kept sum
+ *   divided by the valid count (one IEEE division), so the selection is that
+ *   of sd_topk_blocks bit for bit while the sums are current.  K is not read.
+ *   ws >= sd_workspace_bytes(SD_CALL_TOPK, shape, k).
+ */
+sd_status sd_block_sums(const sd_shape* shape, const void* k_pages, const int32_t* block_table,
+                        const int32_t* ctx_lens, float* block_sums, void* ws, size_t ws_bytes,
+                        void* stream);
+sd_status sd_block_sums_append(const sd_shape* shape, const void* k_pages,
+                               const int32_t* block_table, const int32_t* ctx_lens,
+                               const int32_t* n_new, float* block_sums, void* ws, size_t ws_bytes,
+                               void* stream);
+sd_status sd_topk_blocks_cached(const sd_shape* shape, const void* q, const float* block_sums,
+                                const int32_t* block_table, const int32_t* ctx_lens, int32_t k,
+                                int32_t* sel_blocks, void* ws, size_t ws_bytes, void* stream);
+
 /* Workspace bytes a call needs; `shape` points to an sd_shape (ATTN, TOPK,
- * COMMIT) or an sd_accept_shape (ACCEPT); `extra` is k_sel (ATTN, 0 = dense) or
- * k (TOPK).  0 on bad input. */
+ * COMMIT, BLOCK_SUMS) or an sd_accept_shape (ACCEPT, also for
+ * sd_accept_commit); `extra` is k_sel (ATTN, 0 = dense) or k (TOPK).  0 on bad
+ * input. */
 size_t sd_workspace_bytes(int32_t call_id, const void* shape, int32_t extra);
 
 /* Synchronises `stream`, reads the sticky bits into *bits (may be NULL), clears

@@ -17,7 +17,7 @@ def setup_module():
 
 def test_exports_every_declared_function():
     names = _lib.declared_functions()
-    assert len(names) == 8
+    assert len(names) == 11
     for n in names:
         assert hasattr(L, n), n
 
@@ -112,6 +112,21 @@ def test_accept_commit_rejects_bad_arguments():
     assert call(_lib.SdAcceptShape(2, 8, 100, 5, 8), kv) == 3
     assert call(ok, kv, tau=-1.0) == 1
     assert call(ok, kv, ws=100) == 5
+
+
+def test_block_sums_calls_reject_bad_arguments():
+    s = _shape()
+    big = 1 << 40
+    assert L.sd_block_sums(ctypes.byref(_shape(Hq=7)), FAKE, FAKE, FAKE, FAKE, FAKE, big, None) == 2
+    assert L.sd_block_sums(ctypes.byref(s), FAKE, FAKE, FAKE, None, FAKE, big, None) == 1
+    assert L.sd_block_sums(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, 4, None) == 5
+    assert L.sd_block_sums_append(ctypes.byref(s), FAKE, FAKE, FAKE, None, FAKE, FAKE, big, None) == 1
+    assert L.sd_block_sums_append(ctypes.byref(_shape(D=96)), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, big,
+                                  None) == 4
+    assert L.sd_topk_blocks_cached(ctypes.byref(s), FAKE, None, FAKE, FAKE, 4, FAKE, FAKE, big, None) == 1
+    assert L.sd_topk_blocks_cached(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, 0, FAKE, FAKE, big, None) == 1
+    assert L.sd_topk_blocks_cached(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, 4, FAKE, FAKE, 10, None) == 5
+    assert L.sd_workspace_bytes(5, ctypes.byref(s), 0) > 0
 
 
 def test_commit_and_topk_reject_bad_arguments():

@@ -7,6 +7,6 @@ verification -- as hand-written HIP kernels behind a small C ABI
 (csrc/), the in-tree build (build.py) and a ctypes binding (_lib.py).
 """
 from ._lib import (  # noqa: F401
-    SdError, accept, accept_commit, device_status, kv_commit, lib, topk_blocks, tree_verify_attn,
-    workspace_bytes,
+    SdError, accept, accept_commit, block_sums, block_sums_append, device_status, kv_commit, lib,
+    topk_blocks, topk_blocks_cached, tree_verify_attn, workspace_bytes,
 )

@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(_HERE, "libsdtree.so")
 HEADER = os.path.join(os.path.dirname(_HERE), "include", "sdtree.h")
 
 SD_F32, SD_BF16 = 0, 1
-SD_CALL_ATTN, SD_CALL_ACCEPT, SD_CALL_TOPK, SD_CALL_COMMIT = 1, 2, 3, 4
+SD_CALL_ATTN, SD_CALL_ACCEPT, SD_CALL_TOPK, SD_CALL_COMMIT, SD_CALL_BLOCK_SUMS = 1, 2, 3, 4, 5
 STATUS = {0: "SD_OK", 1: "SD_INVALID_ARG", 2: "SD_BAD_SHAPE", 3: "SD_BAD_DTYPE",
           4: "SD_UNSUPPORTED", 5: "SD_CAPACITY", 6: "SD_HIP_ERROR", 7: "SD_DEVICE_DATA_ERROR"}
 ERR_BITS = {0x1: "parent", 0x2: "block", 0x4: "capacity", 0x8: "token", 0x10: "selection"}
@@ -67,6 +67,9 @@ def lib():
         "sd_accept_commit": [ctypes.POINTER(SdAcceptShape), ctypes.POINTER(SdShape), _P, _P, _P, _P, _P,
                              ctypes.c_float, _P, _P, _P, _P, _P, _P, _P, _P, sz, _P],
         "sd_topk_blocks": [ctypes.POINTER(SdShape), _P, _P, _P, _P, i32, _P, _P, sz, _P],
+        "sd_topk_blocks_cached": [ctypes.POINTER(SdShape), _P, _P, _P, _P, i32, _P, _P, sz, _P],
+        "sd_block_sums": [ctypes.POINTER(SdShape), _P, _P, _P, _P, _P, sz, _P],
+        "sd_block_sums_append": [ctypes.POINTER(SdShape), _P, _P, _P, _P, _P, _P, sz, _P],
         "sd_device_status": [_P, _P, ctypes.POINTER(ctypes.c_uint32)],
         "sd_workspace_bytes": [i32, _P, i32],
         "sd_status_str": [i32],
@@ -221,6 +224,55 @@ def kv_commit(k_pages, v_pages, block_table, ctx_lens, path, path_len, ws=None):
     _check("sd_kv_commit", lib().sd_kv_commit(
         ctypes.byref(shape), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(ctx_lens),
         _ptr(path), _ptr(path_len), _ptr(ws), ws.numel(), _stream(k_pages.device)))
+
+
+def _sums_shape(k_pages, block_table, ctx_lens):
+    nb, Hkv, bs, D = k_pages.shape
+    return SdShape(len(ctx_lens), 1, Hkv, Hkv, D, bs, block_table.shape[1], nb, _dtype_code[k_pages.dtype],
+                   0, 0.0)
+
+
+def block_sums(k_pages, block_table, ctx_lens, sums=None, ws=None):
+    """Kept block key sums, float32 [num_blocks, Hkv, D] (sd_block_sums); a new
+    zero-filled tensor unless `sums` is given."""
+    nb, Hkv, bs, D = k_pages.shape
+    if sums is None:
+        sums = torch.zeros((nb, Hkv, D), dtype=torch.float32, device=k_pages.device)
+    shape = _sums_shape(k_pages, block_table, ctx_lens)
+    need = workspace_bytes(SD_CALL_BLOCK_SUMS, shape)
+    ws = _WS.get(k_pages.device, need, SD_CALL_BLOCK_SUMS) if ws is None else ws
+    _check("sd_block_sums", lib().sd_block_sums(
+        ctypes.byref(shape), _ptr(k_pages), _ptr(block_table), _ptr(ctx_lens), _ptr(sums), _ptr(ws),
+        ws.numel(), _stream(k_pages.device)))
+    return sums
+
+
+def block_sums_append(k_pages, block_table, ctx_lens, n_new, sums, ws=None):
+    """Extends kept block sums by the n_new[b] positions a commit appended
+    (ctx_lens after the commit) (sd_block_sums_append)."""
+    shape = _sums_shape(k_pages, block_table, ctx_lens)
+    need = workspace_bytes(SD_CALL_BLOCK_SUMS, shape)
+    ws = _WS.get(k_pages.device, need, SD_CALL_BLOCK_SUMS) if ws is None else ws
+    _check("sd_block_sums_append", lib().sd_block_sums_append(
+        ctypes.byref(shape), _ptr(k_pages), _ptr(block_table), _ptr(ctx_lens), _ptr(n_new), _ptr(sums),
+        _ptr(ws), ws.numel(), _stream(k_pages.device)))
+    return sums
+
+
+def topk_blocks_cached(q, sums, k_pages_like, block_table, ctx_lens, k, sel=None, ws=None):
+    """sd_topk_blocks_cached: the top-k selection with means from kept block
+    sums.  `k_pages_like` supplies the cache's shape and dtype only (not read)."""
+    B, T, Hq, D = q.shape
+    parent_like = torch.empty((1, T))
+    shape = make_shape(q, k_pages_like, block_table, parent_like)
+    if sel is None:
+        sel = torch.empty((B, T, Hq, k), dtype=torch.int32, device=q.device)
+    need = workspace_bytes(SD_CALL_TOPK, shape, k)
+    ws = _WS.get(q.device, need, SD_CALL_TOPK) if ws is None else ws
+    _check("sd_topk_blocks_cached", lib().sd_topk_blocks_cached(
+        ctypes.byref(shape), _ptr(q), _ptr(sums), _ptr(block_table), _ptr(ctx_lens), int(k),
+        _ptr(sel), _ptr(ws), ws.numel(), _stream(q.device)))
+    return sel
 
 
 def topk_blocks(q, k_pages, block_table, ctx_lens, k, sel=None, ws=None):

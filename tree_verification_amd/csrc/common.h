@@ -152,6 +152,7 @@ struct TopkArgs {
   int32_t* sel;
   float* means;    // [B][nbmax][Hkv][D]
   float* scores;   // [B*T*Hq][nbmax]
+  float* sums;     // kept block key sums [num_blocks][Hkv][D] (cached selection)
   uint32_t* status;
   int B, T, Hq, Hkv, G, D, bs, max_blocks, num_blocks, topk, nbmax;
 };
@@ -163,6 +164,8 @@ hipError_t launch_attn_valu(const AttnArgs& a, bool f32, hipStream_t st);
 hipError_t launch_attn_mfma(const AttnArgs& a, const AttnPlan& p, hipStream_t st);
 hipError_t launch_accept(const AcceptArgs& a, hipStream_t st);
 hipError_t launch_commit(const CommitArgs& a, hipStream_t st);
-hipError_t launch_topk(const TopkArgs& a, bool f32, hipStream_t st);
+hipError_t launch_topk(const TopkArgs& a, bool f32, bool cached, hipStream_t st);
+hipError_t launch_block_sums(const TopkArgs& a, bool f32, hipStream_t st);
+hipError_t launch_block_sums_append(const TopkArgs& a, const int32_t* n_new, bool f32, hipStream_t st);
 
 }  // namespace sdtree

@@ -194,6 +194,10 @@ size_t sd_workspace_bytes(int32_t call_id, const void* shape, int32_t extra) {
     const sd_shape* s = static_cast<const sd_shape*>(shape);
     return check_shape(s) == SD_OK ? commit_ws(s) : 0;
   }
+  if (call_id == SD_CALL_BLOCK_SUMS) {
+    const sd_shape* s = static_cast<const sd_shape*>(shape);
+    return check_shape(s) == SD_OK ? kWsHeader : 0;
+  }
   if (call_id == SD_CALL_TOPK) {
     const sd_shape* s = static_cast<const sd_shape*>(shape);
     if (check_shape(s) != SD_OK || extra < 1) return 0;
@@ -341,28 +345,82 @@ sd_status sd_kv_commit(const sd_shape* shape, void* k_pages, void* v_pages,
   return hip_status(launch_commit(a, static_cast<hipStream_t>(stream)));
 }
 
-sd_status sd_topk_blocks(const sd_shape* shape, const void* q, const void* k_pages,
-                         const int32_t* block_table, const int32_t* ctx_lens, int32_t k,
-                         int32_t* sel_blocks, void* ws, size_t ws_bytes, void* stream) {
+static TopkArgs topk_args(const sd_shape* shape, const int32_t* block_table, const int32_t* ctx_lens,
+                          void* ws) {
+  TopkArgs a;
+  memset(&a, 0, sizeof(a));
+  a.table = block_table; a.ctx = ctx_lens;
+  a.status = static_cast<uint32_t*>(ws);
+  a.B = shape->B; a.T = shape->T; a.Hq = shape->Hq; a.Hkv = shape->Hkv;
+  a.G = shape->Hq / shape->Hkv; a.D = shape->D; a.bs = shape->bs;
+  a.max_blocks = shape->max_blocks; a.num_blocks = shape->num_blocks;
+  a.nbmax = shape->max_blocks;
+  return a;
+}
+
+// Top-k from K (block_sums == nullptr) or from kept block sums.
+static sd_status topk_common(const sd_shape* shape, const void* q, const void* k_pages,
+                             const float* block_sums, const int32_t* block_table,
+                             const int32_t* ctx_lens, int32_t k, int32_t* sel_blocks, void* ws,
+                             size_t ws_bytes, void* stream) {
   sd_status st = check_shape(shape);
   if (st != SD_OK) return st;
-  if (!q || !k_pages || !block_table || !ctx_lens || !sel_blocks || !ws) return SD_INVALID_ARG;
+  if (!q || (!k_pages && !block_sums) || !block_table || !ctx_lens || !sel_blocks || !ws)
+    return SD_INVALID_ARG;
   if (k < 1) return SD_INVALID_ARG;
   size_t mo, so;
   const size_t need = topk_ws(shape, &mo, &so);
   if (ws_bytes < need) return SD_CAPACITY;
   unsigned char* w = static_cast<unsigned char*>(ws);
-  TopkArgs a;
-  memset(&a, 0, sizeof(a));
-  a.q = q; a.k = k_pages; a.table = block_table; a.ctx = ctx_lens; a.sel = sel_blocks;
+  TopkArgs a = topk_args(shape, block_table, ctx_lens, ws);
+  a.q = q; a.k = k_pages; a.sel = sel_blocks; a.topk = k;
+  a.sums = const_cast<float*>(block_sums);
   a.means = reinterpret_cast<float*>(w + mo);
   a.scores = reinterpret_cast<float*>(w + so);
-  a.status = reinterpret_cast<uint32_t*>(w);
-  a.B = shape->B; a.T = shape->T; a.Hq = shape->Hq; a.Hkv = shape->Hkv;
-  a.G = shape->Hq / shape->Hkv; a.D = shape->D; a.bs = shape->bs;
-  a.max_blocks = shape->max_blocks; a.num_blocks = shape->num_blocks; a.topk = k;
-  a.nbmax = shape->max_blocks;
-  return hip_status(launch_topk(a, shape->dtype == SD_F32, static_cast<hipStream_t>(stream)));
+  return hip_status(launch_topk(a, shape->dtype == SD_F32, block_sums != nullptr,
+                                static_cast<hipStream_t>(stream)));
+}
+
+sd_status sd_topk_blocks(const sd_shape* shape, const void* q, const void* k_pages,
+                         const int32_t* block_table, const int32_t* ctx_lens, int32_t k,
+                         int32_t* sel_blocks, void* ws, size_t ws_bytes, void* stream) {
+  if (!k_pages) return SD_INVALID_ARG;
+  return topk_common(shape, q, k_pages, nullptr, block_table, ctx_lens, k, sel_blocks, ws, ws_bytes,
+                     stream);
+}
+
+sd_status sd_topk_blocks_cached(const sd_shape* shape, const void* q, const float* block_sums,
+                                const int32_t* block_table, const int32_t* ctx_lens, int32_t k,
+                                int32_t* sel_blocks, void* ws, size_t ws_bytes, void* stream) {
+  if (!block_sums) return SD_INVALID_ARG;
+  return topk_common(shape, q, nullptr, block_sums, block_table, ctx_lens, k, sel_blocks, ws,
+                     ws_bytes, stream);
+}
+
+sd_status sd_block_sums(const sd_shape* shape, const void* k_pages, const int32_t* block_table,
+                        const int32_t* ctx_lens, float* block_sums, void* ws, size_t ws_bytes,
+                        void* stream) {
+  sd_status st = check_shape(shape);
+  if (st != SD_OK) return st;
+  if (!k_pages || !block_table || !ctx_lens || !block_sums || !ws) return SD_INVALID_ARG;
+  if (ws_bytes < kWsHeader) return SD_CAPACITY;
+  TopkArgs a = topk_args(shape, block_table, ctx_lens, ws);
+  a.k = k_pages; a.sums = block_sums;
+  return hip_status(launch_block_sums(a, shape->dtype == SD_F32, static_cast<hipStream_t>(stream)));
+}
+
+sd_status sd_block_sums_append(const sd_shape* shape, const void* k_pages,
+                               const int32_t* block_table, const int32_t* ctx_lens,
+                               const int32_t* n_new, float* block_sums, void* ws, size_t ws_bytes,
+                               void* stream) {
+  sd_status st = check_shape(shape);
+  if (st != SD_OK) return st;
+  if (!k_pages || !block_table || !ctx_lens || !n_new || !block_sums || !ws) return SD_INVALID_ARG;
+  if (ws_bytes < kWsHeader) return SD_CAPACITY;
+  TopkArgs a = topk_args(shape, block_table, ctx_lens, ws);
+  a.k = k_pages; a.sums = block_sums;
+  return hip_status(launch_block_sums_append(a, n_new, shape->dtype == SD_F32,
+                                             static_cast<hipStream_t>(stream)));
 }
 
 sd_status sd_device_status(void* ws, void* stream, uint32_t* bits) {

@@ -11,6 +11,10 @@
 //          then d + D/4, ..., then d + 1               (block_score_kernel)
 //   select the k largest scores, lower block first on ties, emitted in
 //          ascending block order, -1 padded            (block_select_kernel)
+// Cached selection keeps the sums (the numerators of the means) per physical
+// block: built once from K, extended in position order by the positions each
+// commit appends (block_sums_append_kernel), and divided at selection time,
+// so its means are the same float32 values without reading K.
 #include "common.h"
 
 #pragma clang fp contract(off)
@@ -21,7 +25,11 @@ namespace sdtree {
 // owning one 16-byte column chunk (EPL consecutive dims) of the block's rows:
 // it walks the block's valid tokens in position order, 16 rows in flight, so
 // every dim's sum is the sequential one.  A wavefront serves 64 / LPU units.
-template <typename E, int D>
+// MODE 0 writes the means; MODE 1 writes the sums to the kept block sums of
+// the physical block instead; MODE 2 reads the sums from there (no K walk)
+// and writes the means.
+constexpr int kMeansFromK = 0, kSumsFromK = 1, kMeansFromSums = 2;
+template <typename E, int D, int MODE>
 __global__ void __launch_bounds__(256) block_mean_kernel(TopkArgs a) {
 #pragma clang fp contract(off)
   constexpr int EPL = 16 / (int)sizeof(E);      // dims per lane
@@ -44,41 +52,57 @@ __global__ void __launch_bounds__(256) block_mean_kernel(TopkArgs a) {
   const int nblk = (ctx + a.bs - 1) / a.bs;
   if (n >= nblk) return;
   const int blk = a.table[(size_t)b * a.max_blocks + n];
-  float* out = a.means + (((size_t)b * a.nbmax + n) * a.Hkv + g) * D + col * EPL;
+  float* out = MODE == kSumsFromK ? nullptr : a.means + (((size_t)b * a.nbmax + n) * a.Hkv + g) * D + col * EPL;
   if (blk < 0 || blk >= a.num_blocks) {
     if (col == 0) set_status(a.status, SD_ERR_BLOCK);
-    for (int e = 0; e < EPL; ++e) out[e] = 0.f;
+    if constexpr (MODE != kSumsFromK)
+      for (int e = 0; e < EPL; ++e) out[e] = 0.f;
     return;
   }
   const int valid = min(a.bs, ctx - n * a.bs);
-  const uint4* base = reinterpret_cast<const uint4*>(
-      reinterpret_cast<const E*>(a.k) + (((size_t)blk * a.Hkv + g) * a.bs) * D) + col;
-  constexpr int RS = D * (int)sizeof(E) / 16;    // uint4 per row
+  float* kept = MODE == kMeansFromK ? nullptr : a.sums + ((size_t)blk * a.Hkv + g) * D + col * EPL;
   float s[EPL];
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) s[e] = 0.f;
-  auto add = [&](const uint4& u) {
-    if constexpr (sizeof(E) == 2) {
-      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) s[e] = s[e] + bf16_to_f32((bf16_bits)(w[e >> 1] >> (16 * (e & 1))));
-    } else {
-      s[0] = s[0] + __uint_as_float(u.x);
-      s[1] = s[1] + __uint_as_float(u.y);
-      s[2] = s[2] + __uint_as_float(u.z);
-      s[3] = s[3] + __uint_as_float(u.w);
+  if constexpr (MODE == kMeansFromSums) {
+    const float4 u = reinterpret_cast<const float4*>(kept)[0];
+    s[0] = u.x; s[1] = u.y; s[2] = u.z; s[3] = u.w;
+    if constexpr (EPL == 8) {
+      const float4 w = reinterpret_cast<const float4*>(kept)[1];
+      s[4] = w.x; s[5] = w.y; s[6] = w.z; s[7] = w.w;
     }
-  };
-  constexpr int RIF = 16;   // rows in flight
-  int t = 0;
-  for (; t + RIF <= valid; t += RIF) {
-    uint4 x[RIF];
+  } else {
+    const uint4* base = reinterpret_cast<const uint4*>(
+        reinterpret_cast<const E*>(a.k) + (((size_t)blk * a.Hkv + g) * a.bs) * D) + col;
+    constexpr int RS = D * (int)sizeof(E) / 16;    // uint4 per row
 #pragma unroll
-    for (int u = 0; u < RIF; ++u) x[u] = base[(size_t)(t + u) * RS];
+    for (int e = 0; e < EPL; ++e) s[e] = 0.f;
+    auto add = [&](const uint4& u) {
+      if constexpr (sizeof(E) == 2) {
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
-    for (int u = 0; u < RIF; ++u) add(x[u]);
+        for (int e = 0; e < EPL; ++e) s[e] = s[e] + bf16_to_f32((bf16_bits)(w[e >> 1] >> (16 * (e & 1))));
+      } else {
+        s[0] = s[0] + __uint_as_float(u.x);
+        s[1] = s[1] + __uint_as_float(u.y);
+        s[2] = s[2] + __uint_as_float(u.z);
+        s[3] = s[3] + __uint_as_float(u.w);
+      }
+    };
+    constexpr int RIF = 16;   // rows in flight
+    int t = 0;
+    for (; t + RIF <= valid; t += RIF) {
+      uint4 x[RIF];
+#pragma unroll
+      for (int u = 0; u < RIF; ++u) x[u] = base[(size_t)(t + u) * RS];
+#pragma unroll
+      for (int u = 0; u < RIF; ++u) add(x[u]);
+    }
+    for (; t < valid; ++t) add(base[(size_t)t * RS]);
   }
-  for (; t < valid; ++t) add(base[(size_t)t * RS]);
+  if constexpr (MODE == kSumsFromK) {
+    reinterpret_cast<float4*>(kept)[0] = make_float4(s[0], s[1], s[2], s[3]);
+    if constexpr (EPL == 8) reinterpret_cast<float4*>(kept)[1] = make_float4(s[4], s[5], s[6], s[7]);
+    return;
+  }
   const float fv = (float)valid;
   float r[EPL];
 #pragma unroll
@@ -341,14 +365,91 @@ __global__ void __launch_bounds__(256) block_select_kernel(TopkArgs a) {
   for (int e = sel_before + lane; e < a.topk; e += 64) out[e] = -1;
 }
 
+// Kept block sums after a commit: the positions [ctx_b - n_b, ctx_b) it
+// appended (ctx_lens after the commit, n_b = path_len[b]) are added, in
+// position order, to their blocks' sums; a block whose first position is
+// among them starts from +0, so every sum stays the sequential one.  One
+// wavefront per (b, KV head), D / 64 dims per lane; the touched blocks are
+// validated before anything is written.
 template <typename E, int D>
-static hipError_t launch_topk_t(const TopkArgs& a, hipStream_t st) {
+__global__ void __launch_bounds__(256) block_sums_append_kernel(TopkArgs a, const int32_t* __restrict__ n_new) {
+#pragma clang fp contract(off)
+  constexpr int DPL = D / 64;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const long long unit = (long long)blockIdx.x * 4 + wave;
+  if (unit >= (long long)a.B * a.Hkv) return;
+  const int b = (int)(unit / a.Hkv), g = (int)(unit % a.Hkv);
+  const int ctx = a.ctx[b], L = n_new[b];
+  if (L < 0 || L > ctx || (long long)ctx > (long long)a.max_blocks * a.bs) {
+    if (g == 0 && lane == 0) set_status(a.status, SD_ERR_CAPACITY);
+    return;
+  }
+  if (L == 0) return;
+  const int32_t* table = a.table + (size_t)b * a.max_blocks;
+  for (int n = (ctx - L) / a.bs; n <= (ctx - 1) / a.bs; ++n) {
+    const int blk = table[n];
+    if (blk < 0 || blk >= a.num_blocks) {
+      if (g == 0 && lane == 0) set_status(a.status, SD_ERR_BLOCK);
+      return;
+    }
+  }
+  const E* K = reinterpret_cast<const E*>(a.k);
+  const int d0 = lane * DPL;
+  for (int t = ctx - L; t < ctx;) {
+    const int n = t / a.bs, off = t - n * a.bs;
+    const int t1 = min((n + 1) * a.bs, ctx);
+    const int blk = table[n];
+    float* kept = a.sums + ((size_t)blk * a.Hkv + g) * D + d0;
+    const E* row = K + (((size_t)blk * a.Hkv + g) * a.bs) * D + d0;
+    float s[DPL];
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) s[e] = off == 0 ? 0.f : kept[e];
+    // rows loaded RIF at a time, all in flight, then added in position order
+    constexpr int RIF = 16;
+    const int end = off + (t1 - t);
+    for (int u0 = off; u0 < end; u0 += RIF) {
+      float x[RIF][DPL];
+#pragma unroll
+      for (int r = 0; r < RIF; ++r) {
+        const int u = min(u0 + r, end - 1);     // (past the end: a valid row, not added)
+        if constexpr (sizeof(E) == 2) {
+          if constexpr (DPL == 2) {
+            const uint32_t w = *reinterpret_cast<const uint32_t*>(row + (size_t)u * D);
+            x[r][0] = bf16_to_f32((bf16_bits)(w & 0xFFFFu));
+            x[r][1] = bf16_to_f32((bf16_bits)(w >> 16));
+          } else {
+            x[r][0] = bf16_to_f32(row[(size_t)u * D]);
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < DPL; ++e) x[r][e] = row[(size_t)u * D + e];
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < RIF; ++r)
+        if (u0 + r < end)
+#pragma unroll
+          for (int e = 0; e < DPL; ++e) s[e] = s[e] + x[r][e];
+    }
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) kept[e] = s[e];
+    t = t1;
+  }
+}
+
+template <typename E, int D, int MODE>
+static hipError_t launch_means(const TopkArgs& a, hipStream_t st) {
   constexpr int UPW = 64 / (D / (16 / (int)sizeof(E)));
   const long long units = (long long)a.B * a.nbmax * a.Hkv;
   const long long per_wg = 4LL * UPW;
-  hipLaunchKernelGGL((block_mean_kernel<E, D>), dim3((unsigned)((units + per_wg - 1) / per_wg)), dim3(256), 0,
-                     st, a);
-  hipError_t e = hipGetLastError();
+  hipLaunchKernelGGL((block_mean_kernel<E, D, MODE>), dim3((unsigned)((units + per_wg - 1) / per_wg)),
+                     dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+template <typename E, int D>
+static hipError_t launch_topk_t(const TopkArgs& a, bool cached, hipStream_t st) {
+  hipError_t e = cached ? launch_means<E, D, kMeansFromSums>(a, st) : launch_means<E, D, kMeansFromK>(a, st);
   if (e != hipSuccess) return e;
   dim3 g2((a.nbmax + 63) / 64, a.Hkv, a.B);
   hipLaunchKernelGGL((block_score_kernel<E, D>), g2, dim3(256), 0, st, a);
@@ -359,9 +460,27 @@ static hipError_t launch_topk_t(const TopkArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_topk(const TopkArgs& a, bool f32, hipStream_t st) {
-  if (f32) return a.D == 64 ? launch_topk_t<float, 64>(a, st) : launch_topk_t<float, 128>(a, st);
-  return a.D == 64 ? launch_topk_t<bf16_bits, 64>(a, st) : launch_topk_t<bf16_bits, 128>(a, st);
+hipError_t launch_topk(const TopkArgs& a, bool f32, bool cached, hipStream_t st) {
+  if (f32) return a.D == 64 ? launch_topk_t<float, 64>(a, cached, st) : launch_topk_t<float, 128>(a, cached, st);
+  return a.D == 64 ? launch_topk_t<bf16_bits, 64>(a, cached, st) : launch_topk_t<bf16_bits, 128>(a, cached, st);
+}
+
+hipError_t launch_block_sums(const TopkArgs& a, bool f32, hipStream_t st) {
+  if (f32)
+    return a.D == 64 ? launch_means<float, 64, kSumsFromK>(a, st) : launch_means<float, 128, kSumsFromK>(a, st);
+  return a.D == 64 ? launch_means<bf16_bits, 64, kSumsFromK>(a, st) : launch_means<bf16_bits, 128, kSumsFromK>(a, st);
+}
+
+hipError_t launch_block_sums_append(const TopkArgs& a, const int32_t* n_new, bool f32, hipStream_t st) {
+  const dim3 grid((unsigned)(((long long)a.B * a.Hkv + 3) / 4));
+  if (f32) {
+    if (a.D == 64) hipLaunchKernelGGL((block_sums_append_kernel<float, 64>), grid, dim3(256), 0, st, a, n_new);
+    else hipLaunchKernelGGL((block_sums_append_kernel<float, 128>), grid, dim3(256), 0, st, a, n_new);
+  } else {
+    if (a.D == 64) hipLaunchKernelGGL((block_sums_append_kernel<bf16_bits, 64>), grid, dim3(256), 0, st, a, n_new);
+    else hipLaunchKernelGGL((block_sums_append_kernel<bf16_bits, 128>), grid, dim3(256), 0, st, a, n_new);
+  }
+  return hipGetLastError();
 }
 
 }  // namespace sdtree
