@@ -68,6 +68,11 @@ def parse():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after the run, copy MIB MiB device-to-device 3 times (a plain copy "
                          "kernel of known size that scales the HBM byte counters)")
+    ap.add_argument("--sweep", choices=["tree", "topk"],
+                    help="no bench line: one JSON line per point of a sweep instead.  tree: the "
+                         "attention of the 8B-like shape (B 16, 32/8 heads, ctx 4096) over tree "
+                         "sizes T = 1 .. 4096, across the HBM / MFMA crossover; topk: the block "
+                         "selection of the 4 x 64K workload over k, from K and from kept sums")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="no run: turn the counter_collection.csv files of a rocprofv3 "
                          "--pmc FETCH_SIZE pass and a --pmc WRITE_SIZE pass (both of a run "
@@ -411,8 +416,88 @@ def cpu_baseline(w, budget_s):
             "step_s_est": round(t_step, 3)}
 
 
+def _median_us(torch, fn, reps=10, rounds=5):
+    ts = []
+    for _ in range(rounds):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = HipEvent(), HipEvent()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) / reps * 1e3)
+    return float(np.median(ts))
+
+
+def sweep(kind):
+    """Timing sweeps (one JSON line per point), each point after a 200 ms settle
+    of its own calls.  Inputs are the workloads' seeded synthetic recipes with
+    one dimension varied (a small vocabulary: only attention or selection is
+    timed)."""
+    import dataclasses
+    import torch
+    import tree_verification_amd as tva
+    from synth import CONFIGS, make_inputs
+    from tests.devutil import to_device
+
+    def settle(fn):
+        t_end = time.perf_counter() + 0.2
+        while time.perf_counter() < t_end:
+            for _ in range(5):
+                fn()
+            torch.cuda.synchronize()
+
+    if kind == "tree":
+        base = CONFIGS["llama3_8b_tree64"]
+        for T in (1, 4, 16, 32, 64, 80, 128, 256, 512, 1024, 2048, 4096):
+            c = dataclasses.replace(base, T=T, V=16, max_parent_depth=8)
+            x = make_inputs(c)
+            d = to_device(x)
+            f = lambda: tva.tree_verify_attn(d["q"], d["k"], d["v"], d["table"], d["ctx"], d["parent"])
+            settle(f)
+            t = _median_us(torch, f) * 1e-6
+            bytes_, flops = attention_cost(c, x)
+            line = {"sweep": "tree", "T": T, "M": T * c.Hq // c.Hkv, "attention_us": round(t * 1e6, 1),
+                    "hbm_tb_s": round(bytes_ / t / 1e12, 3), "mfma_tflop_s": round(flops / t / 1e12, 1),
+                    "roofline": roofline_for(c, bytes_, flops, t),
+                    "verified_tree_tokens_per_s": round(c.B * T / t, 1)}
+            print(json.dumps(line), flush=True)
+            del d, x
+    else:
+        base = CONFIGS["sparse_topk32_ctx64k"]
+        x = make_inputs(base)
+        d = to_device(x)
+        sums = tva.block_sums(d["k"], d["table"], d["ctx"])
+        for k in (1, 8, 16, 32, 64, 128, 256):
+            f_k = lambda: tva.topk_blocks(d["q"], d["k"], d["table"], d["ctx"], k)
+            f_c = lambda: tva.topk_blocks_cached(d["q"], sums, d["k"], d["table"], d["ctx"], k)
+            settle(f_c)
+            t_k = _median_us(torch, f_k)
+            t_c = _median_us(torch, f_c)
+            sel = f_c()
+            torch.cuda.synchronize()
+            sel_np = sel.cpu().numpy()
+            bytes_, flops = attention_cost(base, x, sel_np)
+            f_a = lambda: tva.tree_verify_attn(d["q"], d["k"], d["v"], d["table"], d["ctx"], d["parent"],
+                                               sel_blocks=sel)
+            try:
+                t_a = _median_us(torch, f_a)
+            except tva.SdError:
+                t_a = None          # selections wider than sparse attention accepts
+            line = {"sweep": "topk", "k": k, "topk_from_k_us": round(t_k, 1), "topk_cached_us": round(t_c, 1),
+                    "sparse_attention_us": None if t_a is None else round(t_a, 1),
+                    "selected_bytes": int(bytes_),
+                    "sparse_attention_tb_s": None if t_a is None else round(bytes_ / t_a / 1e6, 3)}
+            print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
+    if args.sweep:
+        sweep(args.sweep)
+        return
     if args.write_traffic:
         write_traffic(args.workload, args.write_traffic[0], args.write_traffic[1],
                       args.copy_calibration or 1024)
