@@ -18,6 +18,8 @@ statement of each step:
 * ``commit``     -- the accepted root path becomes committed context.
 * ``topk``       -- keep the top-k KV blocks per query by a cheap relevance
   score (sparse-verification page, "Methodology", attention sparsity).
+* ``expand``     -- one batched step of the draft-tree search: the best
+  children by cumulative log-probability (SpecExec page, "Approach").
 
 Pins (tests/test_oracle_*.py) tie each function to something other than
 itself: torch's scaled_dot_product_attention, closed forms, brute force over
@@ -32,4 +34,5 @@ from .accept import accept, invcdf  # noqa: F401
 from .commit import commit  # noqa: F401
 from .topk import (append_block_sums, block_means, block_scores, block_sums,  # noqa: F401
                    means_from_sums, topk_blocks)
+from .expand import expand  # noqa: F401
 from .codec import decode  # noqa: F401
