@@ -68,11 +68,13 @@ def parse():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after the run, copy MIB MiB device-to-device 3 times (a plain copy "
                          "kernel of known size that scales the HBM byte counters)")
-    ap.add_argument("--sweep", choices=["tree", "topk"],
+    ap.add_argument("--sweep", choices=["tree", "topk", "expand"],
                     help="no bench line: one JSON line per point of a sweep instead.  tree: the "
                          "attention of the 8B-like shape (B 16, 32/8 heads, ctx 4096) over tree "
                          "sizes T = 1 .. 4096, across the HBM / MFMA crossover; topk: the block "
-                         "selection of the 4 x 64K workload over k, from K and from kept sums")
+                         "selection of the 4 x 64K workload over k, from K and from kept sums; "
+                         "expand: one draft-tree expansion step (sd_tree_expand) over batch "
+                         "sizes, vocabulary 32000, k 2048, with the oracle timed beside it")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="no run: turn the counter_collection.csv files of a rocprofv3 "
                          "--pmc FETCH_SIZE pass and a --pmc WRITE_SIZE pass (both of a run "
@@ -465,6 +467,27 @@ def sweep(kind):
                     "verified_tree_tokens_per_s": round(c.B * T / t, 1)}
             print(json.dumps(line), flush=True)
             del d, x
+    elif kind == "expand":
+        import oracle
+        from synth.inputs import f32_to_bf16_bits
+        V, k = 32000, 2048
+        for E in (1, 8, 64, 256, 1024):
+            rng = np.random.default_rng(E)
+            l = f32_to_bf16_bits((rng.standard_normal((E, V)) * 3).astype(np.float32))
+            cum = (-rng.random(E) * 5).astype(np.float32)
+            dl = torch.from_numpy(l.view(np.int16)).cuda().view(torch.bfloat16)
+            dc = torch.from_numpy(cum).cuda()
+            kk = min(k, E * V)
+            f = lambda: tva.tree_expand(dl, dc, 0.6, kk)
+            settle(f)
+            t = _median_us(torch, f)
+            t0 = time.perf_counter()
+            oracle.expand(l, "bf16", cum, 0.6, kk)
+            t_cpu = time.perf_counter() - t0
+            line = {"sweep": "expand", "E": E, "V": V, "k": kk, "expand_us": round(t, 1),
+                    "logit_bytes": E * V * 2, "hbm_tb_s": round(E * V * 2 / t / 1e6, 3),
+                    "oracle_cpu_ms": round(t_cpu * 1e3, 1)}
+            print(json.dumps(line), flush=True)
     else:
         base = CONFIGS["sparse_topk32_ctx64k"]
         x = make_inputs(base)

@@ -14,7 +14,8 @@
  *   sd_topk_blocks       top-k KV blocks per query for sparse verification;
  *   sd_block_sums, sd_block_sums_append, sd_topk_blocks_cached
  *                        the same selection from per-block key sums kept as
- *                        the context grows.
+ *                        the context grows;
+ *   sd_tree_expand       one batched expansion step of the draft-tree search.
  *
  * Conventions shared by every call
  *   - Tensor arguments are DEVICE pointers owned by the caller.  The library
@@ -100,7 +101,14 @@ typedef struct sd_accept_shape {
   int32_t tree_stride;  /* 0 or T, as in sd_shape */
 } sd_accept_shape;
 
-enum { SD_CALL_ATTN = 1, SD_CALL_ACCEPT = 2, SD_CALL_TOPK = 3, SD_CALL_COMMIT = 4, SD_CALL_BLOCK_SUMS = 5 };
+typedef struct sd_expand_shape {
+  int32_t E;            /* expanded nodes (rows of draft logits) */
+  int32_t V;            /* vocabulary */
+  int32_t logit_dtype;  /* sd_dtype of draft_logits */
+} sd_expand_shape;
+
+enum { SD_CALL_ATTN = 1, SD_CALL_ACCEPT = 2, SD_CALL_TOPK = 3, SD_CALL_COMMIT = 4, SD_CALL_BLOCK_SUMS = 5,
+       SD_CALL_EXPAND = 6 };
 
 /*
  * Tree-masked grouped-query attention over the paged cache.
@@ -230,10 +238,30 @@ sd_status sd_topk_blocks_cached(const sd_shape* shape, const void* q, const floa
                                 const int32_t* block_table, const int32_t* ctx_lens, int32_t k,
                                 int32_t* sel_blocks, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * One batched expansion step of the draft-tree search (SpecExec page,
+ * "Approach": the draft tree is grown from the continuations of highest
+ * cumulative probability by a batched shortest-path search with the draft
+ * model).  Every token x after expanded node e is a candidate child scored
+ *   s(e, x) = cum_logp[e] + log_softmax(draft_logits[e] / temperature)[x]
+ * in float32; the k best are written best first (ties to the smaller
+ * e * V + x):
+ *   draft_logits  [E, V] in logit_dtype;  cum_logp  float32 [E];
+ *   out_row int32 [k] (index of e), out_token int32 [k], out_score float32 [k].
+ * 1 <= k <= min(4096, E * V); temperature > 0; E * V < 2^32 - 1.
+ * ws >= sd_workspace_bytes(SD_CALL_EXPAND, shape, k), zero-filled before
+ * its first use (every call leaves it reusable).  The draft model, and which
+ * kept children are inserted or expanded next, stay with the caller.
+ */
+sd_status sd_tree_expand(const sd_expand_shape* shape, const void* draft_logits,
+                         const float* cum_logp, float temperature, int32_t k, int32_t* out_row,
+                         int32_t* out_token, float* out_score, void* ws, size_t ws_bytes,
+                         void* stream);
+
 /* Workspace bytes a call needs; `shape` points to an sd_shape (ATTN, TOPK,
- * COMMIT, BLOCK_SUMS) or an sd_accept_shape (ACCEPT, also for
- * sd_accept_commit); `extra` is k_sel (ATTN, 0 = dense) or k (TOPK).  0 on bad
- * input. */
+ * COMMIT, BLOCK_SUMS), an sd_accept_shape (ACCEPT, also for
+ * sd_accept_commit) or an sd_expand_shape (EXPAND); `extra` is k_sel (ATTN,
+ * 0 = dense) or k (TOPK, EXPAND).  0 on bad input. */
 size_t sd_workspace_bytes(int32_t call_id, const void* shape, int32_t extra);
 
 /* Synchronises `stream`, reads the sticky bits into *bits (may be NULL), clears

@@ -17,7 +17,7 @@ def setup_module():
 
 def test_exports_every_declared_function():
     names = _lib.declared_functions()
-    assert len(names) == 11
+    assert len(names) == 12
     for n in names:
         assert hasattr(L, n), n
 
@@ -127,6 +127,22 @@ def test_block_sums_calls_reject_bad_arguments():
     assert L.sd_topk_blocks_cached(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, 0, FAKE, FAKE, big, None) == 1
     assert L.sd_topk_blocks_cached(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, 4, FAKE, FAKE, 10, None) == 5
     assert L.sd_workspace_bytes(5, ctypes.byref(s), 0) > 0
+
+
+def test_tree_expand_rejects_bad_arguments():
+    def call(E=4, V=100, dt=1, tau=0.8, k=8, ws=1 << 20, out=FAKE):
+        return L.sd_tree_expand(ctypes.byref(_lib.SdExpandShape(E, V, dt)), FAKE, FAKE, tau, k, out, FAKE,
+                                FAKE, FAKE, ws, None)
+    assert call(E=0) == 2
+    assert call(dt=7) == 3
+    assert call(k=0) == 1
+    assert call(k=401) == 1                 # more than E * V
+    assert call(E=100, V=100, k=5000) == 4  # more than 4096
+    assert call(tau=0.0) == 1
+    assert call(out=None) == 1
+    assert call(ws=64) == 5
+    assert L.sd_workspace_bytes(6, ctypes.byref(_lib.SdExpandShape(4, 100, 1)), 8) > 0
+    assert L.sd_workspace_bytes(6, ctypes.byref(_lib.SdExpandShape(4, 100, 1)), 0) == 0
 
 
 def test_commit_and_topk_reject_bad_arguments():

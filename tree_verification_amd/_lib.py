@@ -16,7 +16,8 @@ LIB_PATH = os.path.join(_HERE, "libsdtree.so")
 HEADER = os.path.join(os.path.dirname(_HERE), "include", "sdtree.h")
 
 SD_F32, SD_BF16 = 0, 1
-SD_CALL_ATTN, SD_CALL_ACCEPT, SD_CALL_TOPK, SD_CALL_COMMIT, SD_CALL_BLOCK_SUMS = 1, 2, 3, 4, 5
+SD_CALL_ATTN, SD_CALL_ACCEPT, SD_CALL_TOPK, SD_CALL_COMMIT, SD_CALL_BLOCK_SUMS, SD_CALL_EXPAND = \
+    1, 2, 3, 4, 5, 6
 STATUS = {0: "SD_OK", 1: "SD_INVALID_ARG", 2: "SD_BAD_SHAPE", 3: "SD_BAD_DTYPE",
           4: "SD_UNSUPPORTED", 5: "SD_CAPACITY", 6: "SD_HIP_ERROR", 7: "SD_DEVICE_DATA_ERROR"}
 ERR_BITS = {0x1: "parent", 0x2: "block", 0x4: "capacity", 0x8: "token", 0x10: "selection"}
@@ -33,6 +34,10 @@ class SdShape(ctypes.Structure):
 class SdAcceptShape(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("T", ctypes.c_int32), ("V", ctypes.c_int32),
                 ("logit_dtype", ctypes.c_int32), ("tree_stride", ctypes.c_int32)]
+
+
+class SdExpandShape(ctypes.Structure):
+    _fields_ = [("E", ctypes.c_int32), ("V", ctypes.c_int32), ("logit_dtype", ctypes.c_int32)]
 
 
 class SdError(RuntimeError):
@@ -69,6 +74,8 @@ def lib():
         "sd_topk_blocks": [ctypes.POINTER(SdShape), _P, _P, _P, _P, i32, _P, _P, sz, _P],
         "sd_topk_blocks_cached": [ctypes.POINTER(SdShape), _P, _P, _P, _P, i32, _P, _P, sz, _P],
         "sd_block_sums": [ctypes.POINTER(SdShape), _P, _P, _P, _P, _P, sz, _P],
+        "sd_tree_expand": [ctypes.POINTER(SdExpandShape), _P, _P, ctypes.c_float, i32, _P, _P, _P, _P, sz,
+                           _P],
         "sd_block_sums_append": [ctypes.POINTER(SdShape), _P, _P, _P, _P, _P, _P, sz, _P],
         "sd_device_status": [_P, _P, ctypes.POINTER(ctypes.c_uint32)],
         "sd_workspace_bytes": [i32, _P, i32],
@@ -224,6 +231,24 @@ def kv_commit(k_pages, v_pages, block_table, ctx_lens, path, path_len, ws=None):
     _check("sd_kv_commit", lib().sd_kv_commit(
         ctypes.byref(shape), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(ctx_lens),
         _ptr(path), _ptr(path_len), _ptr(ws), ws.numel(), _stream(k_pages.device)))
+
+
+def tree_expand(draft_logits, cum_logp, temperature, k, ws=None):
+    """sd_tree_expand: the k best children (row, token, score), best first."""
+    E, V = draft_logits.shape
+    shape = SdExpandShape(E, V, _dtype_code[draft_logits.dtype])
+    dev = draft_logits.device
+    row = torch.empty(k, dtype=torch.int32, device=dev)
+    tok = torch.empty(k, dtype=torch.int32, device=dev)
+    score = torch.empty(k, dtype=torch.float32, device=dev)
+    need = workspace_bytes(SD_CALL_EXPAND, shape, k)
+    if need == 0:
+        raise SdError("sd_workspace_bytes", 2)
+    ws = _WS.get(dev, need, SD_CALL_EXPAND) if ws is None else ws
+    _check("sd_tree_expand", lib().sd_tree_expand(
+        ctypes.byref(shape), _ptr(draft_logits), _ptr(cum_logp), float(temperature), int(k), _ptr(row),
+        _ptr(tok), _ptr(score), _ptr(ws), ws.numel(), _stream(dev)))
+    return row, tok, score
 
 
 def _sums_shape(k_pages, block_table, ctx_lens):

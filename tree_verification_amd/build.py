@@ -3,8 +3,9 @@
     python -m tree_verification_amd.build [--verbose]
 
 Every .hip source under csrc/ is compiled to an object and linked into
-tree_verification_amd/libsdtree.so.  The top-k source is compiled with
--ffp-contract=off because its float32 arithmetic order is part of its result.
+tree_verification_amd/libsdtree.so.  The top-k and expansion sources are
+compiled with -ffp-contract=off because their float32 arithmetic order is part
+of their result.
 """
 import os
 import subprocess
@@ -25,8 +26,8 @@ COMMON = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
 ]
-PER_FILE = {"topk.hip": ["-ffp-contract=off"]}
-SOURCES = ["sdtree.hip", "attn.hip", "accept.hip", "commit.hip", "topk.hip"]
+PER_FILE = {"topk.hip": ["-ffp-contract=off"], "expand.hip": ["-ffp-contract=off"]}
+SOURCES = ["sdtree.hip", "attn.hip", "accept.hip", "commit.hip", "topk.hip", "expand.hip"]
 
 
 def _compile(src, verbose):

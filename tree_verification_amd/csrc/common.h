@@ -157,7 +157,24 @@ struct TopkArgs {
   int B, T, Hq, Hkv, G, D, bs, max_blocks, num_blocks, topk, nbmax;
 };
 
+// One batched expansion step of the draft-tree search.
+constexpr int kMaxExpandK = 4096;
+struct ExpandArgs {
+  const void* logits;   // [E][V]
+  const float* cum;     // [E]
+  float inv_tau;
+  int E, V, k;
+  float* off;           // [E] workspace
+  uint32_t* hist;       // [8][256] workspace
+  uint32_t* count;      // workspace, zero between calls
+  unsigned long long* keys;  // [k] workspace
+  int32_t* out_row;
+  int32_t* out_token;
+  float* out_score;
+};
+
 // Launchers (one per kernel family).
+hipError_t launch_expand(const ExpandArgs& a, bool f32, hipStream_t st);
 hipError_t launch_anc_mask(const int32_t* parent, int T, int W64, int n_trees, uint64_t* anc,
                            uint32_t* status, hipStream_t st);
 hipError_t launch_attn_valu(const AttnArgs& a, bool f32, hipStream_t st);

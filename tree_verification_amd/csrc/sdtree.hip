@@ -139,6 +139,30 @@ static AttnPlan plan_attn(const sd_shape* s, int ksel, bool sparse) {
 // Commit scratch: the status header and one completion counter per sequence.
 static size_t commit_ws(const sd_shape* s) { return kWsHeader + align_up((size_t)s->B * 4, 256); }
 
+// Expansion scratch: row offsets, 8 x 256 histograms, a counter, k keys.
+static size_t expand_ws(const sd_expand_shape* s, int32_t k, size_t* off, size_t* hist, size_t* cnt,
+                        size_t* keys) {
+  const size_t o = kWsHeader;
+  const size_t h = align_up(o + (size_t)s->E * 4, 256);
+  const size_t c = h + 8 * 256 * 4;
+  const size_t kk = align_up(c + 4, 256);
+  if (off) *off = o;
+  if (hist) *hist = h;
+  if (cnt) *cnt = c;
+  if (keys) *keys = kk;
+  return align_up(kk + (size_t)k * 8, 256);
+}
+
+static sd_status check_expand(const sd_expand_shape* s, int32_t k) {
+  if (!s) return SD_INVALID_ARG;
+  if (s->E < 1 || s->V < 1) return SD_BAD_SHAPE;
+  if (s->logit_dtype != SD_F32 && s->logit_dtype != SD_BF16) return SD_BAD_DTYPE;
+  if ((long long)s->E * s->V >= 0xFFFFFFFFll || s->E > 65535) return SD_UNSUPPORTED;
+  if (k < 1 || (long long)k > (long long)s->E * s->V) return SD_INVALID_ARG;
+  if (k > kMaxExpandK) return SD_UNSUPPORTED;
+  return SD_OK;
+}
+
 static size_t topk_ws(const sd_shape* s, size_t* means_off, size_t* scores_off) {
   const size_t nbmax = (size_t)s->max_blocks;
   const size_t mo = kWsHeader;
@@ -193,6 +217,10 @@ size_t sd_workspace_bytes(int32_t call_id, const void* shape, int32_t extra) {
   if (call_id == SD_CALL_COMMIT) {
     const sd_shape* s = static_cast<const sd_shape*>(shape);
     return check_shape(s) == SD_OK ? commit_ws(s) : 0;
+  }
+  if (call_id == SD_CALL_EXPAND) {
+    const sd_expand_shape* s = static_cast<const sd_expand_shape*>(shape);
+    return check_expand(s, extra) == SD_OK ? expand_ws(s, extra, nullptr, nullptr, nullptr, nullptr) : 0;
   }
   if (call_id == SD_CALL_BLOCK_SUMS) {
     const sd_shape* s = static_cast<const sd_shape*>(shape);
@@ -421,6 +449,29 @@ sd_status sd_block_sums_append(const sd_shape* shape, const void* k_pages,
   a.k = k_pages; a.sums = block_sums;
   return hip_status(launch_block_sums_append(a, n_new, shape->dtype == SD_F32,
                                              static_cast<hipStream_t>(stream)));
+}
+
+sd_status sd_tree_expand(const sd_expand_shape* shape, const void* draft_logits,
+                         const float* cum_logp, float temperature, int32_t k, int32_t* out_row,
+                         int32_t* out_token, float* out_score, void* ws, size_t ws_bytes,
+                         void* stream) {
+  const sd_status st = check_expand(shape, k);
+  if (st != SD_OK) return st;
+  if (!(temperature > 0.f) || isinf(temperature)) return SD_INVALID_ARG;
+  if (!draft_logits || !cum_logp || !out_row || !out_token || !out_score || !ws) return SD_INVALID_ARG;
+  size_t o, h, c, kk;
+  if (ws_bytes < expand_ws(shape, k, &o, &h, &c, &kk)) return SD_CAPACITY;
+  unsigned char* w = static_cast<unsigned char*>(ws);
+  ExpandArgs a;
+  memset(&a, 0, sizeof(a));
+  a.logits = draft_logits; a.cum = cum_logp; a.inv_tau = 1.f / temperature;
+  a.E = shape->E; a.V = shape->V; a.k = k;
+  a.off = reinterpret_cast<float*>(w + o);
+  a.hist = reinterpret_cast<uint32_t*>(w + h);
+  a.count = reinterpret_cast<uint32_t*>(w + c);
+  a.keys = reinterpret_cast<unsigned long long*>(w + kk);
+  a.out_row = out_row; a.out_token = out_token; a.out_score = out_score;
+  return hip_status(launch_expand(a, shape->logit_dtype == SD_F32, static_cast<hipStream_t>(stream)));
 }
 
 sd_status sd_device_status(void* ws, void* stream, uint32_t* bits) {
