@@ -17,7 +17,9 @@ statement of each step:
   (SpecExec page, "Approach").
 * ``commit``     -- the accepted root path becomes committed context.
 * ``topk``       -- keep the top-k KV blocks per query by a cheap relevance
-  score (sparse-verification page, "Methodology", attention sparsity).
+  score (sparse-verification page, "Methodology", attention sparsity), per
+  query or shared by a KV group's rows (same section, reuse across draft
+  tokens).
 * ``expand``     -- one batched step of the draft-tree search: the best
   children by cumulative log-probability (SpecExec page, "Approach").
 
@@ -33,6 +35,6 @@ from .attention import attention_dense, attention_by_path  # noqa: F401
 from .accept import accept, invcdf  # noqa: F401
 from .commit import commit  # noqa: F401
 from .topk import (append_block_sums, block_means, block_scores, block_sums,  # noqa: F401
-                   means_from_sums, topk_blocks)
+                   means_from_sums, pooled_query, topk_blocks, topk_blocks_shared)
 from .expand import expand  # noqa: F401
 from .codec import decode  # noqa: F401

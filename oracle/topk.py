@@ -21,6 +21,14 @@ context grows): `block_sums` is the numerator of the mean above, per
 physical block, and `append_block_sums` extends it by the positions a
 commit appended, continuing the same sequential sum; a mean formed from the
 kept sums is therefore the same float32 value as one formed from K.
+
+Shared selection (the sparse-verification page, "Methodology", reuse across
+draft tokens): one selection per (sequence, KV group), used by every tree
+node and every query head of the group.  Reading of its score: the sum of the
+group's per-row relevance scores, formed as the pooled query dotted with the
+block mean.  The pooled query is a sequential float32 sum from +0 of the
+group's query rows, node by node and, within a node, head by head; the dot
+product and the order are those above.
 """
 import numpy as np
 
@@ -137,4 +145,33 @@ def topk_blocks(q, k_pages, block_table, ctx_lens, bs, k, dtype, means=None):
                     continue
                 sc = block_scores(decode_f32(q[b, i, h], dtype), means[b, :nb, h // G])
                 sel[b, i, h] = select(sc, k)
+    return sel
+
+
+def pooled_query(q, b, g, G, dtype):
+    """float32 [D]: the sequential sum of q[b, i, g*G + j] over i, then j."""
+    D = q.shape[3]
+    s = np.zeros(D, dtype=np.float32)
+    for i in range(q.shape[1]):
+        for j in range(G):
+            s = s + decode_f32(q[b, i, g * G + j], dtype)
+    return s
+
+
+def topk_blocks_shared(q, k_pages, block_table, ctx_lens, bs, k, dtype, means=None):
+    """sel [B, T, Hq, k] int32: one selection per (b, KV group), repeated for
+    each of the group's rows."""
+    B, T, Hq, D = q.shape
+    Hkv = k_pages.shape[1]
+    G = Hq // Hkv
+    if means is None:
+        means = block_means(k_pages, block_table, ctx_lens, bs, dtype)
+    sel = np.full((B, T, Hq, k), -1, dtype=np.int32)
+    for b in range(B):
+        nb = (int(ctx_lens[b]) + bs - 1) // bs
+        if nb == 0:
+            continue
+        for g in range(Hkv):
+            sc = block_scores(pooled_query(q, b, g, G, dtype), means[b, :nb, g])
+            sel[b, :, g * G:(g + 1) * G] = select(sc, k)
     return sel

@@ -168,3 +168,62 @@ def test_append_block_sums_equals_rebuild(ctx0, L):
     want = oracle.block_sums(kp, table, ctx_new, bs, "f32")
     live = ~np.isnan(want)
     assert np.array_equal(got[live].view(np.uint32), want[live].view(np.uint32))
+
+
+def test_shared_selection_exact_integers_brute_force():
+    """Shared selection: with exact integer arithmetic the score is the sum
+    of the group's per-row dot products; the selection equals a full sort of
+    that exact sum, and every row of a group holds the same list."""
+    rng = np.random.default_rng(11)
+    bs = 4
+    q, kp, table, ctx, Kd = _int_case(rng, bs=bs)
+    G = 2
+    for k in (1, 2, 4, 5, 9):
+        sel = oracle.topk_blocks_shared(q, kp, table, ctx, bs, k, "f32")
+        for b in range(2):
+            nb = (ctx[b] + bs - 1) // bs
+            for g in range(2):
+                exact = []
+                for n in range(nb):
+                    lo, hi = n * bs, min(ctx[b], (n + 1) * bs)
+                    mean = [sum(int(Kd[b, g, t, d]) for t in range(lo, hi)) // (hi - lo) for d in range(16)]
+                    tot = sum(int(q[b, i, g * G + j, d]) * mean[d]
+                              for i in range(3) for j in range(G) for d in range(16))
+                    exact.append((-tot, n))
+                best = sorted(n for _, n in sorted(exact)[:k])
+                want = best + [-1] * (k - len(best))
+                for i in range(3):
+                    for j in range(G):
+                        assert list(sel[b, i, g * G + j]) == want
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_shared_selection_reduces_to_per_row(dtype):
+    """One query row per KV group (T = 1, Hq = Hkv): the shared selection is
+    the per-row selection.  With every other row of a group zero, it is the
+    one nonzero row's selection (adding +0 leaves a float32 sum unchanged)."""
+    rng = np.random.default_rng(12)
+    B, Hkv, D, bs = 2, 3, 32, 8
+    ctx = (70, 45)
+    Kd = rng.standard_normal((B, Hkv, max(ctx) + 4, D)).astype(np.float32)
+    kp, _, table = paged_from_dense(Kd, np.zeros_like(Kd), bs, rng)
+    if dtype == "bf16":
+        kp = f32_to_bf16_bits(kp)
+    ctx = np.array(ctx, np.int32)
+    q1 = rng.standard_normal((B, 1, Hkv, D)).astype(np.float32)
+    if dtype == "bf16":
+        q1 = f32_to_bf16_bits(q1)
+    for k in (1, 3, 6):
+        assert np.array_equal(oracle.topk_blocks_shared(q1, kp, table, ctx, bs, k, dtype),
+                              oracle.topk_blocks(q1, kp, table, ctx, bs, k, dtype))
+    # T = 4, G = 2: only node 2, head 1 of each group is nonzero
+    q = np.zeros((B, 4, 2 * Hkv, D), np.float32)
+    q[:, 2, 1::2] = rng.standard_normal((B, Hkv, D))
+    if dtype == "bf16":
+        q = f32_to_bf16_bits(q)
+    per_row = oracle.topk_blocks(q, kp, table, ctx, bs, 5, dtype)
+    shared = oracle.topk_blocks_shared(q, kp, table, ctx, bs, 5, dtype)
+    for g in range(Hkv):
+        for i in range(4):
+            for j in range(2):
+                assert np.array_equal(shared[:, i, 2 * g + j], per_row[:, 2, 2 * g + 1])
