@@ -60,6 +60,9 @@ def parse():
     ap.add_argument("--kv-copies", type=int, default=2,
                     help="K/V page copies, used by consecutive steps in turn")
     ap.add_argument("--workload", default="llama3_8b_tree64")
+    ap.add_argument("--shared-selection", action="store_true",
+                    help="sparse workload: one block selection per (sequence, KV group) "
+                         "(sd_topk_blocks_shared) instead of one per query row")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="approximate CPU time budget of the oracle sample")
@@ -258,7 +261,7 @@ class HipEvent:
 
 
 class Workload:
-    def __init__(self, name, kv_copies=1):
+    def __init__(self, name, kv_copies=1, shared=False):
         import torch
         import tree_verification_amd as tva
         from synth import CONFIGS, make_inputs
@@ -288,6 +291,7 @@ class Workload:
         self.bonus = torch.empty(B, dtype=torch.int32, device="cuda")
         self.sel = None
         self.sums = None
+        self.shared = shared
         if cfg.topk:
             self.sel = torch.empty((B, T, cfg.Hq, cfg.topk), dtype=torch.int32, device="cuda")
             # kept block key sums for the starting lengths: a commit writes only
@@ -309,7 +313,9 @@ class Workload:
             ctx = self.ctx
         self.k, self.v = self.kvs[self.n_steps % len(self.kvs)]
         self.n_steps += 1
-        if self.sel is not None:
+        if self.sel is not None and self.shared:
+            tva.topk_blocks_shared(self.q, self.k, self.table, ctx, self.cfg.topk, sums=self.sums, sel=self.sel)
+        elif self.sel is not None:
             tva.topk_blocks_cached(self.q, self.sums, self.k, self.table, ctx, self.cfg.topk, sel=self.sel)
         if ev is not None:
             ev[0].record()
@@ -358,6 +364,13 @@ def time_calls(w, reps=10):
         res["topk_cached_us"] = loop(lambda: tva.topk_blocks_cached(w.q, w.sums, w.k, w.table, w.ctx,
                                                                     w.cfg.topk, sel=w.sel))
         res["topk_from_k_us"] = loop(lambda: tva.topk_blocks(w.q, w.k, w.table, w.ctx, w.cfg.topk, sel=w.sel))
+        res["topk_shared_cached_us"] = loop(lambda: tva.topk_blocks_shared(w.q, w.k, w.table, w.ctx, w.cfg.topk,
+                                                                           sums=w.sums, sel=w.sel))
+        # leave the selection the step uses in place
+        if w.shared:
+            tva.topk_blocks_shared(w.q, w.k, w.table, w.ctx, w.cfg.topk, sums=w.sums, sel=w.sel)
+        else:
+            tva.topk_blocks_cached(w.q, w.sums, w.k, w.table, w.ctx, w.cfg.topk, sel=w.sel)
         scratch = w.sums.clone()
         n_new = torch.full_like(w.ctx, 5)
         ctx_new = w.ctx + n_new
@@ -509,10 +522,26 @@ def sweep(kind):
                 t_a = _median_us(torch, f_a)
             except tva.SdError:
                 t_a = None          # selections wider than sparse attention accepts
+            # one selection per (sequence, KV group)
+            f_s = lambda: tva.topk_blocks_shared(d["q"], d["k"], d["table"], d["ctx"], k, sums=sums)
+            t_s = _median_us(torch, f_s)
+            sel_s = f_s()
+            torch.cuda.synchronize()
+            bytes_s, _ = attention_cost(base, x, sel_s.cpu().numpy())
+            f_as = lambda: tva.tree_verify_attn(d["q"], d["k"], d["v"], d["table"], d["ctx"], d["parent"],
+                                                sel_blocks=sel_s)
+            try:
+                t_as = _median_us(torch, f_as)
+            except tva.SdError:
+                t_as = None
             line = {"sweep": "topk", "k": k, "topk_from_k_us": round(t_k, 1), "topk_cached_us": round(t_c, 1),
                     "sparse_attention_us": None if t_a is None else round(t_a, 1),
                     "selected_bytes": int(bytes_),
-                    "sparse_attention_tb_s": None if t_a is None else round(bytes_ / t_a / 1e6, 3)}
+                    "sparse_attention_tb_s": None if t_a is None else round(bytes_ / t_a / 1e6, 3),
+                    "topk_shared_us": round(t_s, 1),
+                    "shared_sparse_attention_us": None if t_as is None else round(t_as, 1),
+                    "shared_selected_bytes": int(bytes_s),
+                    "shared_sparse_attention_tb_s": None if t_as is None else round(bytes_s / t_as / 1e6, 3)}
             print(json.dumps(line), flush=True)
 
 
@@ -533,7 +562,7 @@ def main():
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
-    w = Workload(args.workload, max(1, args.kv_copies))
+    w = Workload(args.workload, max(1, args.kv_copies), shared=args.shared_selection)
     cfg = w.cfg
     settle_steps = 0
     t_end = time.perf_counter() + args.settle_ms * 1e-3
@@ -565,7 +594,8 @@ def main():
     sel_np = None if w.sel is None else w.sel.cpu().numpy()
     bytes_, flops = attention_cost(cfg, w.x, sel_np)
     roof = roofline_for(cfg, bytes_, flops, attn_s)
-    roof["traffic"] = traffic_for("attn", cfg.name)
+    # the committed counter figures are for the per-row selection
+    roof["traffic"] = None if w.shared else traffic_for("attn", cfg.name)
     calls = time_calls(w)
 
     secondary = None
@@ -598,6 +628,8 @@ def main():
         "config": {"workload": cfg.name, "B": cfg.B, "T": cfg.T, "Hq": cfg.Hq, "Hkv": cfg.Hkv,
                    "D": cfg.D, "ctx": [cfg.ctx_lo, cfg.ctx_hi], "block": cfg.bs, "V": cfg.V,
                    "accept": cfg.mode, "temperature": w.tau, "topk": cfg.topk or None,
+                   "selection": (("shared per KV group" if w.shared else "per query row")
+                                 if cfg.topk else None),
                    "kv_copies": len(w.kvs)},
         "roofline": dict(roof, kernel="sd_tree_verify_attn (tree-masked attention kernel)",
                          attention_us=round(attn_s * 1e6, 2), timed_calls=len(evs),

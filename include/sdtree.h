@@ -239,6 +239,24 @@ sd_status sd_topk_blocks_cached(const sd_shape* shape, const void* q, const floa
                                 int32_t* sel_blocks, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * One selection per (sequence, KV group), reused by every tree node and every
+ * query head of the group (sparse-verification page, "Methodology": reuse
+ * across draft tokens).  The group's score of block n is the sum of its rows'
+ * scores, formed as (pooled query) . mean: the pooled query is the float32
+ * sum from +0 of q[b, i, g*G + j] over i, then j, sequentially; the mean,
+ * the dot product and the order are those of sd_topk_blocks.  Means come
+ * from block_sums when it is not NULL (as sd_topk_blocks_cached; k_pages is
+ * then not read), else from K.
+ *   sel_blocks  int32 [B, T, Hq, k]: each group's list in all its rows, so
+ *               sparse attention reads k blocks per (sequence, KV head).
+ *   ws          >= sd_workspace_bytes(SD_CALL_TOPK, shape, k).
+ */
+sd_status sd_topk_blocks_shared(const sd_shape* shape, const void* q, const void* k_pages,
+                                const float* block_sums, const int32_t* block_table,
+                                const int32_t* ctx_lens, int32_t k, int32_t* sel_blocks, void* ws,
+                                size_t ws_bytes, void* stream);
+
+/*
  * One batched expansion step of the draft-tree search (SpecExec page,
  * "Approach": the draft tree is grown from the continuations of highest
  * cumulative probability by a batched shortest-path search with the draft

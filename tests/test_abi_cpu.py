@@ -17,7 +17,7 @@ def setup_module():
 
 def test_exports_every_declared_function():
     names = _lib.declared_functions()
-    assert len(names) == 12
+    assert len(names) == 13
     for n in names:
         assert hasattr(L, n), n
 
@@ -126,6 +126,10 @@ def test_block_sums_calls_reject_bad_arguments():
     assert L.sd_topk_blocks_cached(ctypes.byref(s), FAKE, None, FAKE, FAKE, 4, FAKE, FAKE, big, None) == 1
     assert L.sd_topk_blocks_cached(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, 0, FAKE, FAKE, big, None) == 1
     assert L.sd_topk_blocks_cached(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, 4, FAKE, FAKE, 10, None) == 5
+    # shared selection: neither K nor sums, k < 1, workspace too small
+    assert L.sd_topk_blocks_shared(ctypes.byref(s), FAKE, None, None, FAKE, FAKE, 4, FAKE, FAKE, big, None) == 1
+    assert L.sd_topk_blocks_shared(ctypes.byref(s), FAKE, FAKE, None, FAKE, FAKE, 0, FAKE, FAKE, big, None) == 1
+    assert L.sd_topk_blocks_shared(ctypes.byref(s), FAKE, None, FAKE, FAKE, FAKE, 4, FAKE, FAKE, 10, None) == 5
     assert L.sd_workspace_bytes(5, ctypes.byref(s), 0) > 0
 
 

@@ -73,6 +73,7 @@ def lib():
                              ctypes.c_float, _P, _P, _P, _P, _P, _P, _P, _P, sz, _P],
         "sd_topk_blocks": [ctypes.POINTER(SdShape), _P, _P, _P, _P, i32, _P, _P, sz, _P],
         "sd_topk_blocks_cached": [ctypes.POINTER(SdShape), _P, _P, _P, _P, i32, _P, _P, sz, _P],
+        "sd_topk_blocks_shared": [ctypes.POINTER(SdShape), _P, _P, _P, _P, _P, i32, _P, _P, sz, _P],
         "sd_block_sums": [ctypes.POINTER(SdShape), _P, _P, _P, _P, _P, sz, _P],
         "sd_tree_expand": [ctypes.POINTER(SdExpandShape), _P, _P, ctypes.c_float, i32, _P, _P, _P, _P, sz,
                            _P],
@@ -297,6 +298,23 @@ def topk_blocks_cached(q, sums, k_pages_like, block_table, ctx_lens, k, sel=None
     _check("sd_topk_blocks_cached", lib().sd_topk_blocks_cached(
         ctypes.byref(shape), _ptr(q), _ptr(sums), _ptr(block_table), _ptr(ctx_lens), int(k),
         _ptr(sel), _ptr(ws), ws.numel(), _stream(q.device)))
+    return sel
+
+
+def topk_blocks_shared(q, k_pages, block_table, ctx_lens, k, sums=None, sel=None, ws=None):
+    """sd_topk_blocks_shared: one selection per (sequence, KV group), written
+    to all the group's rows; means from the kept `sums` when given (K is then
+    not read), else from `k_pages`."""
+    B, T, Hq, D = q.shape
+    parent_like = torch.empty((1, T))
+    shape = make_shape(q, k_pages, block_table, parent_like)
+    if sel is None:
+        sel = torch.empty((B, T, Hq, k), dtype=torch.int32, device=q.device)
+    need = workspace_bytes(SD_CALL_TOPK, shape, k)
+    ws = _WS.get(q.device, need, SD_CALL_TOPK) if ws is None else ws
+    _check("sd_topk_blocks_shared", lib().sd_topk_blocks_shared(
+        ctypes.byref(shape), _ptr(q), _ptr(k_pages), None if sums is None else _ptr(sums),
+        _ptr(block_table), _ptr(ctx_lens), int(k), _ptr(sel), _ptr(ws), ws.numel(), _stream(q.device)))
     return sel
 
 

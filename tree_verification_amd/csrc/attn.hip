@@ -382,13 +382,22 @@ __global__ void __launch_bounds__(WQ * WK * 64) attn_mfma_kernel(AttnArgs a) {
       }
     }
     __syncthreads();
-    if (tid == 0) {
-      int acc = 0;
-      for (int w = 0; w < BW; ++w) {
-        upre[w] = acc;
-        acc += __popc(ubits[w]);
+    // exclusive prefix of the words' bit counts: wavefront 0, 64 words a step
+    if (tid < 64) {
+      int carry = 0;
+      for (int w0 = 0; w0 < BW; w0 += 64) {
+        const int w = w0 + tid;
+        const int c = w < BW ? __popc(ubits[w]) : 0;
+        int x = c;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const int y = __shfl_up(x, off);
+          if (tid >= off) x += y;
+        }
+        if (w < BW) upre[w] = carry + x - c;
+        carry += __shfl(x, 63);
       }
-      s_nU = acc;
+      if (tid == 0) s_nU = carry;
     }
     __syncthreads();
     nU = s_nU;
@@ -398,16 +407,18 @@ __global__ void __launch_bounds__(WQ * WK * 64) attn_mfma_kernel(AttnArgs a) {
       while (bits) {
         const int bpos = __ffs(bits) - 1;
         bits &= bits - 1;
-        const int n = w * 32 + bpos;
-        int phys = table[n];
-        if (phys < 0 || phys >= a.num_blocks) {
-          err |= SD_ERR_BLOCK;
-          phys = 0;
-        }
-        U[o] = n;
-        Uphys[o] = phys;
-        ++o;
+        U[o++] = w * 32 + bpos;
       }
+    }
+    __syncthreads();
+    // physical ids of the union's blocks, all loads in flight together
+    for (int o = tid; o < nU; o += NT) {
+      int phys = table[U[o]];
+      if (phys < 0 || phys >= a.num_blocks) {
+        err |= SD_ERR_BLOCK;
+        phys = 0;
+      }
+      Uphys[o] = phys;
     }
     if (cap_ok) {
       for (int idx = tid; idx < nsel; idx += NT) {

@@ -153,6 +153,8 @@ struct TopkArgs {
   float* means;    // [B][nbmax][Hkv][D]
   float* scores;   // [B*T*Hq][nbmax]
   float* sums;     // kept block key sums [num_blocks][Hkv][D] (cached selection)
+  int32_t* rep;    // shared selection: each (b, group) list goes to all the group's rows
+  int rep_T, rep_Hq, rep_G;
   uint32_t* status;
   int B, T, Hq, Hkv, G, D, bs, max_blocks, num_blocks, topk, nbmax;
 };
@@ -182,6 +184,7 @@ hipError_t launch_attn_mfma(const AttnArgs& a, const AttnPlan& p, hipStream_t st
 hipError_t launch_accept(const AcceptArgs& a, hipStream_t st);
 hipError_t launch_commit(const CommitArgs& a, hipStream_t st);
 hipError_t launch_topk(const TopkArgs& a, bool f32, bool cached, hipStream_t st);
+hipError_t launch_topk_shared(const TopkArgs& a, bool f32, bool cached, hipStream_t st);
 hipError_t launch_block_sums(const TopkArgs& a, bool f32, hipStream_t st);
 hipError_t launch_block_sums_append(const TopkArgs& a, const int32_t* n_new, bool f32, hipStream_t st);
 

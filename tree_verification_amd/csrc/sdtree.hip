@@ -386,11 +386,12 @@ static TopkArgs topk_args(const sd_shape* shape, const int32_t* block_table, con
   return a;
 }
 
-// Top-k from K (block_sums == nullptr) or from kept block sums.
+// Top-k from K (block_sums == nullptr) or from kept block sums, per query
+// row or shared by each KV group's rows.
 static sd_status topk_common(const sd_shape* shape, const void* q, const void* k_pages,
                              const float* block_sums, const int32_t* block_table,
                              const int32_t* ctx_lens, int32_t k, int32_t* sel_blocks, void* ws,
-                             size_t ws_bytes, void* stream) {
+                             size_t ws_bytes, void* stream, bool shared = false) {
   sd_status st = check_shape(shape);
   if (st != SD_OK) return st;
   if (!q || (!k_pages && !block_sums) || !block_table || !ctx_lens || !sel_blocks || !ws)
@@ -405,8 +406,9 @@ static sd_status topk_common(const sd_shape* shape, const void* q, const void* k
   a.sums = const_cast<float*>(block_sums);
   a.means = reinterpret_cast<float*>(w + mo);
   a.scores = reinterpret_cast<float*>(w + so);
-  return hip_status(launch_topk(a, shape->dtype == SD_F32, block_sums != nullptr,
-                                static_cast<hipStream_t>(stream)));
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  const bool f32 = shape->dtype == SD_F32, cached = block_sums != nullptr;
+  return hip_status(shared ? launch_topk_shared(a, f32, cached, hs) : launch_topk(a, f32, cached, hs));
 }
 
 sd_status sd_topk_blocks(const sd_shape* shape, const void* q, const void* k_pages,
@@ -423,6 +425,15 @@ sd_status sd_topk_blocks_cached(const sd_shape* shape, const void* q, const floa
   if (!block_sums) return SD_INVALID_ARG;
   return topk_common(shape, q, nullptr, block_sums, block_table, ctx_lens, k, sel_blocks, ws,
                      ws_bytes, stream);
+}
+
+sd_status sd_topk_blocks_shared(const sd_shape* shape, const void* q, const void* k_pages,
+                                const float* block_sums, const int32_t* block_table,
+                                const int32_t* ctx_lens, int32_t k, int32_t* sel_blocks, void* ws,
+                                size_t ws_bytes, void* stream) {
+  if (!k_pages && !block_sums) return SD_INVALID_ARG;
+  return topk_common(shape, q, block_sums ? nullptr : k_pages, block_sums, block_table, ctx_lens, k,
+                     sel_blocks, ws, ws_bytes, stream, true);
 }
 
 sd_status sd_block_sums(const sd_shape* shape, const void* k_pages, const int32_t* block_table,

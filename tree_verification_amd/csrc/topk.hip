@@ -15,6 +15,10 @@
 // block: built once from K, extended in position order by the positions each
 // commit appends (block_sums_append_kernel), and divided at selection time,
 // so its means are the same float32 values without reading K.
+// Shared selection (one list per sequence and KV group, reused by all the
+// group's nodes and heads) scores each block against the group's pooled
+// query, the sequential float32 sum of its rows (group_score_kernel), and
+// selects with one workgroup per list (group_select_kernel).
 #include "common.h"
 
 #pragma clang fp contract(off)
@@ -365,6 +369,251 @@ __global__ void __launch_bounds__(256) block_select_kernel(TopkArgs a) {
   for (int e = sel_before + lane; e < a.topk; e += 64) out[e] = -1;
 }
 
+// Shared selection, scores: one workgroup per (64 blocks, KV group,
+// sequence).  The workgroup first forms the group's pooled query -- the
+// sequential float32 sum from +0 of its T * G rows, node by node and head by
+// head -- staging 32 rows at a time in LDS, one thread per dim.  Each block's
+// mean is then read (MEANS) or formed from the kept sum with one IEEE
+// division (SUMS), and scored against the pooled query with the products and
+// halving tree of block_score_kernel (same lane layout, same pairs).  A block
+// id out of range scores with a zero mean and sets the block bit, as in
+// block_mean_kernel.
+template <typename E, int D, bool SUMS>
+__global__ void __launch_bounds__(256) group_score_kernel(TopkArgs a) {
+#pragma clang fp contract(off)
+  constexpr int EL = D / 16;
+  constexpr int NBC = 64;
+  constexpr int RS = 32;                                  // rows per LDS stage
+  constexpr int CPR = D * (int)sizeof(E) / 16;            // 16-byte chunks per row
+  constexpr int CPT = RS * CPR / 256;                     // chunks per thread per stage
+  static_assert(CPT * 256 == RS * CPR, "stage split");
+  __shared__ __align__(16) uint4 stage[RS * CPR];
+  __shared__ __align__(16) float qs[D];                   // [lane d'][e] = pooled[d' + 16 e]
+  const int chunk = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int ctx = a.ctx[b];
+  if (ctx < 0 || (long long)ctx > (long long)a.max_blocks * a.bs) {
+    if (SUMS && chunk == 0 && g == 0 && tid == 0) set_status(a.status, SD_ERR_CAPACITY);
+    return;
+  }
+  const int nblk = (ctx + a.bs - 1) / a.bs;
+  const int n0 = chunk * NBC;
+  if (n0 >= nblk) return;
+  const int nbc = min(NBC, nblk - n0);
+  const int grp = tid >> 4, dl = tid & 15;
+  constexpr int NBG = NBC / 16;
+  float m[NBG][EL];
+  bool bad[NBG];
+  if constexpr (SUMS) {
+    // block ids, then every sum load issued before the pooled query's loads;
+    // the means are formed after it
+    int blk[NBG];
+#pragma unroll
+    for (int j = 0; j < NBG; ++j) blk[j] = a.table[(size_t)b * a.max_blocks + n0 + min(grp + 16 * j, nbc - 1)];
+#pragma unroll
+    for (int j = 0; j < NBG; ++j) {
+      bad[j] = blk[j] < 0 || blk[j] >= a.num_blocks;
+      const float* srow = a.sums + ((size_t)(bad[j] ? 0 : blk[j]) * a.Hkv + g) * D + dl;
+#pragma unroll
+      for (int e = 0; e < EL; ++e) m[j][e] = srow[16 * e];
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < NBG; ++j) {
+      const float* mrow = a.means + (((size_t)b * a.nbmax + n0 + min(grp + 16 * j, nbc - 1)) * a.Hkv + g) * D;
+#pragma unroll
+      for (int e = 0; e < EL; ++e) m[j][e] = mrow[dl + 16 * e];
+    }
+  }
+  // pooled query
+  const int R = a.T * a.G;
+  float acc = 0.f;
+  for (int r0 = 0; r0 < R; r0 += RS) {
+    const int rc = min(RS, R - r0);
+    uint4 v[CPT];
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int idx = tid + 256 * c, rr = min(idx / CPR, rc - 1), col = idx % CPR;
+      const int r = r0 + rr, i = r / a.G, h = g * a.G + r % a.G;
+      v[c] = reinterpret_cast<const uint4*>(reinterpret_cast<const E*>(a.q) +
+                                            (((size_t)b * a.T + i) * a.Hq + h) * D)[col];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) stage[tid + 256 * c] = v[c];
+    __syncthreads();
+    if (tid < D) {
+      const E* st = reinterpret_cast<const E*>(stage);
+      for (int rr = 0; rr < rc; ++rr) {
+        const E x = st[rr * D + tid];
+        if constexpr (sizeof(E) == 2) acc = acc + bf16_to_f32((bf16_bits)x);
+        else acc = acc + x;
+      }
+    }
+  }
+  if (tid < D) qs[(tid % 16) * EL + tid / 16] = acc;
+  __syncthreads();
+  float q[EL];
+#pragma unroll
+  for (int e = 0; e < EL; ++e) q[e] = qs[dl * EL + e];
+  if constexpr (SUMS) {
+#pragma unroll
+    for (int j = 0; j < NBG; ++j) {
+      const int n = n0 + min(grp + 16 * j, nbc - 1);
+      if (bad[j] && dl == 0 && grp + 16 * j < nbc) set_status(a.status, SD_ERR_BLOCK);
+      const float fv = (float)min(a.bs, ctx - n * a.bs);
+#pragma unroll
+      for (int e = 0; e < EL; ++e) m[j][e] = bad[j] ? 0.f : __fdiv_rn(m[j][e], fv);
+    }
+  }
+  float sc[NBG];
+#pragma unroll
+  for (int j = 0; j < NBG; ++j) {
+    float v[EL];
+#pragma unroll
+    for (int e = 0; e < EL; ++e) v[e] = q[e] * m[j][e];
+#pragma unroll
+    for (int hw = EL / 2; hw >= 1; hw >>= 1)
+#pragma unroll
+      for (int e = 0; e < hw; ++e) v[e] = v[e] + v[e + hw];
+    sc[j] = v[0];
+  }
+#pragma unroll
+  for (int n = 8; n >= 1; n >>= 1)
+#pragma unroll
+    for (int j = 0; j < NBG; ++j) sc[j] = row_ror_add(sc[j], n);
+  if (dl == 0)
+#pragma unroll
+    for (int j = 0; j < NBG; ++j)
+      if (grp + 16 * j < nbc) a.scores[((size_t)b * a.Hkv + g) * a.nbmax + n0 + grp + 16 * j] = sc[j];
+}
+
+// Shared selection, select: one workgroup per (sequence, KV group).  The
+// same radix select as block_select_kernel, spread over four wavefronts (one
+// histogram copy each, bins scanned by all 256 threads), then an ordered
+// block-wide compaction.  The list is gathered in LDS and written to every
+// row of the group by all threads.
+constexpr int kGroupStage = 8192;   // scores staged in LDS (longer rows read global memory)
+constexpr int kGroupList = 4096;    // longer lists are written to the rows as they are found
+
+__global__ void __launch_bounds__(256) group_select_kernel(TopkArgs a) {
+  __shared__ uint32_t keys[kGroupStage];
+  __shared__ int32_t slist[kGroupList];
+  __shared__ uint32_t hist[4][256];
+  __shared__ uint32_t wtot[4], ceq[4], csel[4];
+  __shared__ int s_d;
+  __shared__ uint32_t s_ab;
+  const int row = blockIdx.x, b = row / a.Hkv, g = row % a.Hkv;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ctx = a.ctx[b];
+  const bool ok = ctx >= 0 && (long long)ctx <= (long long)a.max_blocks * a.bs;
+  const int nb = ok ? (ctx + a.bs - 1) / a.bs : 0;
+  const int R = a.rep_T * a.rep_G;
+  auto row_ptr = [&](int r) -> int32_t* {
+    const int i = r / a.rep_G, j = r % a.rep_G;
+    return a.rep + (((size_t)b * a.rep_T + i) * a.rep_Hq + (size_t)g * a.rep_G + j) * a.topk;
+  };
+  if (nb <= a.topk) {
+    for (long long idx = tid; idx < (long long)R * a.topk; idx += 256) {
+      const int r = (int)(idx / a.topk), e = (int)(idx % a.topk);
+      row_ptr(r)[e] = e < nb ? e : -1;
+    }
+    return;
+  }
+  const float* sc = a.scores + (size_t)row * a.nbmax;
+  const bool staged = nb <= kGroupStage;
+  if (staged) {
+    for (int y0 = 0; y0 < nb; y0 += 256 * 8) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int y = y0 + tid + 256 * u;
+        v[u] = sc[y < nb ? y : 0];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int y = y0 + tid + 256 * u;
+        if (y < nb) keys[y] = score_key(v[u]);
+      }
+    }
+  }
+  __syncthreads();
+  auto key_of = [&](int y) -> uint32_t { return staged ? keys[y] : score_key(sc[y]); };
+  uint32_t prefix = 0, mask = 0, krem = (uint32_t)a.topk;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    hist[wave][lane] = 0u; hist[wave][lane + 64] = 0u; hist[wave][lane + 128] = 0u; hist[wave][lane + 192] = 0u;
+    __syncthreads();
+    for (int y = tid; y < nb; y += 256) {
+      const uint32_t u = key_of(y);
+      if ((u & mask) == prefix) atomicAdd(&hist[wave][(u >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    // thread t owns bin t; x = keys in bins t .. (wave end), then wave totals
+    const uint32_t c = hist[0][tid] + hist[1][tid] + hist[2][tid] + hist[3][tid];
+    uint32_t x = c;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint32_t y = __shfl_down(x, off);
+      if (lane + off < 64) x += y;
+    }
+    if (lane == 0) wtot[wave] = x;
+    __syncthreads();
+    uint32_t above = x - c;
+    for (int w = wave + 1; w < 4; ++w) above += wtot[w];
+    if (above < krem && above + c >= krem) {
+      s_d = tid;
+      s_ab = above;
+    }
+    __syncthreads();
+    prefix |= (uint32_t)s_d << shift;
+    mask |= 255u << shift;
+    krem -= s_ab;
+    __syncthreads();
+  }
+  // every key above prefix, and the first krem keys equal to it, lowest block first
+  const bool gather = a.topk <= kGroupList;
+  const unsigned long long below = (1ull << lane) - 1ull;
+  int eq_base = 0, sel_base = 0;
+  for (int base = 0; base < nb; base += 256) {
+    const int y = base + tid;
+    const uint32_t u = y < nb ? key_of(y) : 0u;
+    const bool eq = y < nb && u == prefix;
+    const unsigned long long beq = __ballot(eq);
+    if (lane == 0) ceq[wave] = (uint32_t)__popcll(beq);
+    __syncthreads();
+    int eq_rank = eq_base + __popcll(beq & below);
+    for (int w = 0; w < wave; ++w) eq_rank += (int)ceq[w];
+    const bool take = y < nb && (u > prefix || (eq && eq_rank < (int)krem));
+    const unsigned long long bsel = __ballot(take);
+    if (lane == 0) csel[wave] = (uint32_t)__popcll(bsel);
+    __syncthreads();
+    int pos = sel_base + __popcll(bsel & below);
+    for (int w = 0; w < wave; ++w) pos += (int)csel[w];
+    if (take && pos < a.topk) {
+      if (gather) slist[pos] = y;
+      else
+        for (int r = 0; r < R; ++r) row_ptr(r)[pos] = y;
+    }
+    for (int w = 0; w < 4; ++w) {
+      eq_base += (int)ceq[w];
+      sel_base += (int)csel[w];
+    }
+    __syncthreads();
+  }
+  const int nsel = min(sel_base, a.topk);
+  if (gather) {
+    for (long long idx = tid; idx < (long long)R * a.topk; idx += 256) {
+      const int r = (int)(idx / a.topk), e = (int)(idx % a.topk);
+      row_ptr(r)[e] = e < nsel ? slist[e] : -1;
+    }
+  } else {
+    for (long long idx = tid; idx < (long long)R * (a.topk - nsel); idx += 256) {
+      const int r = (int)(idx / (a.topk - nsel)), e = nsel + (int)(idx % (a.topk - nsel));
+      row_ptr(r)[e] = -1;
+    }
+  }
+}
+
 // Kept block sums after a commit: the positions [ctx_b - n_b, ctx_b) it
 // appended (ctx_lens after the commit, n_b = path_len[b]) are added, in
 // position order, to their blocks' sums; a block whose first position is
@@ -458,6 +707,34 @@ static hipError_t launch_topk_t(const TopkArgs& a, bool cached, hipStream_t st) 
   const long long rows = (long long)a.B * a.T * a.Hq;
   hipLaunchKernelGGL(block_select_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, a);
   return hipGetLastError();
+}
+
+// Shared selection: block means from K first when there are no kept sums,
+// then the group scores and the group select.
+template <typename E, int D>
+static hipError_t launch_topk_shared_t(const TopkArgs& a, bool cached, hipStream_t st) {
+  hipError_t e = hipSuccess;
+  const dim3 grid((a.nbmax + 63) / 64, a.Hkv, a.B);
+  if (cached) {
+    hipLaunchKernelGGL((group_score_kernel<E, D, true>), grid, dim3(256), 0, st, a);
+  } else {
+    e = launch_means<E, D, kMeansFromK>(a, st);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((group_score_kernel<E, D, false>), grid, dim3(256), 0, st, a);
+  }
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  TopkArgs p = a;
+  p.rep = a.sel; p.rep_T = a.T; p.rep_Hq = a.Hq; p.rep_G = a.G;
+  hipLaunchKernelGGL(group_select_kernel, dim3((unsigned)(a.B * a.Hkv)), dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_shared(const TopkArgs& a, bool f32, bool cached, hipStream_t st) {
+  if (f32)
+    return a.D == 64 ? launch_topk_shared_t<float, 64>(a, cached, st) : launch_topk_shared_t<float, 128>(a, cached, st);
+  return a.D == 64 ? launch_topk_shared_t<bf16_bits, 64>(a, cached, st)
+                   : launch_topk_shared_t<bf16_bits, 128>(a, cached, st);
 }
 
 hipError_t launch_topk(const TopkArgs& a, bool f32, bool cached, hipStream_t st) {
