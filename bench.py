@@ -71,13 +71,16 @@ def parse():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after the run, copy MIB MiB device-to-device 3 times (a plain copy "
                          "kernel of known size that scales the HBM byte counters)")
-    ap.add_argument("--sweep", choices=["tree", "topk", "expand"],
+    ap.add_argument("--sweep", choices=["tree", "topk", "expand", "calib"],
                     help="no bench line: one JSON line per point of a sweep instead.  tree: the "
                          "attention of the 8B-like shape (B 16, 32/8 heads, ctx 4096) over tree "
                          "sizes T = 1 .. 4096, across the HBM / MFMA crossover; topk: the block "
                          "selection of the 4 x 64K workload over k, from K and from kept sums; "
                          "expand: one draft-tree expansion step (sd_tree_expand) over batch "
-                         "sizes, vocabulary 32000, k 2048, with the oracle timed beside it")
+                         "sizes, vocabulary 32000, k 2048, with the oracle timed beside it; "
+                         "calib: the drafter's recalibration pass (chain attention over a "
+                         "32/8-head, D 64 cache of 16 x 4096, then the identity-path commit) "
+                         "over chain lengths T = 1 .. 32")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="no run: turn the counter_collection.csv files of a rocprofv3 "
                          "--pmc FETCH_SIZE pass and a --pmc WRITE_SIZE pass (both of a run "
@@ -478,6 +481,32 @@ def sweep(kind):
                     "hbm_tb_s": round(bytes_ / t / 1e12, 3), "mfma_tflop_s": round(flops / t / 1e12, 1),
                     "roofline": roofline_for(c, bytes_, flops, t),
                     "verified_tree_tokens_per_s": round(c.B * T / t, 1)}
+            print(json.dumps(line), flush=True)
+            del d, x
+    elif kind == "calib":
+        # the drafter's recalibration pass: chain attention over its cache
+        # (32/8 heads, D 64, 16 x 4096 context), then the identity-path commit
+        base = dataclasses.replace(CONFIGS["llama3_8b_tree64"], Hq=32, Hkv=8, D=64, tree="chain",
+                                   max_parent_depth=0, max_children=0, V=16)
+        for T in (1, 2, 4, 8, 16, 32):
+            c = dataclasses.replace(base, T=T)
+            x = make_inputs(c)
+            d = to_device(x)
+            path = torch.arange(T, dtype=torch.int32, device="cuda").repeat(c.B, 1).contiguous()
+            plen = torch.full((c.B,), T, dtype=torch.int32, device="cuda")
+            ctx0 = d["ctx"].clone()
+            f = lambda: tva.tree_verify_attn(d["q"], d["k"], d["v"], d["table"], d["ctx"], d["parent"])
+
+            def g():
+                tva.kv_commit(d["k"], d["v"], d["table"], d["ctx"], path, plen)
+                d["ctx"].copy_(ctx0)
+            settle(f)
+            t = _median_us(torch, f) * 1e-6
+            t_c = _median_us(torch, g)
+            bytes_, flops = attention_cost(c, x)
+            line = {"sweep": "calib", "T": T, "attention_us": round(t * 1e6, 1),
+                    "commit_plus_restore_us": round(t_c, 1), "hbm_tb_s": round(bytes_ / t / 1e12, 3),
+                    "attention_bytes": int(bytes_), "recalibrated_tokens_per_s": round(c.B * T / t, 1)}
             print(json.dumps(line), flush=True)
             del d, x
     elif kind == "expand":
