@@ -268,7 +268,8 @@ sd_status sd_topk_blocks_shared(const sd_shape* shape, const void* q, const void
  *   out_row int32 [k] (index of e), out_token int32 [k], out_score float32 [k].
  * 1 <= k <= min(4096, E * V); temperature > 0; E * V < 2^32 - 1.
  * ws >= sd_workspace_bytes(SD_CALL_EXPAND, shape, k), zero-filled before
- * its first use (every call leaves it reusable).  The draft model, and which
+ * its first use (every call leaves it reusable, also for calls of another
+ * shape that fit in it).  The draft model, and which
  * kept children are inserted or expanded next, stay with the caller.
  */
 sd_status sd_tree_expand(const sd_expand_shape* shape, const void* draft_logits,

@@ -80,6 +80,8 @@ def test_rows_far_apart_exact():
     (5, 1001, 4096, 1.0, "f32"),        # ragged vocabulary, k at its maximum
     (7, 333, 1, 0.5, "f32"),
     (1, 4096, 4096, 1.3, "bf16"),       # every candidate
+    (256, 32000, 2048, 0.6, "bf16"),    # large batches: four chunks per workgroup
+    (700, 12345, 1000, 0.9, "f32"),     # the same, ragged vocabulary
 ])
 def test_expand_matches_oracle(E, V, k, tau, dtype):
     rng = np.random.default_rng(E * 7919 + V)
@@ -101,3 +103,16 @@ def test_expand_workspace_reuse():
     c = _run(l, "f32", cum, 0.7, 17)
     assert all(np.array_equal(x, y) for x, y in zip(a, b))
     assert np.array_equal(c[0], a[0][:17]) and np.array_equal(c[1], a[1][:17])
+
+
+def test_expand_workspace_across_shapes():
+    """One workspace for calls of different batch sizes and k in a row: each
+    result matches the oracle (the counter and histograms do not move with
+    the shape)."""
+    for E, V, k in ((300, 2000, 900), (8, 2000, 50), (1000, 1500, 4096), (3, 777, 5)):
+        rng = np.random.default_rng(E + 17)
+        l = (rng.standard_normal((E, V)) * 3).astype(np.float32)
+        cum = -rng.random(E) * 4
+        _say("expand across shapes E=%d" % E)
+        gpu = _run(l, "f32", cum, 0.8, k)
+        _check(gpu, l, "f32", cum.astype(np.float32), 0.8, k)

@@ -28,7 +28,10 @@
 namespace sdtree {
 
 constexpr int kExpTok = 8;                 // tokens per thread per chunk (one 16-byte bf16 load)
-constexpr int kExpChunk = 256 * kExpTok;   // tokens per workgroup per row
+constexpr int kExpChunk = 256 * kExpTok;   // tokens per workgroup per row and step
+// Large batches take IT = 4 steps per workgroup, so each workgroup forms the
+// prefix (and flushes its histogram) once per 4 chunks; small ones one step,
+// for more workgroups.
 
 __device__ __forceinline__ float exp_score(float off, float l, float inv_tau) {
   return __fadd_rn(off, __fmul_rn(l, inv_tau));
@@ -104,16 +107,20 @@ __global__ void __launch_bounds__(256) expand_lse_kernel(ExpandArgs a) {
 // its mask.  Cooperative (256 threads): every histogram is loaded into LDS at
 // once, then each pass's digit is the bin where the count of candidates at or
 // above it first reaches the number still to take (a parallel suffix scan).
+// When that bin holds exactly the candidates still to take, the k best are
+// the keys at or above the prefix (its lower digits zero): the selection is
+// `closed`, later passes have nothing to split and are skipped.
 struct ExpPrefix {
   uint32_t hs[8][256];
   uint32_t suf[257];
   uint32_t wsum[4];
   int d;
   uint32_t above;
+  uint32_t at;
 };
 template <int P>
 __device__ __forceinline__ void exp_prefix(const uint32_t* hist, int k, ExpPrefix& sh, unsigned long long& prefix,
-                                           unsigned long long& mask) {
+                                           unsigned long long& mask, bool& closed) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 #pragma unroll
   for (int p = 0; p < P; ++p) sh.hs[p][tid] = hist[p * 256 + tid];
@@ -121,6 +128,7 @@ __device__ __forceinline__ void exp_prefix(const uint32_t* hist, int k, ExpPrefi
   __syncthreads();
   prefix = 0ull;
   mask = 0ull;
+  closed = false;
   uint32_t k_rem = (uint32_t)k;
 #pragma unroll
   for (int p = 0; p < P; ++p) {
@@ -139,37 +147,51 @@ __device__ __forceinline__ void exp_prefix(const uint32_t* hist, int k, ExpPrefi
     if (sh.suf[tid] >= k_rem && sh.suf[tid + 1] < k_rem) {
       sh.d = tid;
       sh.above = sh.suf[tid + 1];
+      sh.at = sh.suf[tid];
     }
     __syncthreads();
     const int d = sh.d;
+    const bool whole = sh.at == k_rem;
     k_rem -= sh.above;
     const int shift = 56 - 8 * p;
     prefix |= (unsigned long long)d << shift;
     mask |= 0xFFull << shift;
     __syncthreads();
+    if (whole) {
+      closed = true;
+      break;
+    }
   }
 }
 
-template <typename LT, int P>
+template <typename LT, int P, int IT>
 __global__ void __launch_bounds__(256) expand_hist_kernel(ExpandArgs a) {
   __shared__ uint32_t h[4][256];     // one histogram per wavefront
   __shared__ ExpPrefix sh;
   const int tid = threadIdx.x, wave = tid >> 6;
   for (int w = 0; w < 4; ++w) h[w][tid] = 0u;
   unsigned long long prefix, mask;
-  exp_prefix<P>(a.hist, a.k, sh, prefix, mask);
+  bool closed;
+  exp_prefix<P>(a.hist, a.k, sh, prefix, mask, closed);
+  if (closed) return;
   const int e = blockIdx.y;
-  const int x0 = blockIdx.x * kExpChunk + tid * kExpTok;
-  if (x0 < a.V) {
-    const LT* row = reinterpret_cast<const LT*>(a.logits) + (size_t)e * a.V;
-    float v[8];
-    exp_load8<LT>(row, x0, a.V, v);
-    const float off = a.off[e];
-    constexpr int shift = 56 - 8 * P;
+  const LT* row = reinterpret_cast<const LT*>(a.logits) + (size_t)e * a.V;
+  const float off = a.off[e];
+  constexpr int shift = 56 - 8 * P;
+  float v[IT][8];
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int x0 = (blockIdx.x * IT + it) * kExpChunk + tid * kExpTok;
+    if (x0 < a.V) exp_load8<LT>(row, x0, a.V, v[it]);
+  }
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int x0 = (blockIdx.x * IT + it) * kExpChunk + tid * kExpTok;
+    if (x0 >= a.V) continue;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       if (x0 + j >= a.V) break;
-      const unsigned long long key = exp_key(exp_score(off, v[j], a.inv_tau), (uint32_t)e * (uint32_t)a.V + x0 + j);
+      const unsigned long long key = exp_key(exp_score(off, v[it][j], a.inv_tau), (uint32_t)e * (uint32_t)a.V + x0 + j);
       if ((key & mask) == prefix) atomicAdd(&h[wave][(key >> shift) & 0xFF], 1u);
     }
   }
@@ -178,26 +200,35 @@ __global__ void __launch_bounds__(256) expand_hist_kernel(ExpandArgs a) {
   if (c) atomicAdd(a.hist + P * 256 + tid, c);
 }
 
-template <typename LT>
+template <typename LT, int IT>
 __global__ void __launch_bounds__(256) expand_collect_kernel(ExpandArgs a) {
   __shared__ ExpPrefix sh;
   const int tid = threadIdx.x;
   unsigned long long thr, mask;
-  exp_prefix<8>(a.hist, a.k, sh, thr, mask);   // all 8 digits: the k-th largest key itself
+  bool closed;
+  // the k-th largest key itself, or the prefix at which the selection closed
+  exp_prefix<8>(a.hist, a.k, sh, thr, mask, closed);
   const int e = blockIdx.y;
-  const int x0 = blockIdx.x * kExpChunk + tid * kExpTok;
-  if (x0 >= a.V) return;
   const LT* row = reinterpret_cast<const LT*>(a.logits) + (size_t)e * a.V;
-  float v[8];
-  exp_load8<LT>(row, x0, a.V, v);
   const float off = a.off[e];
+  float v[IT][8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    if (x0 + j >= a.V) break;
-    const unsigned long long key = exp_key(exp_score(off, v[j], a.inv_tau), (uint32_t)e * (uint32_t)a.V + x0 + j);
-    if (key >= thr) {
-      const uint32_t slot = atomicAdd(a.count, 1u);
-      if (slot < (uint32_t)a.k) a.keys[slot] = key;
+  for (int it = 0; it < IT; ++it) {
+    const int x0 = (blockIdx.x * IT + it) * kExpChunk + tid * kExpTok;
+    if (x0 < a.V) exp_load8<LT>(row, x0, a.V, v[it]);
+  }
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int x0 = (blockIdx.x * IT + it) * kExpChunk + tid * kExpTok;
+    if (x0 >= a.V) continue;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (x0 + j >= a.V) break;
+      const unsigned long long key = exp_key(exp_score(off, v[it][j], a.inv_tau), (uint32_t)e * (uint32_t)a.V + x0 + j);
+      if (key >= thr) {
+        const uint32_t slot = atomicAdd(a.count, 1u);
+        if (slot < (uint32_t)a.k) a.keys[slot] = key;
+      }
     }
   }
 }
@@ -237,19 +268,26 @@ __global__ void __launch_bounds__(1024) expand_sort_kernel(ExpandArgs a) {
   if (tid == 0) *a.count = 0u;
 }
 
+template <typename LT, int IT>
+static void launch_passes(const ExpandArgs& a, hipStream_t st) {
+  const dim3 grid((unsigned)((a.V + kExpChunk * IT - 1) / (kExpChunk * IT)), (unsigned)a.E);
+  hipLaunchKernelGGL((expand_hist_kernel<LT, 0, IT>), grid, dim3(256), 0, st, a);
+  hipLaunchKernelGGL((expand_hist_kernel<LT, 1, IT>), grid, dim3(256), 0, st, a);
+  hipLaunchKernelGGL((expand_hist_kernel<LT, 2, IT>), grid, dim3(256), 0, st, a);
+  hipLaunchKernelGGL((expand_hist_kernel<LT, 3, IT>), grid, dim3(256), 0, st, a);
+  hipLaunchKernelGGL((expand_hist_kernel<LT, 4, IT>), grid, dim3(256), 0, st, a);
+  hipLaunchKernelGGL((expand_hist_kernel<LT, 5, IT>), grid, dim3(256), 0, st, a);
+  hipLaunchKernelGGL((expand_hist_kernel<LT, 6, IT>), grid, dim3(256), 0, st, a);
+  hipLaunchKernelGGL((expand_hist_kernel<LT, 7, IT>), grid, dim3(256), 0, st, a);
+  hipLaunchKernelGGL((expand_collect_kernel<LT, IT>), grid, dim3(256), 0, st, a);
+}
+
 template <typename LT>
 static hipError_t launch_expand_t(const ExpandArgs& a, hipStream_t st) {
   hipLaunchKernelGGL((expand_lse_kernel<LT>), dim3(a.E), dim3(256), 0, st, a);
-  const dim3 grid((unsigned)((a.V + kExpChunk - 1) / kExpChunk), (unsigned)a.E);
-  hipLaunchKernelGGL((expand_hist_kernel<LT, 0>), grid, dim3(256), 0, st, a);
-  hipLaunchKernelGGL((expand_hist_kernel<LT, 1>), grid, dim3(256), 0, st, a);
-  hipLaunchKernelGGL((expand_hist_kernel<LT, 2>), grid, dim3(256), 0, st, a);
-  hipLaunchKernelGGL((expand_hist_kernel<LT, 3>), grid, dim3(256), 0, st, a);
-  hipLaunchKernelGGL((expand_hist_kernel<LT, 4>), grid, dim3(256), 0, st, a);
-  hipLaunchKernelGGL((expand_hist_kernel<LT, 5>), grid, dim3(256), 0, st, a);
-  hipLaunchKernelGGL((expand_hist_kernel<LT, 6>), grid, dim3(256), 0, st, a);
-  hipLaunchKernelGGL((expand_hist_kernel<LT, 7>), grid, dim3(256), 0, st, a);
-  hipLaunchKernelGGL((expand_collect_kernel<LT>), grid, dim3(256), 0, st, a);
+  const long long chunks = (long long)a.E * ((a.V + kExpChunk - 1) / kExpChunk);
+  if (chunks >= 4096) launch_passes<LT, 4>(a, st);
+  else launch_passes<LT, 1>(a, st);
   hipLaunchKernelGGL(expand_sort_kernel, dim3(1), dim3(1024), 0, st, a);
   return hipGetLastError();
 }

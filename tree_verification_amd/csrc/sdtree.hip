@@ -140,12 +140,15 @@ static AttnPlan plan_attn(const sd_shape* s, int ksel, bool sparse) {
 static size_t commit_ws(const sd_shape* s) { return kWsHeader + align_up((size_t)s->B * 4, 256); }
 
 // Expansion scratch: row offsets, 8 x 256 histograms, a counter, k keys.
+// The counter and the histograms sit at offsets that do not depend on the
+// shape, so a workspace that was zero-filled once stays valid for calls of any
+// shape (the sort kernel clears the counter, the first kernel the histograms).
 static size_t expand_ws(const sd_expand_shape* s, int32_t k, size_t* off, size_t* hist, size_t* cnt,
                         size_t* keys) {
-  const size_t o = kWsHeader;
-  const size_t h = align_up(o + (size_t)s->E * 4, 256);
-  const size_t c = h + 8 * 256 * 4;
-  const size_t kk = align_up(c + 4, 256);
+  const size_t c = kWsHeader;
+  const size_t h = align_up(c + 4, 256);
+  const size_t o = h + 8 * 256 * 4;
+  const size_t kk = align_up(o + (size_t)s->E * 4, 256);
   if (off) *off = o;
   if (hist) *hist = h;
   if (cnt) *cnt = c;
