@@ -114,3 +114,24 @@ def test_shared_selection_workspace_reuse():
     assert torch.equal(a, b)
     ref = oracle.topk_blocks(x.q, x.k_pages, x.block_table, x.ctx_lens, c.bs, 5, c.dtype)
     assert np.array_equal(p.cpu().numpy(), ref)
+
+
+def test_shared_selection_bad_block_sets_status():
+    """A context block id out of range under the kept-sums path: the block
+    bit is set, the call completes, and a sequence whose table is sound gets
+    the oracle's list."""
+    from tests.devutil import dev_tensor
+    c = small_variant("sparse_topk32_ctx64k", B=2, ctx_lo=300, ctx_hi=300, hot_blocks=1)
+    x = make_inputs(c)
+    d = to_device(x)
+    sums = tva.block_sums(d["k"], d["table"], d["ctx"])
+    torch.cuda.synchronize()
+    assert tva.device_status() == 0
+    table = x.block_table.copy()
+    table[1, 2] = x.k_pages.shape[0] + 5
+    _say("shared top-k bad block")
+    sel = tva.topk_blocks_shared(d["q"], d["k"], dev_tensor(table), d["ctx"], 3, sums=sums)
+    torch.cuda.synchronize()
+    assert tva.device_status() & 0x2
+    ref = oracle.topk_blocks_shared(x.q, x.k_pages, x.block_table, x.ctx_lens, c.bs, 3, c.dtype)
+    assert np.array_equal(sel.cpu().numpy()[0], ref[0])
