@@ -178,3 +178,67 @@ def test_invcdf_edges():
     assert oracle.invcdf(w, 0.2499)[0] == 1
     assert oracle.invcdf(w, 0.25)[0] == 3
     assert oracle.invcdf(w, 0.9999999)[0] == 3
+
+
+def _one_node_case(V, tokens, q_row, u_test, u_root_sample, u_leaf_sample=0.0):
+    """A root whose children carry `tokens` (child c is node c + 1), uniform
+    target logits (p = 1/V), the same draft row at every node."""
+    n = len(tokens)
+    T = n + 1
+    parent = np.array([[-1] + [0] * n], np.int32)
+    tok = np.array([[0] + list(tokens)], np.int32)
+    logits = np.zeros((1, T, V), np.float32)
+    qd = np.broadcast_to(np.asarray(q_row, np.float32), (1, T, V)).copy()
+    unif = np.zeros((1, T, 2), np.float32)
+    unif[0, 1:, 0] = u_test
+    unif[0, 0, 1] = u_root_sample
+    unif[0, 1:, 1] = u_leaf_sample
+    return logits, qd, parent, tok, unif
+
+
+def test_zero_residual_mass_leaves_target_unchanged():
+    """Reading R9: a draft row with q >= p everywhere (here q = 2p, summing to
+    2) leaves no residual mass after a rejection; the target is then kept as it
+    was.  With p = 1/8, child c is accepted iff u_c * 1/4 < 1/8, i.e. u_c < 1/2,
+    whatever came before -- so the walk takes the first child with u < 1/2.
+    (Setting r to the zero vector instead would reject every later child; a
+    division by the zero mass would turn r into NaNs and reject them too.)"""
+    V = 8
+    q = np.full(V, 0.25)
+    # children 1, 2 rejected (u >= 1/2), child 3 accepted (u = 0.3)
+    logits, qd, parent, tok, unif = _one_node_case(V, [3, 5, 1], q, [0.7, 0.6, 0.3], 0.0,
+                                                   u_leaf_sample=0.55)
+    path, plen, bonus = oracle.accept(logits, "f32", qd, parent, tok, unif, 1.0)
+    assert list(path[0, :plen[0]]) == [0, 3]
+    # node 3 is a leaf: the bonus is drawn from p = 1/8 there: smallest x with (x+1)/8 > 0.55
+    assert bonus[0] == 4
+    # every child rejected: the bonus comes from the unchanged target, x = floor(8 u)
+    logits, qd, parent, tok, unif = _one_node_case(V, [3, 5, 1], q, [0.7, 0.6, 0.9], 0.8)
+    path, plen, bonus = oracle.accept(logits, "f32", qd, parent, tok, unif, 1.0)
+    assert plen[0] == 1 and bonus[0] == 6
+
+
+def test_wide_node_tests_every_sibling():
+    """A node with 100 children: the first 99 carry token 0, the last token 3.
+    With p = 1/8 and q(0) = 0.9, q(y) = 0.1/7 elsewhere, child 1 is rejected
+    (u q(0) = 0.45 >= 1/8); the residual is then uniform over tokens 1..7
+    (max(p - q, 0) is the same there and zero at token 0) and stays so after
+    every later rejection, while r(0) = 0 rejects children 2..99 for any u.
+    Child 100 (token 3, u = 0.9) passes 0.9 * 0.1/7 < 1/7: the path is
+    [0, 100], and its leaf draws the bonus from p = 1/8."""
+    V = 8
+    q = np.full(V, 0.1 / 7)
+    q[0] = 0.9
+    tokens = [0] * 99 + [3]
+    u = [0.5] + [0.99] * 98 + [0.9]
+    logits, qd, parent, tok, unif = _one_node_case(V, tokens, q, u, 0.0, u_leaf_sample=0.3)
+    path, plen, bonus = oracle.accept(logits, "f32", qd, parent, tok, unif, 1.0)
+    assert list(path[0, :plen[0]]) == [0, 100]
+    assert bonus[0] == 2                      # smallest x with (x+1)/8 > 0.3
+    # the last child made to fail too (u = 0.9999 -> 0.9999 * q(3) < 1/7 still
+    # holds, so give it token 0): every child rejected, the bonus is drawn from
+    # the residual, uniform over 1..7: smallest x >= 1 with x/7 > 0.5 -> 4
+    tokens = [0] * 100
+    logits, qd, parent, tok, unif = _one_node_case(V, tokens, q, u, 0.5)
+    path, plen, bonus = oracle.accept(logits, "f32", qd, parent, tok, unif, 1.0)
+    assert plen[0] == 1 and bonus[0] == 4

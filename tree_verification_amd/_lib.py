@@ -20,7 +20,8 @@ SD_CALL_ATTN, SD_CALL_ACCEPT, SD_CALL_TOPK, SD_CALL_COMMIT, SD_CALL_BLOCK_SUMS, 
     1, 2, 3, 4, 5, 6
 STATUS = {0: "SD_OK", 1: "SD_INVALID_ARG", 2: "SD_BAD_SHAPE", 3: "SD_BAD_DTYPE",
           4: "SD_UNSUPPORTED", 5: "SD_CAPACITY", 6: "SD_HIP_ERROR", 7: "SD_DEVICE_DATA_ERROR"}
-ERR_BITS = {0x1: "parent", 0x2: "block", 0x4: "capacity", 0x8: "token", 0x10: "selection"}
+ERR_BITS = {0x1: "parent", 0x2: "block", 0x4: "capacity", 0x8: "token", 0x10: "selection",
+            0x20: "timeout"}
 
 
 class SdShape(ctypes.Structure):

@@ -36,7 +36,6 @@ constexpr int kAW = kAT / 64;         // wavefronts per workgroup
 constexpr int kChunk = kAT * 8;       // tokens per chunk
 constexpr int kMaxCh = 4;             // chunks kept in registers
 constexpr int kMaxT = kMaxTreeNodes;
-constexpr int kMaxRej = 64;
 constexpr int kMaxP = 16;             // (the slice butterflies span 16 lanes)
 constexpr int kMaxKid = 64;          // children whose test scalars are prefetched
 constexpr int kCKRegs = 4;           // commit: 16-byte K chunks per thread per group
@@ -166,8 +165,10 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
   __shared__ float red_f[kAW];
   __shared__ int red_i[kAW];
   __shared__ double mass[kMaxP];    // per-slice mass of the distribution to draw from
-  __shared__ double zrej[kMaxRej];  // residual normalisers at the current node
-  __shared__ double zinv[kMaxRej];  // their reciprocals (0 when the mass was 0)
+  // reciprocals of the residual normalisers of the siblings rejected so far
+  // at the current node (0 where the mass was 0); a node has fewer than T
+  // children, so the history never overflows
+  __shared__ double zinv[MODE == kRejection ? kMaxT : 1];
   __shared__ __align__(8) uint32_t xv[kMaxP][2];
   __shared__ int s_flag, s_to, s_first, s_last, s_x;
 
@@ -851,6 +852,9 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
         }
       } else {
         int nrej = 0;
+        // the normaliser of the last rejection whose residual mass was
+        // positive (the statistics pass's if none was): the unit of mass[]
+        double units = z0;
         // Residual after `upto` rejections for one token: r <- max(r - q, 0) /
         // Z_j for each rejection j whose mass Z_j was positive (zero mass
         // leaves r unchanged), multiplying by the reciprocals zinv[j].  The
@@ -881,7 +885,7 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
             )
           }
         };
-        for (int c = 0; c < nk && nrej < kMaxRej; ++c) {
+        for (int c = 0; c < nk; ++c) {
           if (c > 0 && c % kMaxKid == 0) {
             // the next batch of children's test scalars (wide nodes only);
             // these loads are waited for here, off the common path
@@ -943,10 +947,8 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
           if (z > 0.0 && tid < P)
             mass[tid] = __longlong_as_double((long long)(((unsigned long long)xv[tid][1] << 32) | xv[tid][0]));
           const double zi = z > 0.0 ? 1.0 / z : 0.0;
-          if (tid == 0) {
-            zrej[nrej] = z;
-            zinv[nrej] = zi;
-          }
+          if (z > 0.0) units = z;
+          if (tid == 0) zinv[nrej] = zi;
           if constexpr (CACHED) {
             if (z > 0.0) {
               FOR_CHUNKS(cc,
@@ -964,11 +966,7 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
           if (nrej == 0) init_rr();   // a leaf: the draw is from p itself
           const float u = a.unif[((size_t)b * T + cur) * 2 + 1];
           const int nr = nrej;
-          // weights in the units of mass[]: the residual times the normaliser of
-          // the last pass that changed it (the statistics pass if none did)
-          double units = z0;
-          for (int j = 0; j < nr; ++j)
-            if (zrej[j] > 0.0) units = zrej[j];
+          // weights in the units of mass[]: the residual times `units`
           auto rw8 = [&](int c, double* w8) {
             if constexpr (CACHED) {
 #pragma unroll
