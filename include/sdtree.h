@@ -11,6 +11,8 @@
  *                        sampling from the target at each node);
  *   sd_kv_commit         the accepted root path becomes committed context;
  *   sd_accept_commit     sd_accept then sd_kv_commit, in one launch;
+ *   sd_accept_commit_noalloc  the same without a workspace argument, for
+ *                        callers that cannot allocate;
  *   sd_topk_blocks       top-k KV blocks per query for sparse verification;
  *   sd_block_sums, sd_block_sums_append, sd_topk_blocks_cached
  *                        the same selection from per-block key sums kept as
@@ -21,7 +23,9 @@
  *   - Tensor arguments are DEVICE pointers owned by the caller.  The library
  *     never allocates or frees device memory.  Scratch comes from a caller
  *     workspace `ws` of at least sd_workspace_bytes(...) bytes, zero-filled
- *     once by the caller before its first use (the library leaves it reusable).
+ *     once by the caller before its first use (the library leaves it reusable);
+ *     the one exception, sd_accept_commit_noalloc, uses a fixed device array
+ *     of the library instead.
  *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = default stream)
  *     and return an sd_status.  Argument and shape errors are detected on the
  *     host before anything is launched; then nothing is launched.
@@ -188,6 +192,32 @@ sd_status sd_accept_commit(const sd_accept_shape* shape, const sd_shape* kv_shap
                            int32_t* path_len, int32_t* bonus, void* k_pages, void* v_pages,
                            const int32_t* block_table, int32_t* ctx_lens, void* ws,
                            size_t ws_bytes, void* stream);
+
+/*
+ * sd_accept_commit for callers that cannot allocate device memory or pass a
+ * workspace (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).  Same arguments and results as sd_accept_commit,
+ * except that there is no workspace: the acceptance walk's cross-workgroup
+ * exchange slots live in a device array of the library (128 KiB, one copy per
+ * GPU, held until the process ends), and the sticky error bits go to
+ * `status`, a caller-owned device word (OR-ed into; read and clear it with
+ * sd_device_status(status, stream, &bits)).
+ *   Limit: when a sequence is walked by several workgroups (up to 16, while
+ *   B * 16 <= 256 and V > 2048), at most 128 sequences per call; a larger
+ *   call returns SD_CAPACITY before launching anything.
+ *   The call allocates nothing (no hipMalloc, no library allocation); it
+ *   clears the slots it uses with a small kernel before the walk.
+ *   Concurrency: every call on one GPU shares that GPU's slots, so two calls
+ *   that may overlap on one GPU (different streams, no ordering) race and
+ *   must not be issued; calls ordered on one stream are fine.
+ */
+sd_status sd_accept_commit_noalloc(const sd_accept_shape* shape, const sd_shape* kv_shape,
+                                   const void* target_logits, const float* draft_probs,
+                                   const int32_t* tree_parent, const int32_t* tree_token,
+                                   const float* uniforms, float temperature, int32_t* path,
+                                   int32_t* path_len, int32_t* bonus, void* k_pages,
+                                   void* v_pages, const int32_t* block_table, int32_t* ctx_lens,
+                                   uint32_t* status, void* stream);
 
 /*
  * Top-k context blocks per query (sparse-verification page, "Methodology":

@@ -17,7 +17,7 @@ def setup_module():
 
 def test_exports_every_declared_function():
     names = _lib.declared_functions()
-    assert len(names) == 13
+    assert len(names) == 14
     for n in names:
         assert hasattr(L, n), n
 
@@ -112,6 +112,24 @@ def test_accept_commit_rejects_bad_arguments():
     assert call(_lib.SdAcceptShape(2, 8, 100, 5, 8), kv) == 3
     assert call(ok, kv, tau=-1.0) == 1
     assert call(ok, kv, ws=100) == 5
+
+
+def test_accept_commit_noalloc_rejects_bad_arguments():
+    """Host checks of the no-workspace variant, before any HIP call: the same
+    as sd_accept_commit's, and a status word is required."""
+    def call(shape, kv, tau=0.8, kpages=FAKE, status=FAKE):
+        return L.sd_accept_commit_noalloc(ctypes.byref(shape), None if kv is None else ctypes.byref(kv),
+                                          FAKE, FAKE, FAKE, FAKE, FAKE, tau, FAKE, FAKE, FAKE, kpages,
+                                          FAKE, FAKE, FAKE, status, None)
+    ok = _lib.SdAcceptShape(2, 8, 100, 1, 8)
+    kv = _shape(B=2, T=8, Hq=8, tree_stride=8)
+    assert call(ok, None) == 1
+    assert call(ok, _shape(B=3, T=8, Hq=8, tree_stride=8)) == 2
+    assert call(ok, _shape(B=2, T=8, Hq=8, tree_stride=8, D=96)) == 4
+    assert call(ok, kv, kpages=None) == 1
+    assert call(_lib.SdAcceptShape(2, 8, 100, 5, 8), kv) == 3
+    assert call(ok, kv, tau=-1.0) == 1
+    assert call(ok, kv, status=None) == 1
 
 
 def test_block_sums_calls_reject_bad_arguments():

@@ -72,6 +72,8 @@ def lib():
         "sd_kv_commit": [ctypes.POINTER(SdShape), _P, _P, _P, _P, _P, _P, _P, sz, _P],
         "sd_accept_commit": [ctypes.POINTER(SdAcceptShape), ctypes.POINTER(SdShape), _P, _P, _P, _P, _P,
                              ctypes.c_float, _P, _P, _P, _P, _P, _P, _P, _P, sz, _P],
+        "sd_accept_commit_noalloc": [ctypes.POINTER(SdAcceptShape), ctypes.POINTER(SdShape), _P, _P, _P,
+                                     _P, _P, ctypes.c_float, _P, _P, _P, _P, _P, _P, _P, _P, _P],
         "sd_topk_blocks": [ctypes.POINTER(SdShape), _P, _P, _P, _P, i32, _P, _P, sz, _P],
         "sd_topk_blocks_cached": [ctypes.POINTER(SdShape), _P, _P, _P, _P, i32, _P, _P, sz, _P],
         "sd_topk_blocks_shared": [ctypes.POINTER(SdShape), _P, _P, _P, _P, _P, i32, _P, _P, sz, _P],
@@ -220,6 +222,32 @@ def accept_commit(target_logits, draft_probs, tree_parent, tree_token, uniforms,
         _ptr(tree_parent), _ptr(tree_token), _ptr(uniforms), float(temperature), _ptr(path),
         _ptr(path_len), _ptr(bonus), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(ctx_lens),
         _ptr(ws), ws.numel(), _stream(dev)))
+    return path, path_len, bonus
+
+
+def accept_commit_noalloc(target_logits, draft_probs, tree_parent, tree_token, uniforms,
+                          temperature, k_pages, v_pages, block_table, ctx_lens, status,
+                          path=None, path_len=None, bonus=None):
+    """sd_accept_commit_noalloc: accept_commit(...) with no workspace; sticky
+    error bits are OR-ed into `status` (an int32 device tensor of one element)."""
+    B, T, V = target_logits.shape
+    shape = SdAcceptShape(B, T, V, _dtype_code[target_logits.dtype],
+                          0 if tree_parent.shape[0] == 1 else T)
+    nb, Hkv, bs, D = k_pages.shape
+    kv_shape = SdShape(B, T, Hkv, Hkv, D, bs, block_table.shape[1], nb, _dtype_code[k_pages.dtype],
+                       T, 0.0)
+    dev = target_logits.device
+    if path is None:
+        path = torch.empty((B, T), dtype=torch.int32, device=dev)
+    if path_len is None:
+        path_len = torch.empty(B, dtype=torch.int32, device=dev)
+    if bonus is None:
+        bonus = torch.empty(B, dtype=torch.int32, device=dev)
+    _check("sd_accept_commit_noalloc", lib().sd_accept_commit_noalloc(
+        ctypes.byref(shape), ctypes.byref(kv_shape), _ptr(target_logits), _ptr(draft_probs),
+        _ptr(tree_parent), _ptr(tree_token), _ptr(uniforms), float(temperature), _ptr(path),
+        _ptr(path_len), _ptr(bonus), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(ctx_lens),
+        _ptr(status), _stream(dev)))
     return path, path_len, bonus
 
 

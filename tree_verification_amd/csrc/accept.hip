@@ -25,6 +25,7 @@
 // picks the slice holding the crossing point from the per-slice masses and
 // only that workgroup rescans its slice.  Sums are float64; the probability a
 // test is taken on is recomputed in float64.
+#include <mutex>
 #include <type_traits>
 
 #include "common.h"
@@ -1067,6 +1068,59 @@ hipError_t launch_accept(const AcceptArgs& a, hipStream_t st) {
   AcceptArgs copy = a;
   void* args[] = {&copy};
   return hipLaunchKernel(fn, grid, block, args, 0, st);
+}
+
+// ---- the allocation-free variant ------------------------------------------
+// Exchange slots of up to kNoAllocMaxSeqs sequences in a device array owned by
+// the library (one copy per GPU, alive until the process ends).  Host code
+// never uses the array's name as an address: the device address is looked up
+// once per device and kept in g_scratch_ptr.
+static __device__ __align__(256) unsigned char scratch[(size_t)kNoAllocMaxSeqs * kAccSeqBytes];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices];
+
+// The current device's copy of `scratch` (looked up on the first call there).
+static hipError_t scratch_on_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+// Zero-fill of n 16-byte words (a kernel rather than a memset node, so the
+// call stays safe to capture in a graph).
+__global__ void __launch_bounds__(256) zero16_kernel(uint4* p, int n) {
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) p[i] = make_uint4(0, 0, 0, 0);
+}
+
+hipError_t launch_accept_noalloc(AcceptArgs a, hipStream_t st) {
+  if (a.P > 1 && a.B > kNoAllocMaxSeqs) return hipErrorInvalidValue;   // (the caller checks first)
+  void* sp = nullptr;
+  hipError_t e = scratch_on_current_device(&sp);
+  if (e != hipSuccess) return e;
+  a.sync = static_cast<unsigned char*>(sp);   // (read only when P > 1)
+  if (a.P > 1) {
+    // the slots of the sequences this call uses start from zero whatever an
+    // earlier call (on any stream of this device) left there
+    const int n16 = (int)((size_t)a.B * kAccSeqBytes / 16);
+    hipLaunchKernelGGL(zero16_kernel, dim3((n16 + 255) / 256), dim3(256), 0, st,
+                       static_cast<uint4*>(sp), n16);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return launch_accept(a, st);
 }
 
 }  // namespace sdtree

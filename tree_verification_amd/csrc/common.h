@@ -182,6 +182,11 @@ hipError_t launch_anc_mask(const int32_t* parent, int T, int W64, int n_trees, u
 hipError_t launch_attn_valu(const AttnArgs& a, bool f32, hipStream_t st);
 hipError_t launch_attn_mfma(const AttnArgs& a, const AttnPlan& p, hipStream_t st);
 hipError_t launch_accept(const AcceptArgs& a, hipStream_t st);
+// The acceptance walk with its exchange slots in the library's own device
+// array (no workspace argument): at most kNoAllocMaxSeqs sequences when a
+// sequence spans several workgroups.
+constexpr int kNoAllocMaxSeqs = 128;
+hipError_t launch_accept_noalloc(AcceptArgs a, hipStream_t st);
 hipError_t launch_commit(const CommitArgs& a, hipStream_t st);
 hipError_t launch_topk(const TopkArgs& a, bool f32, bool cached, hipStream_t st);
 hipError_t launch_topk_shared(const TopkArgs& a, bool f32, bool cached, hipStream_t st);

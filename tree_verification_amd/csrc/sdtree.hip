@@ -287,12 +287,12 @@ sd_status sd_tree_verify_attn(const sd_shape* shape, const void* q, const void* 
 }
 
 // Checks the arguments of an acceptance call and fills its kernel arguments
-// (no commit).
+// (no commit, no scratch: the callers place the status word and the exchange
+// slots).
 static sd_status accept_args(const sd_accept_shape* shape, const void* target_logits,
                              const float* draft_probs, const int32_t* tree_parent,
                              const int32_t* tree_token, const float* uniforms, float temperature,
-                             int32_t* path, int32_t* path_len, int32_t* bonus, void* ws,
-                             size_t ws_bytes, AcceptArgs* out) {
+                             int32_t* path, int32_t* path_len, int32_t* bonus, AcceptArgs* out) {
   if (!shape) return SD_INVALID_ARG;
   const sd_accept_shape& s = *shape;
   if (s.B < 1 || s.T < 1 || s.V < 1) return SD_BAD_SHAPE;
@@ -300,10 +300,9 @@ static sd_status accept_args(const sd_accept_shape* shape, const void* target_lo
   if (s.logit_dtype != SD_F32 && s.logit_dtype != SD_BF16) return SD_BAD_DTYPE;
   if (s.T > kMaxTreeNodes) return SD_UNSUPPORTED;
   if (!(temperature >= 0.f) || isinf(temperature)) return SD_INVALID_ARG;
-  if (!target_logits || !tree_parent || !tree_token || !path || !path_len || !bonus || !ws)
+  if (!target_logits || !tree_parent || !tree_token || !path || !path_len || !bonus)
     return SD_INVALID_ARG;
   if (temperature > 0.f && !uniforms) return SD_INVALID_ARG;
-  if (ws_bytes < accept_ws(&s)) return SD_CAPACITY;
   AcceptArgs a;
   memset(&a, 0, sizeof(a));
   a.logits = target_logits;
@@ -312,12 +311,36 @@ static sd_status accept_args(const sd_accept_shape* shape, const void* target_lo
   a.parent = tree_parent; a.token = tree_token; a.unif = uniforms; a.tau = temperature;
   a.B = s.B; a.T = s.T; a.V = s.V; a.tree_stride = s.tree_stride;
   a.path = path; a.path_len = path_len; a.bonus = bonus;
-  a.status = static_cast<uint32_t*>(ws);
-  a.sync = static_cast<unsigned char*>(ws) + kWsHeader;
   a.P = accept_wgs(s.B, s.V);
   a.SL = (((s.V + a.P - 1) / a.P) + 7) / 8 * 8;
   a.NC = (a.SL + 2047) / 2048;
   *out = a;
+  return SD_OK;
+}
+
+// The status word and exchange slots of a call with a caller workspace.
+static sd_status accept_ws_args(const sd_accept_shape* shape, void* ws, size_t ws_bytes,
+                                AcceptArgs* a) {
+  if (!ws) return SD_INVALID_ARG;
+  if (ws_bytes < accept_ws(shape)) return SD_CAPACITY;
+  a->status = static_cast<uint32_t*>(ws);
+  a->sync = static_cast<unsigned char*>(ws) + kWsHeader;
+  return SD_OK;
+}
+
+// The commit half of an acceptance call that also commits its paths.
+static sd_status accept_commit_args(const sd_accept_shape* shape, const sd_shape* kv_shape,
+                                    void* k_pages, void* v_pages, const int32_t* block_table,
+                                    int32_t* ctx_lens, AcceptArgs* a) {
+  if (!shape || !kv_shape) return SD_INVALID_ARG;
+  const sd_status st = check_shape(kv_shape);
+  if (st != SD_OK) return st;
+  if (kv_shape->B != shape->B || kv_shape->T != shape->T) return SD_BAD_SHAPE;
+  if (!k_pages || !v_pages || !block_table || !ctx_lens) return SD_INVALID_ARG;
+  a->ck = k_pages; a->cv = v_pages; a->ctable = block_table; a->cctx = ctx_lens;
+  a->cHkv = kv_shape->Hkv; a->cD = kv_shape->D; a->cbs = kv_shape->bs;
+  a->cmax_blocks = kv_shape->max_blocks; a->cnum_blocks = kv_shape->num_blocks;
+  a->cesize = kv_shape->dtype == SD_F32 ? 4 : 2;
   return SD_OK;
 }
 
@@ -327,8 +350,10 @@ sd_status sd_accept(const sd_accept_shape* shape, const void* target_logits,
                     int32_t* path, int32_t* path_len, int32_t* bonus, void* ws, size_t ws_bytes,
                     void* stream) {
   AcceptArgs a;
-  const sd_status st = accept_args(shape, target_logits, draft_probs, tree_parent, tree_token,
-                                   uniforms, temperature, path, path_len, bonus, ws, ws_bytes, &a);
+  sd_status st = accept_args(shape, target_logits, draft_probs, tree_parent, tree_token,
+                             uniforms, temperature, path, path_len, bonus, &a);
+  if (st != SD_OK) return st;
+  st = accept_ws_args(shape, ws, ws_bytes, &a);
   if (st != SD_OK) return st;
   return hip_status(launch_accept(a, static_cast<hipStream_t>(stream)));
 }
@@ -340,20 +365,35 @@ sd_status sd_accept_commit(const sd_accept_shape* shape, const sd_shape* kv_shap
                            int32_t* path_len, int32_t* bonus, void* k_pages, void* v_pages,
                            const int32_t* block_table, int32_t* ctx_lens, void* ws,
                            size_t ws_bytes, void* stream) {
-  if (!shape || !kv_shape) return SD_INVALID_ARG;
-  sd_status st = check_shape(kv_shape);
-  if (st != SD_OK) return st;
-  if (kv_shape->B != shape->B || kv_shape->T != shape->T) return SD_BAD_SHAPE;
-  if (!k_pages || !v_pages || !block_table || !ctx_lens) return SD_INVALID_ARG;
   AcceptArgs a;
-  st = accept_args(shape, target_logits, draft_probs, tree_parent, tree_token, uniforms,
-                   temperature, path, path_len, bonus, ws, ws_bytes, &a);
+  sd_status st = accept_args(shape, target_logits, draft_probs, tree_parent, tree_token, uniforms,
+                             temperature, path, path_len, bonus, &a);
   if (st != SD_OK) return st;
-  a.ck = k_pages; a.cv = v_pages; a.ctable = block_table; a.cctx = ctx_lens;
-  a.cHkv = kv_shape->Hkv; a.cD = kv_shape->D; a.cbs = kv_shape->bs;
-  a.cmax_blocks = kv_shape->max_blocks; a.cnum_blocks = kv_shape->num_blocks;
-  a.cesize = kv_shape->dtype == SD_F32 ? 4 : 2;
+  st = accept_commit_args(shape, kv_shape, k_pages, v_pages, block_table, ctx_lens, &a);
+  if (st != SD_OK) return st;
+  st = accept_ws_args(shape, ws, ws_bytes, &a);
+  if (st != SD_OK) return st;
   return hip_status(launch_accept(a, static_cast<hipStream_t>(stream)));
+}
+
+sd_status sd_accept_commit_noalloc(const sd_accept_shape* shape, const sd_shape* kv_shape,
+                                   const void* target_logits, const float* draft_probs,
+                                   const int32_t* tree_parent, const int32_t* tree_token,
+                                   const float* uniforms, float temperature, int32_t* path,
+                                   int32_t* path_len, int32_t* bonus, void* k_pages,
+                                   void* v_pages, const int32_t* block_table, int32_t* ctx_lens,
+                                   uint32_t* status, void* stream) {
+  AcceptArgs a;
+  sd_status st = accept_args(shape, target_logits, draft_probs, tree_parent, tree_token, uniforms,
+                             temperature, path, path_len, bonus, &a);
+  if (st != SD_OK) return st;
+  st = accept_commit_args(shape, kv_shape, k_pages, v_pages, block_table, ctx_lens, &a);
+  if (st != SD_OK) return st;
+  if (!status) return SD_INVALID_ARG;
+  // the library's exchange slots hold kNoAllocMaxSeqs sequences
+  if (a.P > 1 && a.B > kNoAllocMaxSeqs) return SD_CAPACITY;
+  a.status = status;
+  return hip_status(launch_accept_noalloc(a, static_cast<hipStream_t>(stream)));
 }
 
 sd_status sd_kv_commit(const sd_shape* shape, void* k_pages, void* v_pages,
