@@ -21,10 +21,17 @@ Prints one JSON line: verified tree tokens/s (B * T per step) over the timed
 steps, the attention call against the HBM or MFMA roofline (algorithmic
 bytes or FLOPs per call / event-timed call duration), and the CPU oracle
 timed on a bounded sample of the same workload.  The attention call of every
-10th timed step (--event-every) is bracketed by HIP events: an event record
-leaves the GPU idle for a few microseconds, so bracketing every call would
-add that idle time to every step.  Before the warmup steps, untimed steps
-run for --settle-ms so the GPU has left its idle clocks.
+10th timed step (--event-every; more often when fewer than 200 steps are
+timed, so that at least 20 calls are) is bracketed by HIP events: an event
+record leaves the GPU idle for a few microseconds, so bracketing every call
+would add that idle time to every step.  Before the warmup steps, untimed
+steps run for --settle-ms so the GPU has left its idle clocks.
+
+`secondary` lists the other workloads, each with its attention call against
+its roofline (the mean of 3 x 40 back-to-back calls alternating between two
+K/V copies), its whole step, and the selection call of the sparse modes; the
+2048-node tree also reports the MFMA FLOPs its kernel executes against the
+algorithmic ones.
 """
 import argparse
 import hashlib
@@ -67,7 +74,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="approximate CPU time budget of the oracle sample")
     ap.add_argument("--no-secondary", action="store_true",
-                    help="skip the attention roofline of the 2048-node tree workload")
+                    help="skip the other workloads' measurements (attention against its roofline, "
+                         "the whole step, the selection calls)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after the run, copy MIB MiB device-to-device 3 times (a plain copy "
                          "kernel of known size that scales the HBM byte counters)")
@@ -144,6 +152,73 @@ def roofline_for(cfg, bytes_, flops, seconds):
     achieved = flops / seconds / 1e12
     return {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4)}
+
+
+def executed_mfma_flops_256x32(cfg, x):
+    """MFMA FLOPs the bf16 kernel issues when it runs 256-row query tiles over
+    32-key tiles (its plan for the 2048-node tree workload): every tile of a
+    (sequence, KV head, 256-row tile) runs 256 x 32 x D multiply-adds for the
+    scores and as many for P V, over all context tiles and those tree tiles
+    that hold an ancestor of one of the tile's nodes (the others are
+    skipped)."""
+    B, T, Hq, Hkv, D = cfg.B, cfg.T, cfg.Hq, cfg.Hkv, cfg.D
+    G = Hq // Hkv
+    rows, nk = 256, 32
+    per_tile = 4 * rows * nk * D
+    total = 0
+    for b in range(B):
+        par = x.tree_parent[0] if x.tree_parent.shape[0] == 1 else x.tree_parent[b]
+        ctx_tiles = (int(x.ctx_lens[b]) + nk - 1) // nk
+        nodes_per_tile = rows // G
+        for q0 in range(0, T * G, rows):
+            touched = set()
+            for i in range(q0 // G, min(T, q0 // G + nodes_per_tile)):
+                n = i
+                while n >= 0:
+                    touched.add(n // nk)
+                    n = int(par[n]) if n > 0 else -1
+            total += Hkv * (ctx_tiles + len(touched)) * per_tile
+    return total
+
+
+def bound_attention(w, sel=None, kv=0):
+    """A closure calling sd_tree_verify_attn through the C ABI with its
+    arguments marshalled once (so back-to-back calls are not spaced out by
+    host-side argument handling)."""
+    import ctypes
+    from tree_verification_amd import _lib
+    k, v = w.kvs[kv]
+    shape = _lib.make_shape(w.q, k, w.table, w.parent)
+    k_sel = 0 if sel is None else sel.shape[-1]
+    need = _lib.workspace_bytes(_lib.SD_CALL_ATTN, shape, k_sel)
+    ws = _lib._WS.get(w.q.device, need, _lib.SD_CALL_ATTN)
+    fn = _lib.lib().sd_tree_verify_attn
+    args = (ctypes.byref(shape), _lib._ptr(w.q), _lib._ptr(k), _lib._ptr(v), _lib._ptr(w.table),
+            _lib._ptr(w.ctx), _lib._ptr(w.parent), _lib._ptr(sel), k_sel, _lib._ptr(w.out),
+            _lib._ptr(ws), ws.numel(), _lib._stream(w.q.device))
+    keep = (shape, ws)
+
+    def call():
+        assert fn(*args) == 0, keep
+    return call
+
+
+def loop_us(torch, calls, n=40, rounds=3):
+    """Median over `rounds` of the mean device time of n back-to-back calls
+    (cycling through `calls`), two HIP events around each round."""
+    ts = []
+    for _ in range(rounds):
+        for c in calls:
+            c()
+        torch.cuda.synchronize()
+        e0, e1 = HipEvent(), HipEvent()
+        e0.record()
+        for j in range(n):
+            calls[j % len(calls)]()
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) / n * 1e3)
+    return float(np.median(ts))
 
 
 ATTN_SOURCES = ("attn.hip", "common.h", "sdtree.hip")
@@ -302,6 +377,29 @@ class Workload:
             # both K/V copies, which agree below ctx)
             self.sums = self.tva.block_sums(self.k, self.table, self.ctx)
 
+    def set_selection(self, mode):
+        """Sparse workload: 'dense' attends to the whole context, 'per_row'
+        selects blocks per query row from the kept sums, 'shared' one
+        selection per (sequence, KV group)."""
+        import torch
+        cfg = self.cfg
+        if mode == "dense":
+            self.sel = None
+        else:
+            if self.sel is None:
+                self.sel = torch.empty((cfg.B, cfg.T, cfg.Hq, cfg.topk), dtype=torch.int32, device="cuda")
+            self.shared = mode == "shared"
+            self.select(self.ctx)
+            self.torch.cuda.synchronize()
+
+    def select(self, ctx):
+        if self.sel is not None and self.shared:
+            self.tva.topk_blocks_shared(self.q, self.k, self.table, ctx, self.cfg.topk, sums=self.sums,
+                                        sel=self.sel)
+        elif self.sel is not None:
+            self.tva.topk_blocks_cached(self.q, self.sums, self.k, self.table, ctx, self.cfg.topk,
+                                        sel=self.sel)
+
     def attention(self, ctx=None):
         self.tva.tree_verify_attn(self.q, self.k, self.v, self.table, self.ctx if ctx is None else ctx,
                                   self.parent, out=self.out, sel_blocks=self.sel)
@@ -316,10 +414,7 @@ class Workload:
             ctx = self.ctx
         self.k, self.v = self.kvs[self.n_steps % len(self.kvs)]
         self.n_steps += 1
-        if self.sel is not None and self.shared:
-            tva.topk_blocks_shared(self.q, self.k, self.table, ctx, self.cfg.topk, sums=self.sums, sel=self.sel)
-        elif self.sel is not None:
-            tva.topk_blocks_cached(self.q, self.sums, self.k, self.table, ctx, self.cfg.topk, sel=self.sel)
+        self.select(ctx)
         if ev is not None:
             ev[0].record()
         self.attention(ctx)
@@ -380,6 +475,77 @@ def time_calls(w, reps=10):
         res["block_sums_append_5_us"] = loop(lambda: tva.block_sums_append(w.k, w.table, ctx_new, n_new,
                                                                            scratch))
     return {k: round(v, 1) for k, v in res.items()}
+
+
+def step_loop_us(w, n=40):
+    """Mean device time of n whole steps back to back (each on its own copy of
+    the starting context lengths), two HIP events around the loop."""
+    torch = w.torch
+    for _ in range(4):
+        w.step()
+    ctxs = [w.ctx0.clone() for _ in range(n)]
+    torch.cuda.synchronize()
+    e0, e1 = HipEvent(), HipEvent()
+    e0.record()
+    for j in range(n):
+        w.step(None, ctxs[j])
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n * 1e3
+
+
+def measure_workload(w, label, n_calls=40):
+    """One workload's attention against its roofline (n_calls back-to-back
+    calls alternating between the K/V copies), its whole step, and, for the
+    sparse modes, the selection call."""
+    torch, cfg = w.torch, w.cfg
+    sel = w.sel
+    calls = [bound_attention(w, sel, kv) for kv in range(len(w.kvs))]
+    t_us = loop_us(torch, calls, n=n_calls)
+    sel_np = None if sel is None else sel.cpu().numpy()
+    bytes_, flops = attention_cost(cfg, w.x, sel_np)
+    roof = roofline_for(cfg, bytes_, flops, t_us * 1e-6)
+    e = {"workload": cfg.name, "call": label, "attention_us": round(t_us, 2),
+         "timed_calls": 3 * n_calls, "bytes_per_call": int(bytes_), "flops_per_call": int(flops),
+         "roofline": roof, "verified_tree_tokens_per_s": round(cfg.B * cfg.T / (t_us * 1e-6), 1)}
+    if sel is not None:
+        f = (lambda: w.tva.topk_blocks_shared(w.q, w.k, w.table, w.ctx, cfg.topk, sums=w.sums, sel=w.sel)) \
+            if w.shared else \
+            (lambda: w.tva.topk_blocks_cached(w.q, w.sums, w.k, w.table, w.ctx, cfg.topk, sel=w.sel))
+        e["selection_us"] = round(loop_us(torch, [f], n=20), 2)
+    step_us = step_loop_us(w)
+    e["step_us"] = round(step_us, 2)
+    e["step_tree_tokens_per_s"] = round(cfg.B * cfg.T / (step_us * 1e-6), 1)
+    e["mean_path_len"] = round(float(w.plen.cpu().numpy().mean()), 3)
+    return e
+
+
+def secondary_workloads():
+    """The other four workloads, each measured as measure_workload does; the
+    sparse workload three ways (dense attention, per-row selection, shared
+    selection), the 2048-node tree with its executed-to-algorithmic MFMA
+    FLOP ratio."""
+    out = []
+    for name in ("specexec_70b_tree2048", "longctx_paged_tree16", "sparse_topk32_ctx64k", "tiny_chain"):
+        w = Workload(name, kv_copies=2)
+        if w.cfg.topk:
+            for mode in ("dense", "per_row", "shared"):
+                w.set_selection(mode)
+                out.append(measure_workload(w, {"dense": "attention (dense)",
+                                                "per_row": "sparse attention, selection per query row",
+                                                "shared": "sparse attention, selection per KV group"}[mode]))
+        else:
+            e = measure_workload(w, "attention")
+            if name == "specexec_70b_tree2048":
+                ex = executed_mfma_flops_256x32(w.cfg, w.x)
+                e["executed_mfma_flops_per_call"] = int(ex)
+                e["executed_over_algorithmic_flops"] = round(ex / e["flops_per_call"], 4)
+            out.append(e)
+        print(json.dumps({"secondary_done": name}), file=sys.stderr, flush=True)
+        del w
+        import torch
+        torch.cuda.empty_cache()
+    return out
 
 
 def cpu_baseline(w, budget_s):
@@ -603,7 +769,8 @@ def main():
     for _ in range(args.warmup):
         w.step()
     torch.cuda.synchronize()
-    every = max(1, args.event_every)
+    # at least 20 bracketed calls (all of them for fewer than 20 steps)
+    every = max(1, min(args.event_every, args.steps // 20))
     evs = {k: (HipEvent(), HipEvent()) for k in range(0, args.steps, every)}
     # each timed step gets its own copy of the context lengths (its commit
     # advances them), so no restore runs inside the timed region
@@ -626,17 +793,12 @@ def main():
     # the committed counter figures are for the per-row selection
     roof["traffic"] = None if w.shared else traffic_for("attn", cfg.name)
     calls = time_calls(w)
+    loop = [bound_attention(w, w.sel, kv) for kv in range(len(w.kvs))]
+    calls["attention_loop_us"] = round(loop_us(torch, loop), 2)
 
     secondary = None
-    if not args.no_secondary and args.workload != "specexec_70b_tree2048":
-        w2 = Workload("specexec_70b_tree2048")
-        t2 = time_calls(w2, reps=10)["attention_us"] * 1e-6
-        b2, f2 = attention_cost(w2.cfg, w2.x)
-        r2 = roofline_for(w2.cfg, b2, f2, t2)
-        secondary = {"workload": "specexec_70b_tree2048 attention (B=1, 64/8 heads, T=2048, ctx 2048)",
-                     "attention_us": round(t2 * 1e6, 1), "roofline": r2,
-                     "verified_tree_tokens_per_s": round(w2.cfg.B * w2.cfg.T / t2, 1)}
-        del w2
+    if not args.no_secondary:
+        secondary = [e for e in secondary_workloads() if e["workload"] != args.workload]
 
     cpu = None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_seconds)
     value = cfg.B * cfg.T / step_s
@@ -664,6 +826,7 @@ def main():
                          attention_us=round(attn_s * 1e6, 2), timed_calls=len(evs),
                          bytes_per_call=int(bytes_),
                          flops_per_call=int(flops)),
+        "verified_tree_tokens_per_s_attention": round(cfg.B * cfg.T / attn_s, 1),
         "cpu_baseline": cpu,
         "accepted_tokens_per_s": round(float(plen.sum()) / step_s, 1),
         "mean_path_len": round(float(plen.mean()), 3),

@@ -158,7 +158,10 @@ sd_status sd_accept(const sd_accept_shape* shape, const void* target_logits,
                     void* stream);
 
 /*
- * Commit the accepted path: for j < path_len[b], position ctx_b + j takes the
+ * Commit the accepted path (SpecExec page, "Approach": the tokens the walk
+ * accepts become committed context for the next verification pass; the
+ * accepted root path is compacted into the slots right after the context):
+ * for j < path_len[b], position ctx_b + j takes the
  * K/V of position ctx_b + path[b][j] (every KV head), then ctx_lens[b] +=
  * path_len[b].  In place; path must be increasing with path[b][0] == 0 (as
  * sd_accept produces), which makes the in-place copy safe.  k_pages, v_pages
