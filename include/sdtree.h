@@ -41,7 +41,7 @@
  * Layouts (row-major, innermost last)
  *   q, out        [B, T, Hq, D]                 element type `dtype`
  *   k_pages       [num_blocks, Hkv, bs, D]      element type `dtype`
- *   v_pages       [num_blocks, Hkv, D, bs]      V is stored transposed in each page
+ *   v_pages       [num_blocks, Hkv, bs, D]      element type `dtype` (as k_pages)
  *   block_table   int32 [B, max_blocks]         logical block -> physical block
  *   ctx_lens      int32 [B]                     committed context length
  *   tree_parent   int32 [B or 1, T]             parent[0] = -1, 0 <= parent[i] < i

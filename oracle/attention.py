@@ -15,7 +15,7 @@ always attended.
 
 Readings: node i's own K/V sits at position ctx_b + i (the caller writes it
 there); scale defaults to D^-1/2; no positional bias (RoPE is applied by the
-caller).  K pages are [num_blocks, Hkv, bs, D]; V pages [num_blocks, Hkv, D, bs].
+caller).  K and V pages are [num_blocks, Hkv, bs, D].
 
 Two independent formulations are given and must agree:
 ``attention_dense`` builds the context-plus-ancestor mask for all nodes at once;
@@ -39,8 +39,7 @@ def gather_kv(k_pages, v_pages, block_table, b, g, positions, bs, dtype):
     blk = np.asarray(block_table)[b, pos // bs]
     off = pos % bs
     K = decode(k_pages[blk, g, off, :], dtype)
-    V = decode(np.stack([v_pages[bk, g, :, o] for bk, o in zip(blk, off)]), dtype) \
-        if len(pos) else np.zeros((0, k_pages.shape[-1]))
+    V = decode(v_pages[blk, g, off, :], dtype)
     return K, V
 
 

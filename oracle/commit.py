@@ -25,6 +25,6 @@ def commit(k_pages, v_pages, block_table, ctx_lens, path, path_len, bs):
             sb, so = int(block_table[b, src // bs]), src % bs
             db, do = int(block_table[b, dst // bs]), dst % bs
             K[db, :, do, :] = k_pages[sb, :, so, :]
-            V[db, :, :, do] = v_pages[sb, :, :, so]
+            V[db, :, do, :] = v_pages[sb, :, so, :]
     new_ctx = (np.asarray(ctx_lens, dtype=np.int64) + np.asarray(path_len)).astype(np.int32)
     return K, V, new_ctx

@@ -6,8 +6,7 @@ Recipe (the same bytes feed the CPU oracle and the GPU library):
 * normals are drawn in float32 and, for bf16 workloads, rounded once to bf16
   (round to nearest even) and kept as uint16 bit patterns;
 * uniforms are ``integers(0, 2**24) * 2**-24``, exact float32 values in [0, 1);
-* K pages are laid out ``[num_blocks, Hkv, bs, D]`` and V pages
-  ``[num_blocks, Hkv, D, bs]`` (V is stored transposed inside each page);
+* K and V pages are both laid out ``[num_blocks, Hkv, bs, D]``;
 * tree node i's K/V sits at logical position ``ctx_b + i`` of sequence b;
 * draft logits are ``rho * target + sqrt(1 - rho^2) * eps`` with ``eps`` drawn
   at the target's sigma, so the draft keeps the stated marginal and agrees
@@ -71,7 +70,7 @@ class Inputs:
     cfg: Config
     q: np.ndarray             # [B, T, Hq, D] float32 or bf16 bits
     k_pages: np.ndarray       # [num_blocks, Hkv, bs, D]
-    v_pages: np.ndarray       # [num_blocks, Hkv, D, bs]
+    v_pages: np.ndarray       # [num_blocks, Hkv, bs, D]
     block_table: np.ndarray   # int32 [B, max_blocks], -1 past each sequence's blocks
     ctx_lens: np.ndarray      # int32 [B]
     tree_parent: np.ndarray   # int32 [B, T], parent[0] = -1, parent[i] < i
@@ -195,7 +194,7 @@ def make_inputs(cfg: Config) -> Inputs:
     else:
         hot = np.zeros((B, 0), dtype=np.int32)
         k_pages = _normals(_rng(cfg, S_K), (num_blocks, Hkv, bs, D), 1.0, cfg.dtype)
-    v_pages = _normals(_rng(cfg, S_V), (num_blocks, Hkv, D, bs), 1.0, cfg.dtype)
+    v_pages = _normals(_rng(cfg, S_V), (num_blocks, Hkv, bs, D), 1.0, cfg.dtype)
 
     parent = np.full((B, T), -1, dtype=np.int32)
     token = np.zeros((B, T), dtype=np.int32)

@@ -6,7 +6,7 @@ import numpy as np
 
 def paged_from_dense(Kd, Vd, bs, rng=None, spare=0):
     """Kd, Vd: [B, Hkv, n, D] float arrays (same n for all sequences).
-    Returns k_pages [nb, Hkv, bs, D], v_pages [nb, Hkv, D, bs], block_table [B, per]
+    Returns k_pages [nb, Hkv, bs, D], v_pages [nb, Hkv, bs, D], block_table [B, per]
     with blocks optionally shuffled.  ``spare`` extra random blocks are appended."""
     B, Hkv, n, D = Kd.shape
     per = (n + bs - 1) // bs
@@ -15,7 +15,7 @@ def paged_from_dense(Kd, Vd, bs, rng=None, spare=0):
     if rng is not None:
         phys = rng.permutation(nb)
     kp = np.zeros((nb, Hkv, bs, D), dtype=Kd.dtype)
-    vp = np.zeros((nb, Hkv, D, bs), dtype=Vd.dtype)
+    vp = np.zeros((nb, Hkv, bs, D), dtype=Vd.dtype)
     if rng is not None:
         kp[:] = rng.standard_normal(kp.shape)
         vp[:] = rng.standard_normal(vp.shape)
@@ -26,7 +26,7 @@ def paged_from_dense(Kd, Vd, bs, rng=None, spare=0):
             table[b, j] = blk
             lo, hi = j * bs, min(n, (j + 1) * bs)
             kp[blk, :, :hi - lo, :] = Kd[b, :, lo:hi, :]
-            vp[blk, :, :, :hi - lo] = np.swapaxes(Vd[b, :, lo:hi, :], 1, 2)
+            vp[blk, :, :hi - lo, :] = Vd[b, :, lo:hi, :]
     return kp, vp, table
 
 

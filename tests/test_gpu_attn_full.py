@@ -66,8 +66,8 @@ def _plant(c, x):
             blk, off = int(x.block_table[b, p // bs]), p % bs
             x.k_pages[blk, :, off, :] = f32_to_bf16_bits(krow)[None, :]
             for g in range(Hkv):
-                x.v_pages[blk, g, :, off] = 0
-                x.v_pages[blk, g, _onehot_dim(j, g, D), off] = one
+                x.v_pages[blk, g, off, :] = 0
+                x.v_pages[blk, g, off, _onehot_dim(j, g, D)] = one
 
 
 def _planted_expected(c, x):

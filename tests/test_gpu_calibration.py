@@ -83,7 +83,7 @@ def test_calibration_chain_is_causal_attention():
     for b in range(c.B):
         ctx = int(x.ctx_lens[b])
         rows_k = np.stack([x.k_pages[x.block_table[b, p // c.bs], :, p % c.bs] for p in range(ctx + c.T)])
-        rows_v = np.stack([x.v_pages[x.block_table[b, p // c.bs], :, :, p % c.bs] for p in range(ctx + c.T)])
+        rows_v = np.stack([x.v_pages[x.block_table[b, p // c.bs], :, p % c.bs] for p in range(ctx + c.T)])
         for i in range(c.T):
             for h in range(c.Hq):
                 kk = rows_k[:ctx + i + 1, h // G].astype(np.float64)

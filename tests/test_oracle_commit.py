@@ -15,7 +15,7 @@ def _cache(rng, B=2, n=40, Hkv=2, D=4, bs=4):
 
 def _logical(kp, vp, table, b, p, bs):
     blk, off = table[b, p // bs], p % bs
-    return kp[blk, :, off, :], vp[blk, :, :, off]
+    return kp[blk, :, off, :], vp[blk, :, off, :]
 
 
 def test_identity_path_changes_nothing_but_lengths():

@@ -39,8 +39,7 @@ constexpr int kMaxCh = 4;             // chunks kept in registers
 constexpr int kMaxT = kMaxTreeNodes;
 constexpr int kMaxP = 16;             // (the slice butterflies span 16 lanes)
 constexpr int kMaxKid = 64;          // children whose test scalars are prefetched
-constexpr int kCKRegs = 4;           // commit: 16-byte K chunks per thread per group
-constexpr int kCVRegs = 24;          // commit: V^T elements per thread per group
+constexpr int kCKRegs = 4;           // commit: 16-byte K (and V) chunks per thread per group
 constexpr int kMaxCBlk = kMaxT / 8 + 2;  // commit: blocks of the tree slots (bs >= 8)
 constexpr unsigned kSpinLimit = 1u << 20;
 
@@ -242,67 +241,49 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
   // blocks be valid, else the sequence is left untouched and a sticky bit is
   // set.
   // Copies the path's entries of this workgroup's KV heads (g = wg, wg + P,
-  // ...) in groups: every thread loads its share of a group (16-byte K chunks,
-  // V^T elements), the workgroup waits for all of them, then stores.  Since
+  // ...) in groups: every thread loads its share of a group (16-byte chunks of
+  // the K and V rows), the workgroup waits for all of them, then stores.  Since
   // path[j] >= j and the path increases, a group's destinations never overlap
   // a later group's sources, so the copy is safe in place.  kids[] holds the
   // path and s_cblk[] the block ids of slots [ctx, ctx + T).
   auto commit_copy = [&](int L) {
     const int D = a.cD, esize = a.cesize, bs = a.cbs, lo = c_ctx / bs;
     const int rowb = D * esize;
-    const int kch = rowb / 16;                      // 16-byte chunks per K row
-    const int kstep = kAT / kch, vstep = kAT / D;
+    const int kch = rowb / 16;                      // 16-byte chunks per row
+    const int kstep = kAT / kch;
     const int kcol = tid % kch, ku0 = tid / kch;
-    const int vcol = tid % D, vu0 = tid / D;
-    const int JG = min(kCKRegs * kstep, kCVRegs * vstep);
+    const int JG = kCKRegs * kstep;
     const long long blk_bytes = (long long)a.cHkv * bs * rowb;
     unsigned char* K = static_cast<unsigned char*>(a.ck);
     unsigned char* Vb = static_cast<unsigned char*>(a.cv);
-    const long long kc_off = (long long)kcol * 16;
-    const long long vc_off = (long long)vcol * bs * esize;
+    const long long c_off = (long long)kcol * 16;
     for (int g = wg; g < a.cHkv; g += P) {
-      const long long head_k = (long long)g * bs * rowb;
-      const long long head_v = (long long)g * D * bs * esize;
-      auto k_at = [&](int pos) {
-        return (long long)s_cblk[pos / bs - lo] * blk_bytes + head_k + (long long)(pos % bs) * rowb;
-      };
-      auto v_at = [&](int pos) {
-        return (long long)s_cblk[pos / bs - lo] * blk_bytes + head_v + (long long)(pos % bs) * esize;
+      const long long head = (long long)g * bs * rowb;
+      auto row_at = [&](int pos) {
+        return (long long)s_cblk[pos / bs - lo] * blk_bytes + head + (long long)(pos % bs) * rowb;
       };
       for (int j0 = 0; j0 < L; j0 += JG) {
         const int nj = min(JG, L - j0);
-        uint4 kr[kCKRegs];
-        uint32_t vr[kCVRegs];
+        uint4 kr[kCKRegs], vr[kCKRegs];
 #pragma unroll
         for (int r = 0; r < kCKRegs; ++r) {
           const int jj = ku0 + r * kstep;
           kr[r] = make_uint4(0, 0, 0, 0);
-          if (jj < nj && kids[j0 + jj] != j0 + jj)
-            kr[r] = *reinterpret_cast<const uint4*>(K + k_at(c_ctx + kids[j0 + jj]) + kc_off);
-        }
-#pragma unroll
-        for (int r = 0; r < kCVRegs; ++r) {
-          const int jj = vu0 + r * vstep;
-          vr[r] = 0;
+          vr[r] = make_uint4(0, 0, 0, 0);
           if (jj < nj && kids[j0 + jj] != j0 + jj) {
-            const unsigned char* src = Vb + v_at(c_ctx + kids[j0 + jj]) + vc_off;
-            vr[r] = esize == 2 ? *reinterpret_cast<const uint16_t*>(src) : *reinterpret_cast<const uint32_t*>(src);
+            const long long src = row_at(c_ctx + kids[j0 + jj]) + c_off;
+            kr[r] = *reinterpret_cast<const uint4*>(K + src);
+            vr[r] = *reinterpret_cast<const uint4*>(Vb + src);
           }
         }
         __syncthreads();   // every load of the group has landed before any store
 #pragma unroll
         for (int r = 0; r < kCKRegs; ++r) {
           const int jj = ku0 + r * kstep;
-          if (jj < nj && kids[j0 + jj] != j0 + jj)
-            *reinterpret_cast<uint4*>(K + k_at(c_ctx + j0 + jj) + kc_off) = kr[r];
-        }
-#pragma unroll
-        for (int r = 0; r < kCVRegs; ++r) {
-          const int jj = vu0 + r * vstep;
           if (jj < nj && kids[j0 + jj] != j0 + jj) {
-            unsigned char* dst = Vb + v_at(c_ctx + j0 + jj) + vc_off;
-            if (esize == 2) *reinterpret_cast<uint16_t*>(dst) = (uint16_t)vr[r];
-            else *reinterpret_cast<uint32_t*>(dst) = vr[r];
+            const long long dst = row_at(c_ctx + j0 + jj) + c_off;
+            *reinterpret_cast<uint4*>(K + dst) = kr[r];
+            *reinterpret_cast<uint4*>(Vb + dst) = vr[r];
           }
         }
         __syncthreads();

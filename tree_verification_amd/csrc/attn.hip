@@ -9,7 +9,7 @@
 // Kernels:
 //   anc_mask_kernel     ancestor bitmask per node, anc(i) = anc(parent(i)) | bit(i)
 //   attn_valu_kernel    one workgroup per query row, float32 math (fp32 inputs)
-//   attn_mfma_kernel    bf16 MFMA flash-style kernel: K / V^T tiles staged in LDS
+//   attn_mfma_kernel    bf16 MFMA flash-style kernel: K / V tiles staged in LDS
 //                       and shared by every query row of a KV group, online
 //                       softmax in registers, split context with partials
 //   attn_combine_kernel merges split partials into the normalised output
@@ -123,7 +123,7 @@ __global__ void __launch_bounds__(256) attn_valu_kernel(AttnArgs a) {
         float acc = 0.f;
         for (int d = 0; d < D; ++d) acc += Elem<E>::load(q, d) * Elem<E>::load(kr, d);
         s = acc * a.scale_log2;
-        vbase = ((long long)blk * a.Hkv + g) * D * a.bs + off;
+        vbase = (((long long)blk * a.Hkv + g) * a.bs + off) * D;
       }
     }
     float cm = s;
@@ -150,7 +150,7 @@ __global__ void __launch_bounds__(256) attn_valu_kernel(AttnArgs a) {
         const long long bb = vis ? base : 0;
 #pragma unroll
         for (int k = 0; k < DL; ++k) {
-          const float x = Elem<E>::load(V, bb + (size_t)(lane + 64 * k) * a.bs);
+          const float x = Elem<E>::load(V, bb + lane + 64 * k);
           v[u][k] = vis ? x : 0.f;
         }
       }
@@ -191,13 +191,14 @@ __global__ void __launch_bounds__(256) attn_valu_kernel(AttnArgs a) {
 // disjoint key slices of each tile and merge their softmax states at the end.
 //
 // Key tiles of NK keys stream through an S-stage LDS ring: each K row [D] and
-// each V^T row [NK] is brought in with 16-byte direct global-to-LDS loads
+// each V row [D] is brought in with 16-byte direct global-to-LDS loads
 // (global_load_lds_dwordx4), issued S - 1 tiles ahead and waited for with an
 // explicit vmcnt before the tile's barrier, so up to S - 1 tiles are in flight
 // while one is computed.  LDS rows are unpadded; the 16-byte chunk a lane
-// writes is chosen (XOR swizzle) so that the 16 rows read by one MFMA operand
-// fetch fall on distinct banks.  V^T chunks that cannot be copied whole (a
-// context or tree edge that is not 8-aligned) are assembled in registers.
+// writes is chosen (XOR swizzle) so that the rows read by one MFMA operand
+// fetch fall on distinct banks.  Keys that do not exist (past a context or
+// tree edge) read a zero page.  The V^T operand of P V is formed from the V
+// rows by the LDS transposing reads (ds_read_b64_tr_b16).
 //
 // S^T = K Q^T is formed with v_mfma_f32_16x16x32_bf16 with Q^T held in
 // registers; the K rows fed to the two 16-row halves of each 32-key group are
@@ -219,30 +220,32 @@ __global__ void __launch_bounds__(WQ * WK * 64) attn_mfma_kernel(AttnArgs a) {
   constexpr int DS = D / 32;
   constexpr int DB = D / 16;
   constexpr int KG = KW / 32;
-  constexpr int CK = D / 8;                      // 16-byte chunks per K row
-  constexpr int CV = NK / 8;                     // 16-byte chunks per V^T row
+  constexpr int CK = D / 8;                      // 16-byte chunks per K or V row
   constexpr int K_BYTES = NK * D * 2;
-  constexpr int V_BYTES = D * NK * 2;
+  constexpr int V_BYTES = NK * D * 2;
   constexpr int K_OPS = K_BYTES / (NT * 16);     // DMA instructions per thread per tile
-  constexpr int V_OPS = V_BYTES / (NT * 16);
+  constexpr int V_OPS = K_OPS;                   // (a V row is laid out as a K row)
   constexpr int OPS = K_OPS + V_OPS;
-  static_assert(K_OPS * NT * 16 == K_BYTES && V_OPS * NT * 16 == V_BYTES, "tile split");
+  static_assert(K_OPS * NT * 16 == K_BYTES, "tile split");
   static_assert(NWAVE == 4 || NWAVE == 8, "four or eight wavefronts");
   static_assert(S >= 2 && (S - 1) * OPS <= 63, "vmcnt range");
 
-  // Swizzles: chunk c of K row r sits at position c ^ kswz(r); chunk c of V^T
-  // row d at c ^ vswz(d).  (Rows one MFMA operand reads: 16 K rows
-  // {8a + 4h + b} of a 32-key group, or 16 consecutive V^T rows.)
+  // K tile: chunk c of K row r sits at position c ^ kswz(r) of the row (one
+  // K operand read takes 16-byte chunks of the 16 K rows {8a + 4h + b} of a
+  // 32-key group).
+  // V tile: stored in 256-byte slabs of 8 keys x 16 dims.  Key
+  // 16 m + 8 e + 4 h + k (e, h in {0, 1}, k < 4), dims 16 d .. 16 d + 15, lie
+  // at byte m * 32 D + h * 16 D + d * 256 + (4 e + k) * 32.  One V operand
+  // read is a pair of transposing 8-byte reads (h = 0, 1) in which the 32
+  // lanes of a half wavefront cover one slab exactly, so they meet no bank
+  // twice, and a lane's address differs between fragments by constants only.
   auto kswz = [](int r) -> int {
     return CK == 16 ? ((r & 3) | ((r >> 1) & 12)) : (((r >> 1) & 1) | (((r >> 3) & 3) << 1));
   };
-  auto vswz = [](int d) -> int {
-    return CV == 16 ? (d & 15) : CV == 8 ? ((d >> 1) & 7) : ((d >> 2) & 3);
-  };
 
   extern __shared__ __align__(16) unsigned char smem[];
-  unsigned char* Kst = smem;                                 // [S][K_BYTES]
-  unsigned char* Vst = smem + S * K_BYTES;                   // [S][V_BYTES]
+  unsigned char* Kst = smem;                                 // [S][K_BYTES]  (NK rows of D)
+  unsigned char* Vst = smem + S * K_BYTES;                   // [S][V_BYTES]  (NK rows of D)
   unsigned char* tflag = Vst + S * V_BYTES;                  // [128]
   int* tlist = reinterpret_cast<int*>(tflag + 128);          // [128]
   // element offset of (block, head g) for this split's context blocks / the tree blocks
@@ -500,38 +503,32 @@ __global__ void __launch_bounds__(WQ * WK * 64) attn_mfma_kernel(AttnArgs a) {
     boff = ttab[(p >> bsh) - tb0];
     return p;
   };
-  // Do the 8-key chunks of tile t copy whole (8-aligned, all valid or all not)?
-  auto v_clean = [&](int t) __attribute__((always_inline)) -> bool {
-    if ((ctx & 7) == 0) return t < nct || ((t - nct) * NK + NK <= T) || (T & 7) == 0;
-    return t < nct && !sparse && t * NK + NK <= ctx;
-  };
   const bf16_bits* zeros = reinterpret_cast<const bf16_bits*>(a.zeros);
 
-  // Per-thread DMA geometry (loop invariant).  K: DMA n of a tile writes slot
-  // s = lane + 64 (wave + 4 n), i.e. row s / CK, position s % CK, so it copies
-  // global chunk (s % CK) ^ kswz(row).  V^T: row s / CV, chunk (s % CV) ^ vswz.
-  int k_row[K_OPS], k_col[K_OPS], v_row[V_OPS], v_key[V_OPS];
+  // Per-thread DMA geometry (loop invariant).  DMA n of a tile writes the
+  // 16-byte slot s = lane + 64 (wave + NWAVE n).  K: row s / CK (a key),
+  // position s % CK, holding global chunk (s % CK) ^ kswz(row).  V: byte 16 s
+  // of the slab layout, i.e. key v_key and element offset v_col of its row.
+  int k_row[K_OPS], k_col[K_OPS], v_key[V_OPS], v_col[V_OPS];
 #pragma unroll
   for (int n = 0; n < K_OPS; ++n) {
     const int sl = lane + 64 * (wave + NWAVE * n);
     k_row[n] = sl / CK;
     k_col[n] = ((sl % CK) ^ kswz(sl / CK)) * 8;
-  }
-#pragma unroll
-  for (int n = 0; n < V_OPS; ++n) {
-    const int sl = lane + 64 * (wave + NWAVE * n);
-    v_row[n] = sl / CV;
-    v_key[n] = ((sl % CV) ^ vswz(sl / CV)) * 8;
+    const int o = sl * 16;                      // byte in the V tile
+    const int m = o / (32 * D), h = (o / (16 * D)) & 1, d = (o >> 8) & (DB - 1);
+    const int j = (o >> 5) & 7, half = (o >> 4) & 1;
+    v_key[n] = 16 * m + 8 * (j >> 2) + 4 * h + (j & 3);
+    v_col[n] = (2 * d + half) * 8;
   }
 
-  // Issue the loads of tile t's K (issue_k) or V^T (issue_v) into ring slot
-  // `slot`.  Every thread issues the same number of DMA operations.  The LDS
+  // Issue the loads of tile t's K (issue_k) or V (issue_v) into the ring slot
+  // at `kst` / `vst`.  Every thread issues the same number of DMA operations.  The LDS
   // DMA builtin is always given a named pointer variable: handed an array
   // element directly, the host compilation pass silently drops the kernel's
   // launch stub (the link check in the build catches that).
   auto dense_full = [&](int t) { return t < nct && !sparse && t * NK + NK <= ctx; };
-  auto issue_k = [&](int t, int slot) __attribute__((always_inline)) {
-    unsigned char* kst = Kst + slot * K_BYTES;
+  auto issue_k = [&](int t, unsigned char* kst) __attribute__((always_inline)) {
     if (dense_full(t)) {
 #pragma unroll
       for (int n = 0; n < K_OPS; ++n) {
@@ -549,39 +546,22 @@ __global__ void __launch_bounds__(WQ * WK * 64) attn_mfma_kernel(AttnArgs a) {
       __builtin_amdgcn_global_load_lds(src, kst + (wave + NWAVE * n) * 1024, 16, 0, 0);
     }
   };
-  auto issue_v = [&](int t, int slot) __attribute__((always_inline)) {
-    unsigned char* vst = Vst + slot * V_BYTES;
+  auto issue_v = [&](int t, unsigned char* vst) __attribute__((always_inline)) {
     if (dense_full(t)) {
 #pragma unroll
       for (int n = 0; n < V_OPS; ++n) {
         const int p = t * NK + v_key[n];
-        const bf16_bits* src = Vp + ctab[(p >> bsh) - cb0] + (long long)(v_row[n] * bs + (p & bsm));
+        const bf16_bits* src = Vp + ctab[(p >> bsh) - cb0] + (long long)((p & bsm) * D + v_col[n]);
         __builtin_amdgcn_global_load_lds(src, vst + (wave + NWAVE * n) * 1024, 16, 0, 0);
       }
       return;
     }
-    if (v_clean(t)) {
 #pragma unroll
-      for (int n = 0; n < V_OPS; ++n) {
-        long long boff = 0;
-        const int p = key_at(t, v_key[n], boff);
-        const bf16_bits* src = p >= 0 ? Vp + boff + (long long)(v_row[n] * bs + (p & bsm)) : zeros;
-        __builtin_amdgcn_global_load_lds(src, vst + (wave + NWAVE * n) * 1024, 16, 0, 0);
-      }
-    } else {
-      // assemble each 8-key chunk element by element (zeros past the edge);
-      // these plain loads are waited for here, so the DMA counts stay exact
-#pragma unroll
-      for (int n = 0; n < V_OPS; ++n) {
-        uint32_t w[4] = {0, 0, 0, 0};
-        for (int e = 0; e < 8; ++e) {
-          long long boff = 0;
-          const int p = key_at(t, v_key[n] + e, boff);
-          if (p >= 0) w[e >> 1] |= (uint32_t)Vp[boff + v_row[n] * bs + (p & bsm)] << (16 * (e & 1));
-        }
-        const int sl = lane + 64 * (wave + NWAVE * n);
-        *reinterpret_cast<uint4*>(vst + sl * 16) = make_uint4(w[0], w[1], w[2], w[3]);
-      }
+    for (int n = 0; n < V_OPS; ++n) {
+      long long boff = 0;
+      const int p = key_at(t, v_key[n], boff);
+      const bf16_bits* src = p >= 0 ? Vp + boff + (long long)((p & bsm) * D + v_col[n]) : zeros;
+      __builtin_amdgcn_global_load_lds(src, vst + (wave + NWAVE * n) * 1024, 16, 0, 0);
     }
   };
 
@@ -610,9 +590,8 @@ __global__ void __launch_bounds__(WQ * WK * 64) attn_mfma_kernel(AttnArgs a) {
   typedef f32x4 STile[QB][2 * KG];
   typedef bf16x8 PTile[QB][KG];
 
-  // S^T = K Q^T for this wave's keys of the tile in ring slot `slot`.
-  auto qk = [&](int slot, STile& s) __attribute__((always_inline)) {
-    const unsigned char* Kt = Kst + slot * K_BYTES;
+  // S^T = K Q^T for this wave's keys of the K tile at Kt.
+  auto qk = [&](const unsigned char* Kt, STile& s) __attribute__((always_inline)) {
 #pragma unroll
     for (int kg = 0; kg < KG; ++kg) {
 #pragma unroll
@@ -634,8 +613,7 @@ __global__ void __launch_bounds__(WQ * WK * 64) attn_mfma_kernel(AttnArgs a) {
   };
 
   typedef bf16x8 KFrag[KG][2][DS];
-  auto load_k = [&](int slot, KFrag& kf) __attribute__((always_inline)) {
-    const unsigned char* Kt = Kst + slot * K_BYTES;
+  auto load_k = [&](const unsigned char* Kt, KFrag& kf) __attribute__((always_inline)) {
 #pragma unroll
     for (int kg = 0; kg < KG; ++kg)
 #pragma unroll
@@ -766,17 +744,38 @@ __global__ void __launch_bounds__(WQ * WK * 64) attn_mfma_kernel(AttnArgs a) {
     }
   };
   // O^T += V^T P^T: the V^T fragments of the tile in ring slot `slot` are
-  // read into registers (load_v), then multiplied (pv_regs).
+  // read into registers (load_v), then multiplied (pv_regs).  Fragment
+  // (kg, db) of lane (lg, l16) is V^T[db * 16 + l16][8 keys from
+  // kbase + 32 kg + 8 lg]: two transposing reads, each giving 4 consecutive
+  // keys of dim l16.  For such a read the lanes of a 16-lane group each name
+  // one 8-byte piece of a 4-key x 16-dim block, lane 4 k + c the piece
+  // (key k, dims 4c .. 4c + 3), and lane n receives dim n of the 4 keys.
   typedef bf16x8 VFrag[KG][DB];
-  auto load_v = [&](int slot, VFrag& vf) __attribute__((always_inline)) {
-    const unsigned char* Vt = Vst + slot * V_BYTES;
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) v4i16* lds_v4p;
+  // this lane's byte in the slab layout for key kbase + 8 lg + (l16 >> 2),
+  // dims 4 (l16 & 3) .. + 3; fragments add kg, h and d terms
+  const int v_lane = ((kbase >> 4) + (lg >> 1)) * (32 * D) + (4 * (lg & 1) + (l16 >> 2)) * 32 + (l16 & 3) * 8;
+  // (fragments db0 <= db < db1 only: a step can split the reads in batches
+  // that keep the LDS counter's waits exact)
+  auto load_v = [&](const unsigned char* Vs, VFrag& vf, int db0 = 0, int db1 = D / 16)
+      __attribute__((always_inline)) {
+    const unsigned char* Vt = Vs + v_lane;
 #pragma unroll
     for (int kg = 0; kg < KG; ++kg)
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const int d = db * 16 + l16;
-        const int cc = (kbase + 32 * kg + 8 * lg) >> 3;
-        vf[kg][db] = *reinterpret_cast<const bf16x8*>(Vt + d * (NK * 2) + ((cc ^ vswz(d)) * 16));
+        if (db < db0 || db >= db1) continue;
+        v4i16 h[2];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const unsigned char* at = Vt + kg * (64 * D) + hh * (16 * D) + db * 256;
+          h[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4p)(at));
+        }
+        const v4i16 lo = h[0], hi = h[1];
+        typedef short v8i16 __attribute__((ext_vector_type(8)));
+        const v8i16 w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        vf[kg][db] = __builtin_bit_cast(bf16x8, w);
       }
   };
   auto pv_regs = [&](const VFrag& vf, const PTile& pf) __attribute__((always_inline)) {
@@ -788,9 +787,9 @@ __global__ void __launch_bounds__(WQ * WK * 64) attn_mfma_kernel(AttnArgs a) {
         for (int qb = 0; qb < QB; ++qb)
           o[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[kg][db], pf[qb][kg], o[qb][db], 0, 0, 0);
   };
-  auto pv = [&](int slot, const PTile& pf) __attribute__((always_inline)) {
+  auto pv = [&](const unsigned char* Vs, const PTile& pf) __attribute__((always_inline)) {
     VFrag vf;
-    load_v(slot, vf);
+    load_v(Vs, vf);
     pv_regs(vf, pf);
   };
 
@@ -804,7 +803,7 @@ __global__ void __launch_bounds__(WQ * WK * 64) attn_mfma_kernel(AttnArgs a) {
   };
 
   // ---- main loop --------------------------------------------------------------
-  // K and V^T have rings of S slots each.  Tile k's scores are computed one
+  // K and V have rings of S slots each.  Tile k's scores are computed one
   // iteration ahead, so iteration k reads K(k + 1) and V(k): it runs the score
   // MFMAs of tile k + 1 beside the softmax of tile k, then tile k's P V.  It
   // then issues K(k + S) into K(k)'s slot (last read in iteration k - 1) and
@@ -820,27 +819,25 @@ __global__ void __launch_bounds__(WQ * WK * 64) attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
   for (int k = 0; k < S - 1; ++k)
     if (k < nuse) {
-      issue_k(tile_at(k), k);
-      issue_v(tile_at(k), k);
+      issue_k(tile_at(k), Kst + k * K_BYTES);
+      issue_v(tile_at(k), Vst + k * V_BYTES);
     }
-  if (S - 1 < nuse) issue_k(tile_at(S - 1), S - 1);
+  if (S - 1 < nuse) issue_k(tile_at(S - 1), Kst + (S - 1) * K_BYTES);
   STile sa, sb;
   PTile pf;
   if (nuse > 0) {
     // K(0) has landed once at most the (S - 1) * OPS operations issued after
     // it (V(0), tiles 1 .. S - 2, K(S - 1)) are outstanding; with fewer than S
-    // usable tiles that count is not exact and everything is drained.  (A V^T
-    // tile assembled from plain loads waits for them, and with them for every
-    // operation before it, so the count stays a safe bound.)  Only K(0) is
-    // waited for: the rest of the first tiles land while tile 0's scores are
-    // formed.
+    // usable tiles that count is not exact and everything is drained.  Only
+    // K(0) is waited for: the rest of the first tiles land while tile 0's
+    // scores are formed.
     if (nuse >= S) __builtin_amdgcn_s_waitcnt(vmcnt_imm((S - 1) * OPS));
     else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __builtin_amdgcn_s_waitcnt(lgkmcnt_imm(0));
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    qk(0, sa);
+    qk(Kst, sa);
   }
   // Whole tiles: dense context tiles inside ctx; sparse tiles made only of
   // whole selected blocks (the union is ascending, so only its last block can
@@ -893,7 +890,7 @@ __global__ void __launch_bounds__(WQ * WK * 64) attn_mfma_kernel(AttnArgs a) {
     for (int n = 0; n < V_OPS; ++n) {
       const int p = (tk - 1) * NK + v_key[n];
       const long long boff = SP ? (long long)Uphys[p >> bsh] * blk_elems + head_off : ctab[(p >> bsh) - cb0];
-      vsrc[n] = Vp + boff + (long long)(v_row[n] * bs + (p & bsm));
+      vsrc[n] = Vp + boff + (long long)((p & bsm) * D + v_col[n]);
     }
   };
   // Mask of a whole sparse tile: a row sees an 8-key chunk when it selected
@@ -911,58 +908,75 @@ __global__ void __launch_bounds__(WQ * WK * 64) attn_mfma_kernel(AttnArgs a) {
       }
     }
   };
-  auto tight_step = [&](auto sp_tag, int k, STile& sc, STile& sn) __attribute__((always_inline)) {
+  // A step's DMA destinations (kdst, vdst) and the tiles it reads (krd,
+  // vrd) are distinct ring slots, and the reads' own DMA was waited for by
+  // sync_tiles; the restrict qualifiers say so to the compiler, which would
+  // otherwise drain every DMA in flight before the transposing reads.
+  auto tight_body = [&](auto sp_tag, int k, STile& sc, STile& sn, unsigned char* __restrict__ kdst,
+                        unsigned char* __restrict__ vdst, const unsigned char* __restrict__ krd,
+                        const unsigned char* __restrict__ vrd) __attribute__((always_inline)) {
     constexpr bool SP = decltype(sp_tag)::value;
-    sync_tiles(true);
+#pragma unroll
+    for (int n = 0; n < K_OPS; ++n)
     {
-      unsigned char* kst = Kst + (k % S) * K_BYTES;
+      const unsigned char* src = kpage[n] + koff[n];  // (a named pointer: see issue_k)
+      __builtin_amdgcn_global_load_lds(src, kdst + (wave + NWAVE * n) * 1024, 16, 0, 0);
+    }
 #pragma unroll
-      for (int n = 0; n < K_OPS; ++n)
-      {
-        const unsigned char* src = kpage[n] + koff[n];  // (a named pointer: see issue_k)
-        __builtin_amdgcn_global_load_lds(src, kst + (wave + NWAVE * n) * 1024, 16, 0, 0);
-      }
-      unsigned char* vst = Vst + ((k + S - 1) % S) * V_BYTES;
-#pragma unroll
-      for (int n = 0; n < V_OPS; ++n)
-      {
-        const bf16_bits* src = vsrc[n];
-        __builtin_amdgcn_global_load_lds(src, vst + (wave + NWAVE * n) * 1024, 16, 0, 0);
-      }
+    for (int n = 0; n < V_OPS; ++n)
+    {
+      const bf16_bits* src = vsrc[n];  // (a named pointer: see issue_k)
+      __builtin_amdgcn_global_load_lds(src, vdst + (wave + NWAVE * n) * 1024, 16, 0, 0);
     }
     if (k + 1 < n_tight) tight_sources(sp_tag, t_lo + k + 1 + S);
     if constexpr (SP) sparse_mask(t_lo + k, sc);
     softmax_bound(sc);
-    // the K fragments of tile k + 1 and the V^T fragments of tile k are read
-    // before any MFMA, so their LDS latency is covered; the scheduling
-    // barrier keeps the compiler from sinking the reads to their first use
-    // The next step's block-table reads are scalar loads, which return out of
-    // order; waited for here, they leave only the in-order fragment reads
-    // pending.  At most 15 of those are outstanding at a time (the counter's
-    // range), so each MFMA waits for just its own operands: the K fragments,
-    // the first key half's scores, then the V^T fragments.
+    // The K fragments of tile k + 1 are read before any MFMA and the V^T
+    // fragments of tile k ahead of their MFMAs, so their LDS latency is
+    // covered; the scheduling barriers keep the compiler from sinking the
+    // reads to their first use.  The next step's block-table reads (scalar
+    // loads, which return out of order, and LDS reads) are waited for here,
+    // leaving only the in-order fragment reads pending.  At most 15 of those
+    // are outstanding at a time (the counter's range), so each MFMA waits for
+    // just its own operands.
     __builtin_amdgcn_s_waitcnt(lgkmcnt_imm(0));
     KFrag kf;
-    load_k((k + 1) % S, kf);
+    load_k(krd, kf);
     __builtin_amdgcn_sched_barrier(0);
     qk_regs(kf, sn, 1);
+    // the V^T fragments take two transposing reads each: half of them before
+    // the second key half's score MFMAs, half after, so at most 15 LDS reads
+    // are outstanding when an MFMA waits for its operands
     VFrag vf;
-    load_v(k % S, vf);
+    load_v(vrd, vf, 0, DB / 2);
     __builtin_amdgcn_sched_barrier(0);
     qk_regs(kf, sn, 2);
+    load_v(vrd, vf, DB / 2, DB);
+    __builtin_amdgcn_sched_barrier(0);
     exp_tile(sc, pf);
     pv_regs(vf, pf);
   };
-  auto general_step = [&](int k, STile& sc, STile& sn) __attribute__((always_inline)) {
-    sync_tiles(k + S - 1 < nuse);
-    if (k + S < nuse) issue_k(tile_at(k + S), k % S);
-    if (k + S - 1 < nuse) issue_v(tile_at(k + S - 1), (k + S - 1) % S);
+  auto tight_step = [&](auto sp_tag, int k, STile& sc, STile& sn) __attribute__((always_inline)) {
+    sync_tiles(true);
+    tight_body(sp_tag, k, sc, sn, Kst + (k % S) * K_BYTES, Vst + ((k + S - 1) % S) * V_BYTES,
+               Kst + ((k + 1) % S) * K_BYTES, Vst + (k % S) * V_BYTES);
+  };
+  auto general_body = [&](int k, STile& sc, STile& sn, unsigned char* __restrict__ kdst,
+                          unsigned char* __restrict__ vdst, const unsigned char* __restrict__ krd,
+                          const unsigned char* __restrict__ vrd) __attribute__((always_inline)) {
+    if (k + S < nuse) issue_k(tile_at(k + S), kdst);
+    if (k + S - 1 < nuse) issue_v(tile_at(k + S - 1), vdst);
     const int t = tile_at(k);
     if (!dense_full(t)) mask_tile(t, sc);
     softmax_bound(sc);
-    if (k + 1 < nuse) qk((k + 1) % S, sn);
+    if (k + 1 < nuse) qk(krd, sn);
     exp_tile(sc, pf);
-    pv(k % S, pf);
+    pv(vrd, pf);
+  };
+  auto general_step = [&](int k, STile& sc, STile& sn) __attribute__((always_inline)) {
+    sync_tiles(k + S - 1 < nuse);
+    general_body(k, sc, sn, Kst + (k % S) * K_BYTES, Vst + ((k + S - 1) % S) * V_BYTES,
+                 Kst + ((k + 1) % S) * K_BYTES, Vst + (k % S) * V_BYTES);
   };
   int k = 0;
   // (two copies of the loop: dense and sparse, each specialised)

@@ -4,7 +4,7 @@
 // position ctx_b + j takes the K/V held at ctx_b + path[j], then ctx_b grows by
 // the path length.  One workgroup per (sequence, KV head) copies the path in
 // groups of JG entries: every thread first loads its share of the group (16-byte
-// K chunks and V^T elements) into registers, the workgroup synchronises, then
+// chunks of the K and V rows) into registers, the workgroup synchronises, then
 // the stores are issued.  The path is increasing with path[j] >= j, so a
 // group's destinations (positions < ctx + j0 + JG) never overlap the sources of
 // a later group (positions >= ctx + j0 + JG): the copy is safe in place.
@@ -16,8 +16,7 @@
 namespace sdtree {
 
 constexpr int kCommitThreads = 256;
-constexpr int kKRegs = 4;        // 16-byte K chunks per thread per group
-constexpr int kVRegs = 24;       // V^T elements per thread per group
+constexpr int kKRegs = 4;        // 16-byte chunks of K (and of V) per thread per group
 constexpr int kMaxCommitBlocks = kMaxCommitT / 8 + 2;  // blocks of slots [ctx, ctx + T), bs >= 8
 
 __global__ void __launch_bounds__(kCommitThreads) commit_kernel(CommitArgs a) {
@@ -59,62 +58,44 @@ __global__ void __launch_bounds__(kCommitThreads) commit_kernel(CommitArgs a) {
     return;
   }
 
-  // Threads own fixed columns of an entry: a 16-byte K chunk (kch per row) or
-  // one V^T element (D per column).
-  const int kch = a.D * a.esize / 16;                 // 16-byte chunks per K row (power of 2)
+  // Threads own a fixed 16-byte column chunk (kch per row) of the K and V
+  // rows of an entry.
+  const int kch = a.D * a.esize / 16;                 // 16-byte chunks per row (power of 2)
   const int rowb = a.D * a.esize;
   unsigned char* K = reinterpret_cast<unsigned char*>(a.k);
   unsigned char* V = reinterpret_cast<unsigned char*>(a.v);
-  const int kstep = kCommitThreads / kch, vstep = kCommitThreads / a.D;
+  const int kstep = kCommitThreads / kch;
   const int kcol = tid % kch, ku0 = tid / kch;
-  const int vcol = tid % a.D, vu0 = tid / a.D;
-  const int JG = min(kKRegs * kstep, kVRegs * vstep);
+  const int JG = kKRegs * kstep;
   const long long blk_bytes = (long long)a.Hkv * a.bs * rowb;
-  const long long head_k = (long long)g * a.bs * rowb;
-  const long long head_v = (long long)g * a.D * a.bs * a.esize;
-  // byte offsets of slot p's K row and V^T column (head g)
-  auto k_at = [&](int p) -> long long {
-    return (long long)s_blk[p / a.bs - lo] * blk_bytes + head_k + (long long)(p % a.bs) * rowb;
+  const long long head = (long long)g * a.bs * rowb;
+  // byte offset of slot p's row (head g), K and V alike
+  auto row_at = [&](int p) -> long long {
+    return (long long)s_blk[p / a.bs - lo] * blk_bytes + head + (long long)(p % a.bs) * rowb;
   };
-  auto v_at = [&](int p) -> long long {
-    return (long long)s_blk[p / a.bs - lo] * blk_bytes + head_v + (long long)(p % a.bs) * a.esize;
-  };
-  const long long kc_off = (long long)kcol * 16;
-  const long long vc_off = (long long)vcol * a.bs * a.esize;
+  const long long c_off = (long long)kcol * 16;
   for (int j0 = 0; j0 < L; j0 += JG) {
     const int nj = min(JG, L - j0);
-    uint4 kr[kKRegs];
-    uint32_t vr[kVRegs];
+    uint4 kr[kKRegs], vr[kKRegs];
 #pragma unroll
     for (int r = 0; r < kKRegs; ++r) {
       const int jj = ku0 + r * kstep;
       kr[r] = make_uint4(0, 0, 0, 0);
-      if (jj < nj && s_path[j0 + jj] != j0 + jj)
-        kr[r] = *reinterpret_cast<const uint4*>(K + k_at(ctx + s_path[j0 + jj]) + kc_off);
-    }
-#pragma unroll
-    for (int r = 0; r < kVRegs; ++r) {
-      const int jj = vu0 + r * vstep;
-      vr[r] = 0;
+      vr[r] = make_uint4(0, 0, 0, 0);
       if (jj < nj && s_path[j0 + jj] != j0 + jj) {
-        const unsigned char* src = V + v_at(ctx + s_path[j0 + jj]) + vc_off;
-        vr[r] = a.esize == 2 ? *reinterpret_cast<const uint16_t*>(src) : *reinterpret_cast<const uint32_t*>(src);
+        const long long src = row_at(ctx + s_path[j0 + jj]) + c_off;
+        kr[r] = *reinterpret_cast<const uint4*>(K + src);
+        vr[r] = *reinterpret_cast<const uint4*>(V + src);
       }
     }
     __syncthreads();
 #pragma unroll
     for (int r = 0; r < kKRegs; ++r) {
       const int jj = ku0 + r * kstep;
-      if (jj < nj && s_path[j0 + jj] != j0 + jj)
-        *reinterpret_cast<uint4*>(K + k_at(ctx + j0 + jj) + kc_off) = kr[r];
-    }
-#pragma unroll
-    for (int r = 0; r < kVRegs; ++r) {
-      const int jj = vu0 + r * vstep;
       if (jj < nj && s_path[j0 + jj] != j0 + jj) {
-        unsigned char* dst = V + v_at(ctx + j0 + jj) + vc_off;
-        if (a.esize == 2) *reinterpret_cast<uint16_t*>(dst) = (uint16_t)vr[r];
-        else *reinterpret_cast<uint32_t*>(dst) = vr[r];
+        const long long dst = row_at(ctx + j0 + jj) + c_off;
+        *reinterpret_cast<uint4*>(K + dst) = kr[r];
+        *reinterpret_cast<uint4*>(V + dst) = vr[r];
       }
     }
     __syncthreads();

@@ -94,7 +94,7 @@ static AttnPlan plan_attn(const sd_shape* s, int ksel, bool sparse) {
   p.n_splits = (ntiles + p.tps - 1) / p.tps;
   p.ct_max = (int)(((long long)p.tps * p.NK + s->bs - 1) / s->bs) + 2;
   p.tt_max = (s->T + s->bs - 1) / s->bs + 2;
-  // LDS: the K / V^T ring, tree-tile flags and list, block-id tables, staged
+  // LDS: the K / V ring, tree-tile flags and list, block-id tables, staged
   // ancestor words, sparse tables.  The key-slice merge reuses the ring.
   const size_t stage = (size_t)p.NK * p.D * 2 * 2;
   const int nnodes = (p.rows + G - 1) / G + 1;
