@@ -520,6 +520,28 @@ def measure_workload(w, label, n_calls=40):
     return e
 
 
+def tree_build_on_gpu(w):
+    """The 2048-node tree built on the GPU (sd_tree_build) from the drafter
+    table the input generator uses: its time (median of 5 builds, each
+    waiting once per round) and whether it equals the tree the step verifies."""
+    from synth.inputs import _normals, _rng, S_DRAFT
+    torch, cfg = w.torch, w.cfg
+    d = _normals(_rng(cfg, S_DRAFT), (cfg.T, cfg.V), cfg.logit_sigma, "f32")
+    dt = torch.from_numpy(d).cuda()
+    root = int(w.x.tree_token[0, 0])
+    ts = []
+    for _ in range(6):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        p, tk, _, rounds = w.tva.tree_build(dt, 1.0, root)
+        torch.cuda.synchronize()
+        ts.append(time.perf_counter() - t0)
+    same = bool(np.array_equal(p.cpu().numpy(), w.x.tree_parent[0]) and
+                np.array_equal(tk.cpu().numpy(), w.x.tree_token[0]))
+    return {"tree_build_us": round(float(np.median(ts[1:])) * 1e6, 1), "tree_build_rounds": rounds,
+            "tree_build_equals_input_tree": same}
+
+
 def secondary_workloads():
     """The other four workloads, each measured as measure_workload does; the
     sparse workload three ways (dense attention, per-row selection, shared
@@ -540,6 +562,7 @@ def secondary_workloads():
                 ex = executed_mfma_flops_256x32(w.cfg, w.x)
                 e["executed_mfma_flops_per_call"] = int(ex)
                 e["executed_over_algorithmic_flops"] = round(ex / e["flops_per_call"], 4)
+                e.update(tree_build_on_gpu(w))
             out.append(e)
         print(json.dumps({"secondary_done": name}), file=sys.stderr, flush=True)
         del w

@@ -17,7 +17,8 @@
  *   sd_block_sums, sd_block_sums_append, sd_topk_blocks_cached
  *                        the same selection from per-block key sums kept as
  *                        the context grows;
- *   sd_tree_expand       one batched expansion step of the draft-tree search.
+ *   sd_tree_expand       one batched expansion step of the draft-tree search;
+ *   sd_tree_build        the whole best-first draft-tree search to a budget.
  *
  * Conventions shared by every call
  *   - Tensor arguments are DEVICE pointers owned by the caller.  The library
@@ -80,6 +81,8 @@ typedef enum sd_dtype { SD_F32 = 0, SD_BF16 = 1 } sd_dtype;
 #define SD_ERR_CAPACITY   0x4u   /* ctx_b + T exceeds max_blocks * bs, or ctx_b < 0 */
 #define SD_ERR_TOKEN      0x8u   /* tree token outside [0, V) */
 #define SD_ERR_SELECTION  0x10u  /* sel_blocks entry not a context block / not ascending */
+#define SD_ERR_BUILD      0x40u  /* sd_tree_build: a round's float32 pre-selection missed a candidate
+                                    (more than its margin within float32 rounding of the cut) */
 #define SD_ERR_TIMEOUT    0x20u  /* a cross-workgroup wait gave up; results of the call are invalid
                                     and the workspace must be zero-filled again */
 
@@ -111,8 +114,16 @@ typedef struct sd_expand_shape {
   int32_t logit_dtype;  /* sd_dtype of draft_logits */
 } sd_expand_shape;
 
+/* Shape of a draft-tree build: T nodes (the budget, root included), a drafter
+   logits table of T rows of V. */
+typedef struct sd_build_shape {
+  int32_t T;
+  int32_t V;
+  int32_t logit_dtype;  /* SD_F32 or SD_BF16 */
+} sd_build_shape;
+
 enum { SD_CALL_ATTN = 1, SD_CALL_ACCEPT = 2, SD_CALL_TOPK = 3, SD_CALL_COMMIT = 4, SD_CALL_BLOCK_SUMS = 5,
-       SD_CALL_EXPAND = 6 };
+       SD_CALL_EXPAND = 6, SD_CALL_BUILD = 7 };
 
 /*
  * Tree-masked grouped-query attention over the paged cache.
@@ -310,10 +321,42 @@ sd_status sd_tree_expand(const sd_expand_shape* shape, const void* draft_logits,
                          int32_t* out_token, float* out_score, void* ws, size_t ws_bytes,
                          void* stream);
 
+/*
+ * The draft-tree search to a budget (SpecExec page, "Approach": the tree is
+ * built deterministically from the continuations of highest cumulative
+ * probability by a parallel shortest-path search with the drafter).  Node
+ * ids follow the order a sequential best-first search would take the nodes:
+ * after ids 0 .. n - 1 the next node is the best child of those nodes not
+ * yet taken, by (cumulative log-probability descending, parent id, token),
+ * where the log-probability of token x after node e is
+ * log_softmax(draft_logits[e] / temperature)[x] in float64 and the root has
+ * cumulative log-probability 0.  Row n of draft_logits is the drafter's
+ * output at the node that receives id n (the caller's drafter fills rows in
+ * that order).
+ *   The search runs in rounds that each take the longest prefix of the next
+ *   candidates that the sequential search would take in a row (see
+ *   csrc/build.hip); a round selects candidates in float32 with a margin of
+ *   256 and orders them in float64.  The call waits on `stream` once per
+ *   round (it reads the node count back) and returns when the tree is full.
+ *   draft_logits  [T, V] in logit_dtype (finite values).
+ *   parent, token int32 [T]: parent[0] = -1, token[0] = root_token;
+ *                 0 <= parent[i] < i.   cum_logp  float64 [T].
+ *   rounds        host pointer, may be NULL: the number of rounds run.
+ *   Limits: 1 <= T <= 3841 (T - 1 + 256 candidates per round at most 4096),
+ *   T * V < 2^32, temperature > 0, 0 <= root_token < V.  A round whose
+ *   pre-selection missed a candidate stops the build and sets SD_ERR_BUILD.
+ *   ws >= sd_workspace_bytes(SD_CALL_BUILD, shape, 0), zero-filled before its
+ *   first use.
+ */
+sd_status sd_tree_build(const sd_build_shape* shape, const void* draft_logits, float temperature,
+                        int32_t root_token, int32_t* parent, int32_t* token, double* cum_logp,
+                        int32_t* rounds, void* ws, size_t ws_bytes, void* stream);
+
 /* Workspace bytes a call needs; `shape` points to an sd_shape (ATTN, TOPK,
  * COMMIT, BLOCK_SUMS), an sd_accept_shape (ACCEPT, also for
- * sd_accept_commit) or an sd_expand_shape (EXPAND); `extra` is k_sel (ATTN,
- * 0 = dense) or k (TOPK, EXPAND).  0 on bad input. */
+ * sd_accept_commit), an sd_expand_shape (EXPAND) or an sd_build_shape
+ * (BUILD); `extra` is k_sel (ATTN, 0 = dense) or k (TOPK, EXPAND).  0 on bad
+ * input. */
 size_t sd_workspace_bytes(int32_t call_id, const void* shape, int32_t extra);
 
 /* Synchronises `stream`, reads the sticky bits into *bits (may be NULL), clears

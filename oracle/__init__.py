@@ -22,6 +22,8 @@ statement of each step:
   tokens).
 * ``expand``     -- one batched step of the draft-tree search: the best
   children by cumulative log-probability (SpecExec page, "Approach").
+* ``build``      -- the whole draft-tree search to a budget: sequential
+  best-first over cumulative log-probability (same section).
 
 Pins (tests/test_oracle_*.py) tie each function to something other than
 itself: torch's scaled_dot_product_attention, closed forms, brute force over
@@ -37,4 +39,5 @@ from .commit import commit  # noqa: F401
 from .topk import (append_block_sums, block_means, block_scores, block_sums,  # noqa: F401
                    means_from_sums, pooled_query, topk_blocks, topk_blocks_shared)
 from .expand import expand  # noqa: F401
+from .build import build_tree, log_softmax_rows  # noqa: F401
 from .codec import decode  # noqa: F401

@@ -17,7 +17,7 @@ def setup_module():
 
 def test_exports_every_declared_function():
     names = _lib.declared_functions()
-    assert len(names) == 14
+    assert len(names) == 15
     for n in names:
         assert hasattr(L, n), n
 
@@ -130,6 +130,28 @@ def test_accept_commit_noalloc_rejects_bad_arguments():
     assert call(_lib.SdAcceptShape(2, 8, 100, 5, 8), kv) == 3
     assert call(ok, kv, tau=-1.0) == 1
     assert call(ok, kv, status=None) == 1
+
+
+def test_tree_build_rejects_bad_arguments():
+    """Host checks of sd_tree_build, before any HIP call."""
+    def call(T=64, V=100, dt=0, tau=1.0, root=0, ws=1 << 30, draft=FAKE, parent=FAKE):
+        s = _lib.SdBuildShape(T, V, dt)
+        return L.sd_tree_build(ctypes.byref(s), draft, tau, root, parent, FAKE, FAKE, None, FAKE, ws, None)
+    assert call(T=0) == 2
+    assert call(V=0) == 2
+    assert call(dt=7) == 3
+    assert call(T=3842) == 4                      # T - 1 + 256 candidates would exceed 4096
+    assert call(T=3000, V=2000000) == 4           # T * V >= 2^32
+    assert call(tau=0.0) == 1
+    assert call(tau=float("inf")) == 1
+    assert call(root=100) == 1
+    assert call(root=-1) == 1
+    assert call(draft=None) == 1
+    assert call(parent=None) == 1
+    assert call(ws=1000) == 5
+    need = L.sd_workspace_bytes(7, ctypes.byref(_lib.SdBuildShape(2048, 32000, 0)), 0)
+    assert need > 2048 * (8 + 8 + 4)
+    assert L.sd_workspace_bytes(7, ctypes.byref(_lib.SdBuildShape(5000, 100, 0)), 0) == 0
 
 
 def test_block_sums_calls_reject_bad_arguments():

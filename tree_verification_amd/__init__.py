@@ -8,5 +8,6 @@ verification -- as hand-written HIP kernels behind a small C ABI
 """
 from ._lib import (  # noqa: F401
     SdError, accept, accept_commit, accept_commit_noalloc, block_sums, block_sums_append, device_status, kv_commit, lib,
-    topk_blocks, topk_blocks_cached, topk_blocks_shared, tree_expand, tree_verify_attn, workspace_bytes,
+    topk_blocks, topk_blocks_cached, topk_blocks_shared, tree_build, tree_expand, tree_verify_attn,
+    workspace_bytes,
 )

@@ -16,12 +16,12 @@ LIB_PATH = os.path.join(_HERE, "libsdtree.so")
 HEADER = os.path.join(os.path.dirname(_HERE), "include", "sdtree.h")
 
 SD_F32, SD_BF16 = 0, 1
-SD_CALL_ATTN, SD_CALL_ACCEPT, SD_CALL_TOPK, SD_CALL_COMMIT, SD_CALL_BLOCK_SUMS, SD_CALL_EXPAND = \
-    1, 2, 3, 4, 5, 6
+SD_CALL_ATTN, SD_CALL_ACCEPT, SD_CALL_TOPK, SD_CALL_COMMIT, SD_CALL_BLOCK_SUMS, SD_CALL_EXPAND, \
+    SD_CALL_BUILD = 1, 2, 3, 4, 5, 6, 7
 STATUS = {0: "SD_OK", 1: "SD_INVALID_ARG", 2: "SD_BAD_SHAPE", 3: "SD_BAD_DTYPE",
           4: "SD_UNSUPPORTED", 5: "SD_CAPACITY", 6: "SD_HIP_ERROR", 7: "SD_DEVICE_DATA_ERROR"}
 ERR_BITS = {0x1: "parent", 0x2: "block", 0x4: "capacity", 0x8: "token", 0x10: "selection",
-            0x20: "timeout"}
+            0x20: "timeout", 0x40: "build"}
 
 
 class SdShape(ctypes.Structure):
@@ -39,6 +39,10 @@ class SdAcceptShape(ctypes.Structure):
 
 class SdExpandShape(ctypes.Structure):
     _fields_ = [("E", ctypes.c_int32), ("V", ctypes.c_int32), ("logit_dtype", ctypes.c_int32)]
+
+
+class SdBuildShape(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("V", ctypes.c_int32), ("logit_dtype", ctypes.c_int32)]
 
 
 class SdError(RuntimeError):
@@ -81,6 +85,8 @@ def lib():
         "sd_tree_expand": [ctypes.POINTER(SdExpandShape), _P, _P, ctypes.c_float, i32, _P, _P, _P, _P, sz,
                            _P],
         "sd_block_sums_append": [ctypes.POINTER(SdShape), _P, _P, _P, _P, _P, _P, sz, _P],
+        "sd_tree_build": [ctypes.POINTER(SdBuildShape), _P, ctypes.c_float, i32, _P, _P, _P,
+                          ctypes.POINTER(ctypes.c_int32), _P, sz, _P],
         "sd_device_status": [_P, _P, ctypes.POINTER(ctypes.c_uint32)],
         "sd_workspace_bytes": [i32, _P, i32],
         "sd_status_str": [i32],
@@ -279,6 +285,27 @@ def tree_expand(draft_logits, cum_logp, temperature, k, ws=None):
         ctypes.byref(shape), _ptr(draft_logits), _ptr(cum_logp), float(temperature), int(k), _ptr(row),
         _ptr(tok), _ptr(score), _ptr(ws), ws.numel(), _stream(dev)))
     return row, tok, score
+
+
+def tree_build(draft_logits, temperature, root_token=0, ws=None):
+    """sd_tree_build: the best-first draft tree of T = draft_logits.shape[0]
+    nodes; returns (parent int32 [T], token int32 [T], cum_logp float64 [T],
+    rounds)."""
+    T, V = draft_logits.shape
+    shape = SdBuildShape(T, V, _dtype_code[draft_logits.dtype])
+    dev = draft_logits.device
+    parent = torch.empty(T, dtype=torch.int32, device=dev)
+    token = torch.empty(T, dtype=torch.int32, device=dev)
+    cum = torch.empty(T, dtype=torch.float64, device=dev)
+    need = workspace_bytes(SD_CALL_BUILD, shape)
+    if need == 0:
+        raise SdError("sd_workspace_bytes", 2)
+    ws = _WS.get(dev, need, SD_CALL_BUILD) if ws is None else ws
+    rounds = ctypes.c_int32(0)
+    _check("sd_tree_build", lib().sd_tree_build(
+        ctypes.byref(shape), _ptr(draft_logits), float(temperature), int(root_token), _ptr(parent),
+        _ptr(token), _ptr(cum), ctypes.byref(rounds), _ptr(ws), ws.numel(), _stream(dev)))
+    return parent, token, cum, rounds.value
 
 
 def _sums_shape(k_pages, block_table, ctx_lens):

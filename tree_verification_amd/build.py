@@ -27,7 +27,7 @@ COMMON = [
     "-Wno-unused-command-line-argument",
 ]
 PER_FILE = {"topk.hip": ["-ffp-contract=off"], "expand.hip": ["-ffp-contract=off"]}
-SOURCES = ["sdtree.hip", "attn.hip", "accept.hip", "commit.hip", "topk.hip", "expand.hip"]
+SOURCES = ["sdtree.hip", "attn.hip", "accept.hip", "commit.hip", "topk.hip", "expand.hip", "build.hip"]
 
 
 def _compile(src, verbose):

@@ -175,8 +175,29 @@ struct ExpandArgs {
   float* out_score;
 };
 
+// Best-first construction of a draft tree on the GPU.
+struct BuildArgs {
+  const void* logits;   // [T][V] drafter logits, row n = node n's
+  int T, V;
+  float tau;
+  int root_token;
+  int margin;           // extra candidates of the float32 pre-selection
+  int32_t* parent;      // [T] out
+  int32_t* token;       // [T] out
+  double* cum;          // [T] out: cumulative log-probability
+  float* cum32;         // [T] workspace: float32 copy for the pre-selection
+  double* rmax;         // [T] workspace: row max of l / tau
+  double* rlse;         // [T] workspace: row log-sum-exp after the max
+  int32_t* cand_row;    // [k] workspace: pre-selected candidates
+  int32_t* cand_token;
+  int* n_dev;           // nodes in the tree
+  uint32_t* status;
+};
+
 // Launchers (one per kernel family).
 hipError_t launch_expand(const ExpandArgs& a, bool f32, hipStream_t st);
+hipError_t run_tree_build(const BuildArgs& a, const ExpandArgs& ex0, bool f32, hipStream_t st,
+                          int* rounds);
 hipError_t launch_anc_mask(const int32_t* parent, int T, int W64, int n_trees, uint64_t* anc,
                            uint32_t* status, hipStream_t st);
 hipError_t launch_attn_valu(const AttnArgs& a, bool f32, hipStream_t st);

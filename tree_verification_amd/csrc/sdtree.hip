@@ -156,6 +156,39 @@ static size_t expand_ws(const sd_expand_shape* s, int32_t k, size_t* off, size_t
   return align_up(kk + (size_t)k * 8, 256);
 }
 
+constexpr int kBuildMargin = 256;
+
+static sd_status check_build(const sd_build_shape* s) {
+  if (!s) return SD_INVALID_ARG;
+  if (s->T < 1 || s->V < 1) return SD_BAD_SHAPE;
+  if (s->logit_dtype != SD_F32 && s->logit_dtype != SD_BF16) return SD_BAD_DTYPE;
+  if ((long long)s->T * s->V >= 0xFFFFFFFFll) return SD_UNSUPPORTED;
+  if (s->T - 1 + kBuildMargin > kMaxExpandK) return SD_UNSUPPORTED;
+  return SD_OK;
+}
+
+// Build scratch: the expansion step's scratch for T rows and the round's
+// candidate count, then per-row float64 statistics, the float32 copy of the
+// cumulative log-probabilities, the candidates and the node counter.
+struct BuildLayout {
+  size_t exp_off, exp_hist, exp_cnt, exp_keys, rmax, rlse, cum32, crow, ctok, cscore, ndev, total;
+};
+static BuildLayout build_layout(const sd_build_shape* s) {
+  BuildLayout L;
+  sd_expand_shape es{s->T, s->V, s->logit_dtype};
+  const int kc = s->T - 1 + kBuildMargin;
+  const size_t e = expand_ws(&es, kc, &L.exp_off, &L.exp_hist, &L.exp_cnt, &L.exp_keys);
+  L.rmax = align_up(e, 256);
+  L.rlse = align_up(L.rmax + (size_t)s->T * 8, 256);
+  L.cum32 = align_up(L.rlse + (size_t)s->T * 8, 256);
+  L.crow = align_up(L.cum32 + (size_t)s->T * 4, 256);
+  L.ctok = align_up(L.crow + (size_t)kc * 4, 256);
+  L.cscore = align_up(L.ctok + (size_t)kc * 4, 256);
+  L.ndev = align_up(L.cscore + (size_t)kc * 4, 256);
+  L.total = L.ndev + 256;
+  return L;
+}
+
 static sd_status check_expand(const sd_expand_shape* s, int32_t k) {
   if (!s) return SD_INVALID_ARG;
   if (s->E < 1 || s->V < 1) return SD_BAD_SHAPE;
@@ -224,6 +257,10 @@ size_t sd_workspace_bytes(int32_t call_id, const void* shape, int32_t extra) {
   if (call_id == SD_CALL_EXPAND) {
     const sd_expand_shape* s = static_cast<const sd_expand_shape*>(shape);
     return check_expand(s, extra) == SD_OK ? expand_ws(s, extra, nullptr, nullptr, nullptr, nullptr) : 0;
+  }
+  if (call_id == SD_CALL_BUILD) {
+    const sd_build_shape* s = static_cast<const sd_build_shape*>(shape);
+    return check_build(s) == SD_OK ? build_layout(s).total : 0;
   }
   if (call_id == SD_CALL_BLOCK_SUMS) {
     const sd_shape* s = static_cast<const sd_shape*>(shape);
@@ -526,6 +563,45 @@ sd_status sd_tree_expand(const sd_expand_shape* shape, const void* draft_logits,
   a.keys = reinterpret_cast<unsigned long long*>(w + kk);
   a.out_row = out_row; a.out_token = out_token; a.out_score = out_score;
   return hip_status(launch_expand(a, shape->logit_dtype == SD_F32, static_cast<hipStream_t>(stream)));
+}
+
+sd_status sd_tree_build(const sd_build_shape* shape, const void* draft_logits, float temperature,
+                        int32_t root_token, int32_t* parent, int32_t* token, double* cum_logp,
+                        int32_t* rounds, void* ws, size_t ws_bytes, void* stream) {
+  const sd_status st = check_build(shape);
+  if (st != SD_OK) return st;
+  if (!(temperature > 0.f) || isinf(temperature)) return SD_INVALID_ARG;
+  if (root_token < 0 || root_token >= shape->V) return SD_INVALID_ARG;
+  if (!draft_logits || !parent || !token || !cum_logp || !ws) return SD_INVALID_ARG;
+  const BuildLayout L = build_layout(shape);
+  if (ws_bytes < L.total) return SD_CAPACITY;
+  unsigned char* w = static_cast<unsigned char*>(ws);
+  BuildArgs a;
+  memset(&a, 0, sizeof(a));
+  a.logits = draft_logits; a.T = shape->T; a.V = shape->V; a.tau = temperature;
+  a.root_token = root_token; a.margin = kBuildMargin;
+  a.parent = parent; a.token = token; a.cum = cum_logp;
+  a.cum32 = reinterpret_cast<float*>(w + L.cum32);
+  a.rmax = reinterpret_cast<double*>(w + L.rmax);
+  a.rlse = reinterpret_cast<double*>(w + L.rlse);
+  a.cand_row = reinterpret_cast<int32_t*>(w + L.crow);
+  a.cand_token = reinterpret_cast<int32_t*>(w + L.ctok);
+  a.n_dev = reinterpret_cast<int*>(w + L.ndev);
+  a.status = reinterpret_cast<uint32_t*>(w);
+  ExpandArgs ex;
+  memset(&ex, 0, sizeof(ex));
+  ex.logits = draft_logits; ex.cum = a.cum32; ex.inv_tau = 1.f / temperature;
+  ex.V = shape->V;
+  ex.off = reinterpret_cast<float*>(w + L.exp_off);
+  ex.hist = reinterpret_cast<uint32_t*>(w + L.exp_hist);
+  ex.count = reinterpret_cast<uint32_t*>(w + L.exp_cnt);
+  ex.keys = reinterpret_cast<unsigned long long*>(w + L.exp_keys);
+  ex.out_row = a.cand_row; ex.out_token = a.cand_token;
+  ex.out_score = reinterpret_cast<float*>(w + L.cscore);
+  int r = 0;
+  const hipError_t e = run_tree_build(a, ex, shape->logit_dtype == SD_F32, static_cast<hipStream_t>(stream), &r);
+  if (rounds) *rounds = r;
+  return hip_status(e);
 }
 
 sd_status sd_device_status(void* ws, void* stream, uint32_t* bits) {
