@@ -239,7 +239,6 @@ def test_commit_bit_exact(name):
     c = small_variant(name)
     _say("commit %s" % name)
     x, d, path, plen = _commit_case(c)
-    # force a long aliasing path on sequence 0 when the tree has a deep chain
     K, V, ctx2 = oracle.commit(x.k_pages, x.v_pages, x.block_table, x.ctx_lens, path, plen, c.bs)
     tva.kv_commit(d["k"], d["v"], d["table"], d["ctx"], dev_tensor(path), dev_tensor(plen))
     torch.cuda.synchronize()
