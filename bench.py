@@ -474,6 +474,14 @@ def time_calls(w, reps=10):
         ctx_new = w.ctx + n_new
         res["block_sums_append_5_us"] = loop(lambda: tva.block_sums_append(w.k, w.table, ctx_new, n_new,
                                                                            scratch))
+
+        def accept_commit_sums():
+            # the acceptance, the commit and the sums' extension in one launch
+            # (the scratch sums' values do not matter for the timing)
+            tva.accept_commit(w.logits, w.draft, w.parent, w.token, w.unif, w.tau, w.k, w.v, w.table,
+                              w.ctx, path=w.path, path_len=w.plen, bonus=w.bonus, sums=scratch)
+            w.ctx.copy_(w.ctx0)
+        res["accept_commit_sums_plus_restore_us"] = loop(accept_commit_sums)
     return {k: round(v, 1) for k, v in res.items()}
 
 

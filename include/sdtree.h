@@ -176,15 +176,22 @@ sd_status sd_accept(const sd_accept_shape* shape, const void* target_logits,
  * K/V of position ctx_b + path[b][j] (every KV head), then ctx_lens[b] +=
  * path_len[b].  In place; path must be increasing with path[b][0] == 0 (as
  * sd_accept produces), which makes the in-place copy safe.  k_pages, v_pages
- * and ctx_lens are modified.  A sequence whose path or table fails validation
+ * and ctx_lens are modified.
+ *   block_sums  float32 [num_blocks, Hkv, D] or NULL: kept block key sums
+ *               (sd_block_sums), current for the old lengths; the commit then
+ *               extends them over the committed positions exactly as
+ *               sd_block_sums_append would (sparse-verification page,
+ *               "Methodology": the blocks' summaries are maintained as the
+ *               context grows, so selection never reads K).  A sequence whose path or table fails validation
  * is left untouched and a sticky bit is set in ws (>= sd_workspace_bytes(
  * SD_CALL_COMMIT, shape, 0) bytes: the status word and one completion counter
  * per sequence, which every call leaves at zero).
  *   path      int32 [B, T] as produced by sd_accept; path_len int32 [B].
  */
 sd_status sd_kv_commit(const sd_shape* shape, void* k_pages, void* v_pages,
-                       const int32_t* block_table, int32_t* ctx_lens, const int32_t* path,
-                       const int32_t* path_len, void* ws, size_t ws_bytes, void* stream);
+                       const int32_t* block_table, int32_t* ctx_lens, float* block_sums,
+                       const int32_t* path, const int32_t* path_len, void* ws, size_t ws_bytes,
+                       void* stream);
 
 /*
  * sd_accept followed by sd_kv_commit of the accepted paths, in one launch:
@@ -198,14 +205,15 @@ sd_status sd_kv_commit(const sd_shape* shape, void* k_pages, void* v_pages,
  * (>= sd_workspace_bytes(SD_CALL_ACCEPT, shape, 0)); a sequence whose tree
  * fails validation gets path_len 0 and commits nothing, and one whose slots
  * [ctx, ctx + T) fail the commit's checks keeps its cache and length.
+ * block_sums (may be NULL) as for sd_kv_commit: extended in the same launch.
  */
 sd_status sd_accept_commit(const sd_accept_shape* shape, const sd_shape* kv_shape,
                            const void* target_logits, const float* draft_probs,
                            const int32_t* tree_parent, const int32_t* tree_token,
                            const float* uniforms, float temperature, int32_t* path,
                            int32_t* path_len, int32_t* bonus, void* k_pages, void* v_pages,
-                           const int32_t* block_table, int32_t* ctx_lens, void* ws,
-                           size_t ws_bytes, void* stream);
+                           const int32_t* block_table, int32_t* ctx_lens, float* block_sums,
+                           void* ws, size_t ws_bytes, void* stream);
 
 /*
  * sd_accept_commit for callers that cannot allocate device memory or pass a
@@ -231,7 +239,7 @@ sd_status sd_accept_commit_noalloc(const sd_accept_shape* shape, const sd_shape*
                                    const float* uniforms, float temperature, int32_t* path,
                                    int32_t* path_len, int32_t* bonus, void* k_pages,
                                    void* v_pages, const int32_t* block_table, int32_t* ctx_lens,
-                                   uint32_t* status, void* stream);
+                                   float* block_sums, uint32_t* status, void* stream);
 
 /*
  * Top-k context blocks per query (sparse-verification page, "Methodology":

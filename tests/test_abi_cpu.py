@@ -101,7 +101,7 @@ def test_accept_commit_rejects_bad_arguments():
     def call(shape, kv, tau=0.8, kpages=FAKE, ws=256):
         return L.sd_accept_commit(ctypes.byref(shape), None if kv is None else ctypes.byref(kv), FAKE,
                                   FAKE, FAKE, FAKE, FAKE, tau, FAKE, FAKE, FAKE, kpages, FAKE, FAKE,
-                                  FAKE, FAKE, ws, None)
+                                  FAKE, None, FAKE, ws, None)
     ok = _lib.SdAcceptShape(2, 8, 100, 1, 8)
     kv = _shape(B=2, T=8, Hq=8, tree_stride=8)
     assert call(ok, None) == 1                        # no cache shape
@@ -120,7 +120,7 @@ def test_accept_commit_noalloc_rejects_bad_arguments():
     def call(shape, kv, tau=0.8, kpages=FAKE, status=FAKE):
         return L.sd_accept_commit_noalloc(ctypes.byref(shape), None if kv is None else ctypes.byref(kv),
                                           FAKE, FAKE, FAKE, FAKE, FAKE, tau, FAKE, FAKE, FAKE, kpages,
-                                          FAKE, FAKE, FAKE, status, None)
+                                          FAKE, FAKE, FAKE, None, status, None)
     ok = _lib.SdAcceptShape(2, 8, 100, 1, 8)
     kv = _shape(B=2, T=8, Hq=8, tree_stride=8)
     assert call(ok, None) == 1
@@ -191,10 +191,10 @@ def test_tree_expand_rejects_bad_arguments():
 
 def test_commit_and_topk_reject_bad_arguments():
     s = _shape()
-    assert L.sd_kv_commit(ctypes.byref(_shape(Hq=7)), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 256,
-                          None) == 2
-    assert L.sd_kv_commit(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 256, None) == 1
-    assert L.sd_kv_commit(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 256, None) == 5
+    assert L.sd_kv_commit(ctypes.byref(_shape(Hq=7)), FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE,
+                          256, None) == 2
+    assert L.sd_kv_commit(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, None, 256, None) == 1
+    assert L.sd_kv_commit(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, 256, None) == 5
     assert L.sd_topk_blocks(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, 0, FAKE, FAKE, 1 << 40, None) == 1
     assert L.sd_topk_blocks(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, 4, FAKE, FAKE, 10, None) == 5
     assert L.sd_device_status(None, None, None) == 1

@@ -140,3 +140,48 @@ def test_block_sums_append_bad_block_leaves_sums():
     mask = np.ones(got.shape[0], bool)
     mask[blk0] = False
     assert np.array_equal(got[mask].view(np.uint32), before.cpu().numpy()[mask].view(np.uint32))
+
+
+@pytest.mark.parametrize("ctx0,case", [(128, "bf16"), (125, "bf16"), (61, "f32"), (3, "bf16"),
+                                       (37, "d64_bs8")])
+@pytest.mark.parametrize("call", ["accept_commit", "kv_commit", "noalloc"])
+def test_commit_extends_sums_in_the_same_launch(ctx0, case, call):
+    """The kept sums passed to the commit (sd_accept_commit, sd_kv_commit or
+    the no-workspace variant) come out equal to sums rebuilt at the new
+    lengths, bit for bit, and equal to the separate append's."""
+    over = dict(B=3, ctx_lo=ctx0, ctx_hi=ctx0 + 2, hot_blocks=1)
+    if case == "f32":
+        over["dtype"] = "f32"
+    if case == "d64_bs8":
+        over.update(D=64, bs=8)
+    c = small_variant("sparse_topk32_ctx64k", **over)
+    _say("commit with sums %s ctx0=%d %s" % (call, ctx0, case))
+    x = make_inputs(c)
+    d = to_device(x)
+    sums = tva.block_sums(d["k"], d["table"], d["ctx"])
+    sums_sep = sums.clone()
+    if call == "kv_commit":
+        rp, rl, _ = oracle.accept(x.target_logits, c.logit_dtype, None, x.tree_parent, x.tree_token,
+                                  x.uniforms, 0.0)
+        p, l = dev_tensor(rp), dev_tensor(rl)
+        tva.kv_commit(d["k"], d["v"], d["table"], d["ctx"], p, l, sums=sums)
+    elif call == "accept_commit":
+        p, l, _ = tva.accept_commit(d["logits"], None, d["parent"], d["token"], d["unif"], 0.0,
+                                    d["k"], d["v"], d["table"], d["ctx"], sums=sums)
+    else:
+        status = torch.zeros(1, dtype=torch.int32, device="cuda")
+        p, l, _ = tva.accept_commit_noalloc(d["logits"], None, d["parent"], d["token"], d["unif"], 0.0,
+                                            d["k"], d["v"], d["table"], d["ctx"], status, sums=sums)
+        torch.cuda.synchronize()
+        assert tva.device_status(ws=status) == 0
+    tva.block_sums_append(d["k"], d["table"], d["ctx"], l, sums_sep)
+    torch.cuda.synchronize()
+    assert tva.device_status() == 0
+    plen = l.cpu().numpy()
+    K, V, ctx2 = oracle.commit(x.k_pages, x.v_pages, x.block_table, x.ctx_lens, p.cpu().numpy(), plen,
+                               c.bs)
+    assert np.array_equal(d["ctx"].cpu().numpy(), ctx2)
+    ref = oracle.block_sums(K, x.block_table, ctx2, c.bs, c.dtype)
+    live = _live(ctx2, x.block_table, c.bs)
+    _check_sums(sums, ref, live)
+    assert torch.equal(sums, sums_sep)

@@ -73,11 +73,11 @@ def lib():
         "sd_tree_verify_attn": [ctypes.POINTER(SdShape), _P, _P, _P, _P, _P, _P, _P, i32, _P, _P, sz, _P],
         "sd_accept": [ctypes.POINTER(SdAcceptShape), _P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P,
                       _P, sz, _P],
-        "sd_kv_commit": [ctypes.POINTER(SdShape), _P, _P, _P, _P, _P, _P, _P, sz, _P],
+        "sd_kv_commit": [ctypes.POINTER(SdShape), _P, _P, _P, _P, _P, _P, _P, _P, sz, _P],
         "sd_accept_commit": [ctypes.POINTER(SdAcceptShape), ctypes.POINTER(SdShape), _P, _P, _P, _P, _P,
-                             ctypes.c_float, _P, _P, _P, _P, _P, _P, _P, _P, sz, _P],
+                             ctypes.c_float, _P, _P, _P, _P, _P, _P, _P, _P, _P, sz, _P],
         "sd_accept_commit_noalloc": [ctypes.POINTER(SdAcceptShape), ctypes.POINTER(SdShape), _P, _P, _P,
-                                     _P, _P, ctypes.c_float, _P, _P, _P, _P, _P, _P, _P, _P, _P],
+                                     _P, _P, ctypes.c_float, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
         "sd_topk_blocks": [ctypes.POINTER(SdShape), _P, _P, _P, _P, i32, _P, _P, sz, _P],
         "sd_topk_blocks_cached": [ctypes.POINTER(SdShape), _P, _P, _P, _P, i32, _P, _P, sz, _P],
         "sd_topk_blocks_shared": [ctypes.POINTER(SdShape), _P, _P, _P, _P, _P, i32, _P, _P, sz, _P],
@@ -206,8 +206,10 @@ def accept(target_logits, draft_probs, tree_parent, tree_token, uniforms, temper
 
 def accept_commit(target_logits, draft_probs, tree_parent, tree_token, uniforms, temperature,
                   k_pages, v_pages, block_table, ctx_lens, path=None, path_len=None, bonus=None,
-                  ws=None):
-    """accept(...) then kv_commit(...) of its paths, in one launch (sd_accept_commit)."""
+                  ws=None, sums=None):
+    """accept(...) then kv_commit(...) of its paths, in one launch (sd_accept_commit);
+    with `sums` (kept block key sums) also their extension over the committed
+    positions."""
     B, T, V = target_logits.shape
     shape = SdAcceptShape(B, T, V, _dtype_code[target_logits.dtype],
                           0 if tree_parent.shape[0] == 1 else T)
@@ -227,13 +229,13 @@ def accept_commit(target_logits, draft_probs, tree_parent, tree_token, uniforms,
         ctypes.byref(shape), ctypes.byref(kv_shape), _ptr(target_logits), _ptr(draft_probs),
         _ptr(tree_parent), _ptr(tree_token), _ptr(uniforms), float(temperature), _ptr(path),
         _ptr(path_len), _ptr(bonus), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(ctx_lens),
-        _ptr(ws), ws.numel(), _stream(dev)))
+        _ptr(sums), _ptr(ws), ws.numel(), _stream(dev)))
     return path, path_len, bonus
 
 
 def accept_commit_noalloc(target_logits, draft_probs, tree_parent, tree_token, uniforms,
                           temperature, k_pages, v_pages, block_table, ctx_lens, status,
-                          path=None, path_len=None, bonus=None):
+                          path=None, path_len=None, bonus=None, sums=None):
     """sd_accept_commit_noalloc: accept_commit(...) with no workspace; sticky
     error bits are OR-ed into `status` (an int32 device tensor of one element)."""
     B, T, V = target_logits.shape
@@ -253,11 +255,11 @@ def accept_commit_noalloc(target_logits, draft_probs, tree_parent, tree_token, u
         ctypes.byref(shape), ctypes.byref(kv_shape), _ptr(target_logits), _ptr(draft_probs),
         _ptr(tree_parent), _ptr(tree_token), _ptr(uniforms), float(temperature), _ptr(path),
         _ptr(path_len), _ptr(bonus), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(ctx_lens),
-        _ptr(status), _stream(dev)))
+        _ptr(sums), _ptr(status), _stream(dev)))
     return path, path_len, bonus
 
 
-def kv_commit(k_pages, v_pages, block_table, ctx_lens, path, path_len, ws=None):
+def kv_commit(k_pages, v_pages, block_table, ctx_lens, path, path_len, ws=None, sums=None):
     B, T = path.shape
     nb, Hkv, bs, D = k_pages.shape
     shape = SdShape(B, T, Hkv, Hkv, D, bs, block_table.shape[1], nb, _dtype_code[k_pages.dtype],
@@ -266,7 +268,7 @@ def kv_commit(k_pages, v_pages, block_table, ctx_lens, path, path_len, ws=None):
     ws = _WS.get(k_pages.device, need, SD_CALL_COMMIT) if ws is None else ws
     _check("sd_kv_commit", lib().sd_kv_commit(
         ctypes.byref(shape), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(ctx_lens),
-        _ptr(path), _ptr(path_len), _ptr(ws), ws.numel(), _stream(k_pages.device)))
+        _ptr(sums), _ptr(path), _ptr(path_len), _ptr(ws), ws.numel(), _stream(k_pages.device)))
 
 
 def tree_expand(draft_logits, cum_logp, temperature, k, ws=None):

@@ -288,6 +288,14 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
         }
         __syncthreads();
       }
+      // kept block key sums: this head's, extended over the committed
+      // positions [ctx, ctx + L) (the rows written above are visible to the
+      // workgroup after the last barrier)
+      if (a.csums && wave == 0)
+        extend_head_sums_rt(
+            esize, D, bs, c_ctx, c_ctx + L, lane,
+            [&](int n) { return K + (long long)s_cblk[n - lo] * blk_bytes + head; },
+            [&](int n) { return a.csums + ((size_t)s_cblk[n - lo] * a.cHkv + g) * D; });
     }
   };
   if (s_flag) {

@@ -8,9 +8,11 @@
 // the stores are issued.  The path is increasing with path[j] >= j, so a
 // group's destinations (positions < ctx + j0 + JG) never overlap the sources of
 // a later group (positions >= ctx + j0 + JG): the copy is safe in place.
-// The sequence's last workgroup to finish (a counter per sequence in the
-// workspace) writes the new context length; every workgroup has read the old
-// one before it counts itself.
+// With kept block key sums, the workgroup then extends its head's sums over
+// the committed positions (the same sequential float32 sums as
+// sd_block_sums_append).  The sequence's last workgroup to finish (a counter
+// per sequence in the workspace) writes the new context length; every
+// workgroup has read the old one before it counts itself.
 #include "common.h"
 
 namespace sdtree {
@@ -100,6 +102,15 @@ __global__ void __launch_bounds__(kCommitThreads) commit_kernel(CommitArgs a) {
     }
     __syncthreads();
   }
+  // With kept block key sums: extend this head's sums over the committed
+  // positions [ctx, ctx + L) (the rows the workgroup just wrote are visible
+  // to it after the copy's last barrier); the blocks are those validated
+  // above.
+  if (a.sums && (tid >> 6) == 0)
+    extend_head_sums_rt(
+        a.esize, a.D, a.bs, ctx, ctx + L, tid & 63,
+        [&](int n) { return K + (long long)s_blk[n - lo] * blk_bytes + head; },
+        [&](int n) { return a.sums + ((size_t)s_blk[n - lo] * a.Hkv + g) * a.D; });
   if (tid == 0) {
     const unsigned done = atomicAdd(a.counters + b, 1u);
     if (done == (unsigned)a.Hkv - 1) {

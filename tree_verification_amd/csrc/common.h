@@ -57,6 +57,74 @@ template <> struct Elem<bf16_bits> {
 };
 
 // ---------------------------------------------------------------------------
+// Kept block key sums (float32 [num_blocks][Hkv][D], per physical block):
+// extend one KV head's sums over positions [t0, t1) of a sequence, in
+// position order, each block continuing from its current sum, or from +0 for
+// a block whose first position is among them -- the sequential sum the block
+// selection divides.  One wavefront: lane owns dims lane * D / 64 ...
+// krow(n): the K rows of logical block n, head g (row 0); sum_at(n): its sums.
+template <typename E, int D, typename KRow, typename SumAt>
+__device__ __forceinline__ void extend_head_sums(int bs, int t0, int t1, int lane, KRow krow, SumAt sum_at) {
+  constexpr int DPL = D / 64;
+  const int d0 = lane * DPL;
+  for (int t = t0; t < t1;) {
+    const int n = t / bs, off = t - n * bs;
+    const int tn = min((n + 1) * bs, t1);
+    float* kept = sum_at(n) + d0;
+    const E* row = krow(n) + d0;
+    float s[DPL];
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) s[e] = off == 0 ? 0.f : kept[e];
+    // rows loaded RIF at a time, all in flight, then added in position order
+    constexpr int RIF = 16;
+    const int end = off + (tn - t);
+    for (int u0 = off; u0 < end; u0 += RIF) {
+      float x[RIF][DPL];
+#pragma unroll
+      for (int r = 0; r < RIF; ++r) {
+        const int u = min(u0 + r, end - 1);     // (past the end: a valid row, not added)
+        if constexpr (sizeof(E) == 2) {
+          if constexpr (DPL == 2) {
+            const uint32_t w = *reinterpret_cast<const uint32_t*>(row + (size_t)u * D);
+            x[r][0] = bf16_to_f32((bf16_bits)(w & 0xFFFFu));
+            x[r][1] = bf16_to_f32((bf16_bits)(w >> 16));
+          } else {
+            x[r][0] = bf16_to_f32(row[(size_t)u * D]);
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < DPL; ++e) x[r][e] = row[(size_t)u * D + e];
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < RIF; ++r)
+        if (u0 + r < end)
+#pragma unroll
+          for (int e = 0; e < DPL; ++e) s[e] = s[e] + x[r][e];
+    }
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) kept[e] = s[e];
+    t = tn;
+  }
+}
+
+// extend_head_sums for the element type and head dim known at run time
+// (D in {64, 128}, esize 2 = bf16 or 4 = float32).
+template <typename KRow, typename SumAt>
+__device__ __forceinline__ void extend_head_sums_rt(int esize, int D, int bs, int t0, int t1, int lane,
+                                                    KRow krow_bytes, SumAt sum_at) {
+  if (esize == 2) {
+    auto kr = [&](int n) { return reinterpret_cast<const bf16_bits*>(krow_bytes(n)); };
+    if (D == 128) extend_head_sums<bf16_bits, 128>(bs, t0, t1, lane, kr, sum_at);
+    else extend_head_sums<bf16_bits, 64>(bs, t0, t1, lane, kr, sum_at);
+  } else {
+    auto kr = [&](int n) { return reinterpret_cast<const float*>(krow_bytes(n)); };
+    if (D == 128) extend_head_sums<float, 128>(bs, t0, t1, lane, kr, sum_at);
+    else extend_head_sums<float, 64>(bs, t0, t1, lane, kr, sum_at);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Attention launch plan (host side; depends on the shape only).
 struct AttnPlan {
   int variant;          // 0: VALU (fp32 or tiny), 1: MFMA bf16
@@ -124,6 +192,7 @@ struct AcceptArgs {
   void* cv;
   const int32_t* ctable;
   int32_t* cctx;
+  float* csums;         // kept block key sums to extend with the commit (NULL: none)
   int cHkv, cD, cbs, cmax_blocks, cnum_blocks, cesize;
 };
 
@@ -141,6 +210,7 @@ struct CommitArgs {
   const int32_t* path_len;
   uint32_t* status;
   unsigned* counters;   // one per sequence, zero between calls
+  float* sums;          // kept block key sums to extend (NULL: none)
   int B, T, Hkv, D, bs, max_blocks, num_blocks, esize;
 };
 

@@ -368,13 +368,14 @@ static sd_status accept_ws_args(const sd_accept_shape* shape, void* ws, size_t w
 // The commit half of an acceptance call that also commits its paths.
 static sd_status accept_commit_args(const sd_accept_shape* shape, const sd_shape* kv_shape,
                                     void* k_pages, void* v_pages, const int32_t* block_table,
-                                    int32_t* ctx_lens, AcceptArgs* a) {
+                                    int32_t* ctx_lens, float* block_sums, AcceptArgs* a) {
   if (!shape || !kv_shape) return SD_INVALID_ARG;
   const sd_status st = check_shape(kv_shape);
   if (st != SD_OK) return st;
   if (kv_shape->B != shape->B || kv_shape->T != shape->T) return SD_BAD_SHAPE;
   if (!k_pages || !v_pages || !block_table || !ctx_lens) return SD_INVALID_ARG;
   a->ck = k_pages; a->cv = v_pages; a->ctable = block_table; a->cctx = ctx_lens;
+  a->csums = block_sums;
   a->cHkv = kv_shape->Hkv; a->cD = kv_shape->D; a->cbs = kv_shape->bs;
   a->cmax_blocks = kv_shape->max_blocks; a->cnum_blocks = kv_shape->num_blocks;
   a->cesize = kv_shape->dtype == SD_F32 ? 4 : 2;
@@ -400,13 +401,13 @@ sd_status sd_accept_commit(const sd_accept_shape* shape, const sd_shape* kv_shap
                            const int32_t* tree_parent, const int32_t* tree_token,
                            const float* uniforms, float temperature, int32_t* path,
                            int32_t* path_len, int32_t* bonus, void* k_pages, void* v_pages,
-                           const int32_t* block_table, int32_t* ctx_lens, void* ws,
-                           size_t ws_bytes, void* stream) {
+                           const int32_t* block_table, int32_t* ctx_lens, float* block_sums,
+                           void* ws, size_t ws_bytes, void* stream) {
   AcceptArgs a;
   sd_status st = accept_args(shape, target_logits, draft_probs, tree_parent, tree_token, uniforms,
                              temperature, path, path_len, bonus, &a);
   if (st != SD_OK) return st;
-  st = accept_commit_args(shape, kv_shape, k_pages, v_pages, block_table, ctx_lens, &a);
+  st = accept_commit_args(shape, kv_shape, k_pages, v_pages, block_table, ctx_lens, block_sums, &a);
   if (st != SD_OK) return st;
   st = accept_ws_args(shape, ws, ws_bytes, &a);
   if (st != SD_OK) return st;
@@ -419,12 +420,12 @@ sd_status sd_accept_commit_noalloc(const sd_accept_shape* shape, const sd_shape*
                                    const float* uniforms, float temperature, int32_t* path,
                                    int32_t* path_len, int32_t* bonus, void* k_pages,
                                    void* v_pages, const int32_t* block_table, int32_t* ctx_lens,
-                                   uint32_t* status, void* stream) {
+                                   float* block_sums, uint32_t* status, void* stream) {
   AcceptArgs a;
   sd_status st = accept_args(shape, target_logits, draft_probs, tree_parent, tree_token, uniforms,
                              temperature, path, path_len, bonus, &a);
   if (st != SD_OK) return st;
-  st = accept_commit_args(shape, kv_shape, k_pages, v_pages, block_table, ctx_lens, &a);
+  st = accept_commit_args(shape, kv_shape, k_pages, v_pages, block_table, ctx_lens, block_sums, &a);
   if (st != SD_OK) return st;
   if (!status) return SD_INVALID_ARG;
   // the library's exchange slots hold kNoAllocMaxSeqs sequences
@@ -434,8 +435,9 @@ sd_status sd_accept_commit_noalloc(const sd_accept_shape* shape, const sd_shape*
 }
 
 sd_status sd_kv_commit(const sd_shape* shape, void* k_pages, void* v_pages,
-                       const int32_t* block_table, int32_t* ctx_lens, const int32_t* path,
-                       const int32_t* path_len, void* ws, size_t ws_bytes, void* stream) {
+                       const int32_t* block_table, int32_t* ctx_lens, float* block_sums,
+                       const int32_t* path, const int32_t* path_len, void* ws, size_t ws_bytes,
+                       void* stream) {
   sd_status st = check_shape(shape);
   if (st != SD_OK) return st;
   if (!k_pages || !v_pages || !block_table || !ctx_lens || !path || !path_len || !ws)
@@ -444,7 +446,7 @@ sd_status sd_kv_commit(const sd_shape* shape, void* k_pages, void* v_pages,
   CommitArgs a;
   memset(&a, 0, sizeof(a));
   a.k = k_pages; a.v = v_pages; a.table = block_table; a.ctx = ctx_lens; a.path = path;
-  a.path_len = path_len;
+  a.path_len = path_len; a.sums = block_sums;
   a.B = shape->B; a.T = shape->T; a.Hkv = shape->Hkv; a.D = shape->D; a.bs = shape->bs;
   a.max_blocks = shape->max_blocks; a.num_blocks = shape->num_blocks;
   a.esize = shape->dtype == SD_F32 ? 4 : 2;

@@ -623,7 +623,6 @@ __global__ void __launch_bounds__(256) group_select_kernel(TopkArgs a) {
 template <typename E, int D>
 __global__ void __launch_bounds__(256) block_sums_append_kernel(TopkArgs a, const int32_t* __restrict__ n_new) {
 #pragma clang fp contract(off)
-  constexpr int DPL = D / 64;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const long long unit = (long long)blockIdx.x * 4 + wave;
   if (unit >= (long long)a.B * a.Hkv) return;
@@ -643,47 +642,10 @@ __global__ void __launch_bounds__(256) block_sums_append_kernel(TopkArgs a, cons
     }
   }
   const E* K = reinterpret_cast<const E*>(a.k);
-  const int d0 = lane * DPL;
-  for (int t = ctx - L; t < ctx;) {
-    const int n = t / a.bs, off = t - n * a.bs;
-    const int t1 = min((n + 1) * a.bs, ctx);
-    const int blk = table[n];
-    float* kept = a.sums + ((size_t)blk * a.Hkv + g) * D + d0;
-    const E* row = K + (((size_t)blk * a.Hkv + g) * a.bs) * D + d0;
-    float s[DPL];
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) s[e] = off == 0 ? 0.f : kept[e];
-    // rows loaded RIF at a time, all in flight, then added in position order
-    constexpr int RIF = 16;
-    const int end = off + (t1 - t);
-    for (int u0 = off; u0 < end; u0 += RIF) {
-      float x[RIF][DPL];
-#pragma unroll
-      for (int r = 0; r < RIF; ++r) {
-        const int u = min(u0 + r, end - 1);     // (past the end: a valid row, not added)
-        if constexpr (sizeof(E) == 2) {
-          if constexpr (DPL == 2) {
-            const uint32_t w = *reinterpret_cast<const uint32_t*>(row + (size_t)u * D);
-            x[r][0] = bf16_to_f32((bf16_bits)(w & 0xFFFFu));
-            x[r][1] = bf16_to_f32((bf16_bits)(w >> 16));
-          } else {
-            x[r][0] = bf16_to_f32(row[(size_t)u * D]);
-          }
-        } else {
-#pragma unroll
-          for (int e = 0; e < DPL; ++e) x[r][e] = row[(size_t)u * D + e];
-        }
-      }
-#pragma unroll
-      for (int r = 0; r < RIF; ++r)
-        if (u0 + r < end)
-#pragma unroll
-          for (int e = 0; e < DPL; ++e) s[e] = s[e] + x[r][e];
-    }
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) kept[e] = s[e];
-    t = t1;
-  }
+  extend_head_sums<E, D>(
+      a.bs, ctx - L, ctx, lane,
+      [&](int n) { return K + (((size_t)table[n] * a.Hkv + g) * a.bs) * D; },
+      [&](int n) { return a.sums + ((size_t)table[n] * a.Hkv + g) * D; });
 }
 
 template <typename E, int D, int MODE>
