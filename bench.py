@@ -67,9 +67,11 @@ def parse():
     ap.add_argument("--kv-copies", type=int, default=2,
                     help="K/V page copies, used by consecutive steps in turn")
     ap.add_argument("--workload", default="llama3_8b_tree64")
-    ap.add_argument("--shared-selection", action="store_true",
-                    help="sparse workload: one block selection per (sequence, KV group) "
-                         "(sd_topk_blocks_shared) instead of one per query row")
+    ap.add_argument("--selection", choices=["per_row", "shared", "dense"], default="per_row",
+                    help="sparse workload: one block selection per query row (sd_topk_blocks_cached), "
+                         "one per (sequence, KV group) (sd_topk_blocks_shared), or none (dense "
+                         "attention over the whole context)")
+    ap.add_argument("--shared-selection", action="store_true", help="the same as --selection shared")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="approximate CPU time budget of the oracle sample")
@@ -221,14 +223,22 @@ def loop_us(torch, calls, n=40, rounds=3):
     return float(np.median(ts))
 
 
-ATTN_SOURCES = ("attn.hip", "common.h", "sdtree.hip")
+def _between(text, start, end):
+    i = text.index(start)
+    return text[i:text.index(end, i)]
 
 
 def attn_source_hash():
-    """sha256 over the sources that decide the attention kernels and their plan."""
+    """sha256 over what decides the attention kernels and their launch: the
+    attention source, the plan function and the argument structs."""
+    csrc = os.path.join(ROOT, "tree_verification_amd", "csrc")
     h = hashlib.sha256()
-    for f in ATTN_SOURCES:
-        h.update(open(os.path.join(ROOT, "tree_verification_amd", "csrc", f), "rb").read())
+    h.update(open(os.path.join(csrc, "attn.hip"), "rb").read())
+    host = open(os.path.join(csrc, "sdtree.hip")).read()
+    h.update(_between(host, "static AttnPlan plan_attn", "\n}\n").encode())
+    common = open(os.path.join(csrc, "common.h")).read()
+    h.update(_between(common, "struct AttnPlan {", "};").encode())
+    h.update(_between(common, "struct AttnArgs {", "};").encode())
     return h.hexdigest()
 
 
@@ -788,7 +798,10 @@ def main():
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
-    w = Workload(args.workload, max(1, args.kv_copies), shared=args.shared_selection)
+    selection = "shared" if args.shared_selection else args.selection
+    w = Workload(args.workload, max(1, args.kv_copies), shared=selection == "shared")
+    if w.cfg.topk and selection == "dense":
+        w.set_selection("dense")
     cfg = w.cfg
     settle_steps = 0
     t_end = time.perf_counter() + args.settle_ms * 1e-3
@@ -821,8 +834,8 @@ def main():
     sel_np = None if w.sel is None else w.sel.cpu().numpy()
     bytes_, flops = attention_cost(cfg, w.x, sel_np)
     roof = roofline_for(cfg, bytes_, flops, attn_s)
-    # the committed counter figures are for the per-row selection
-    roof["traffic"] = None if w.shared else traffic_for("attn", cfg.name)
+    # the committed counter figures are for the default selection of the workload
+    roof["traffic"] = None if (w.shared or (cfg.topk and w.sel is None)) else traffic_for("attn", cfg.name)
     calls = time_calls(w)
     loop = [bound_attention(w, w.sel, kv) for kv in range(len(w.kvs))]
     calls["attention_loop_us"] = round(loop_us(torch, loop), 2)
@@ -850,7 +863,8 @@ def main():
         "config": {"workload": cfg.name, "B": cfg.B, "T": cfg.T, "Hq": cfg.Hq, "Hkv": cfg.Hkv,
                    "D": cfg.D, "ctx": [cfg.ctx_lo, cfg.ctx_hi], "block": cfg.bs, "V": cfg.V,
                    "accept": cfg.mode, "temperature": w.tau, "topk": cfg.topk or None,
-                   "selection": (("shared per KV group" if w.shared else "per query row")
+                   "selection": (("none (dense attention)" if w.sel is None else
+                                  "shared per KV group" if w.shared else "per query row")
                                  if cfg.topk else None),
                    "kv_copies": len(w.kvs)},
         "roofline": dict(roof, kernel="sd_tree_verify_attn (tree-masked attention kernel)",
