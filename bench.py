@@ -757,7 +757,7 @@ def sweep(kind):
             try:
                 t_a = _median_us(torch, f_a)
             except tva.SdError:
-                t_a = None          # selections wider than sparse attention accepts
+                t_a = None          # a selection the call does not support
             # one selection per (sequence, KV group)
             f_s = lambda: tva.topk_blocks_shared(d["q"], d["k"], d["table"], d["ctx"], k, sums=sums)
             t_s = _median_us(torch, f_s)

@@ -85,6 +85,9 @@ typedef enum sd_dtype { SD_F32 = 0, SD_BF16 = 1 } sd_dtype;
                                     (more than its margin within float32 rounding of the cut) */
 #define SD_ERR_TIMEOUT    0x20u  /* a cross-workgroup wait gave up; results of the call are invalid
                                     and the workspace must be zero-filled again */
+#define SD_ERR_DEBUG      0x80u  /* debug build (libsdtree_debug.so) only: a device-side
+                                    consistency check between a launch's plan and its kernel
+                                    failed; the call's results are invalid */
 
 typedef struct sd_shape {
   int32_t B;            /* sequences */
@@ -134,6 +137,9 @@ enum { SD_CALL_ATTN = 1, SD_CALL_ACCEPT = 2, SD_CALL_TOPK = 3, SD_CALL_COMMIT = 
  *               context blocks each query keeps, ascending, -1 padded at the
  *               end (sparse-verification page, "Methodology": top-k blocks per
  *               query); tree ancestors are always attended.
+ *   k_sel       0 for dense attention, else 1 .. 65536 (SD_UNSUPPORTED above:
+ *               a wider list is padding, since it cannot hold more distinct
+ *               blocks than the context has).
  *   out         written in `dtype`.
  *   ws          >= sd_workspace_bytes(SD_CALL_ATTN, shape, k_sel).
  */
@@ -372,7 +378,7 @@ size_t sd_workspace_bytes(int32_t call_id, const void* shape, int32_t extra);
 sd_status sd_device_status(void* ws, void* stream, uint32_t* bits);
 
 /* Static description of a status code. */
-const char* sd_status_str(sd_status s);
+const char* sd_status_str(int32_t code);
 
 #ifdef __cplusplus
 }

@@ -22,6 +22,18 @@ def test_exports_every_declared_function():
         assert hasattr(L, n), n
 
 
+def test_debug_library_exports_every_declared_function():
+    """libsdtree_debug.so (the build with device-side consistency checks)
+    loads and exports the same functions."""
+    import os
+    assert os.path.exists(_lib.DEBUG_LIB_PATH), "run `python -m tree_verification_amd.build --debug`"
+    D = ctypes.CDLL(_lib.DEBUG_LIB_PATH)
+    for n in _lib.declared_functions():
+        assert hasattr(D, n), n
+    s = _shape()
+    assert D.sd_workspace_bytes(1, ctypes.byref(s), 0) == L.sd_workspace_bytes(1, ctypes.byref(s), 0)
+
+
 def test_status_strings():
     for code in range(8):
         assert L.sd_status_str(code)
@@ -59,7 +71,7 @@ def test_attention_rejects_null_small_ws_and_bad_ksel():
     assert need > 0
     assert _attn(s, ws_bytes=need - 1) == 5
     assert _attn(s, sel=FAKE, ksel=0) == 1
-    assert _attn(s, sel=FAKE, ksel=65) == 1
+    assert _attn(s, sel=FAKE, ksel=65537) == 4
     assert _attn(s, sel=None, ksel=3) == 1
 
 
@@ -68,7 +80,8 @@ def test_workspace_sizes():
     assert L.sd_workspace_bytes(1, ctypes.byref(s), 0) >= 256
     # float32: header + one precomputed ancestor word per node
     assert L.sd_workspace_bytes(1, ctypes.byref(_shape(dtype=0)), 0) >= 256 + 16 * 64 * 8
-    assert L.sd_workspace_bytes(1, ctypes.byref(s), 65) == 0
+    assert L.sd_workspace_bytes(1, ctypes.byref(s), 65537) == 0
+    assert L.sd_workspace_bytes(1, ctypes.byref(s), 256) > 0
     assert L.sd_workspace_bytes(3, ctypes.byref(s), 32) >= 16 * 260 * 8 * 128 * 4
     assert L.sd_workspace_bytes(3, ctypes.byref(s), 0) == 0
     # commit: status header plus one completion counter per sequence

@@ -313,6 +313,23 @@ def test_sparse_attention(size):
         check_attention(np.stack([gpu[b, i, h] for b, i, h in rows]), ref, c.dtype, "sparse full")
 
 
+@pytest.mark.parametrize("k", [100, 200])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_sparse_attention_wide_selection(k, dtype):
+    """Selections of more than 64 blocks per query row (the sparse-verification
+    page's k trade-off reaches past 64): the library's top-k of a context of
+    1500-2500 tokens in blocks of 8 (188-313 blocks) equals the oracle's, and
+    the attention over it matches the oracle's attention over the same lists."""
+    c = small_variant("sparse_topk32_ctx64k", topk=k, dtype=dtype, bs=8, ctx_lo=1500, ctx_hi=2500, B=2)
+    _say("sparse wide k=%d %s" % (k, dtype))
+    x, d, sel, ref_sel = _topk_case(c)
+    assert np.array_equal(sel, ref_sel)
+    gpu = _run_attn(x, d, sel=ref_sel)
+    ref = oracle.attention_dense(x.q, x.k_pages, x.v_pages, x.block_table, x.ctx_lens,
+                                 x.tree_parent, c.bs, c.dtype, sel_blocks=ref_sel)
+    check_attention(gpu, ref, c.dtype, "sparse wide")
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_sparse_attention_fp32_and_partial_selection(dtype):
     c = small_variant("sparse_topk32_ctx64k", dtype=dtype, B=2, ctx_lo=300, ctx_hi=500, bs=16)

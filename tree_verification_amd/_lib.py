@@ -13,6 +13,8 @@ import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libsdtree.so")
+# the same library with the kernels' device-side consistency checks
+DEBUG_LIB_PATH = os.path.join(_HERE, "libsdtree_debug.so")
 HEADER = os.path.join(os.path.dirname(_HERE), "include", "sdtree.h")
 
 SD_F32, SD_BF16 = 0, 1
@@ -21,7 +23,7 @@ SD_CALL_ATTN, SD_CALL_ACCEPT, SD_CALL_TOPK, SD_CALL_COMMIT, SD_CALL_BLOCK_SUMS, 
 STATUS = {0: "SD_OK", 1: "SD_INVALID_ARG", 2: "SD_BAD_SHAPE", 3: "SD_BAD_DTYPE",
           4: "SD_UNSUPPORTED", 5: "SD_CAPACITY", 6: "SD_HIP_ERROR", 7: "SD_DEVICE_DATA_ERROR"}
 ERR_BITS = {0x1: "parent", 0x2: "block", 0x4: "capacity", 0x8: "token", 0x10: "selection",
-            0x20: "timeout", 0x40: "build"}
+            0x20: "timeout", 0x40: "build", 0x80: "debug check"}
 
 
 class SdShape(ctypes.Structure):
@@ -53,6 +55,7 @@ class SdError(RuntimeError):
 
 _P = ctypes.c_void_p
 _LIB = None
+_LIB_FILE = LIB_PATH
 
 
 def declared_functions():
@@ -61,13 +64,25 @@ def declared_functions():
     return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w]+\*?\s+\*?(sd_\w+)\s*\(", text, re.M)))
 
 
+def use_library(path):
+    """Makes the binding call the library at `path` from now on (LIB_PATH by
+    default; DEBUG_LIB_PATH is the build with device-side consistency checks).
+    Returns the path it replaces."""
+    global _LIB, _LIB_FILE
+    prev = _LIB_FILE
+    _LIB_FILE = path
+    _LIB = None
+    return prev
+
+
 def lib():
     global _LIB
     if _LIB is not None:
         return _LIB
-    if not os.path.exists(LIB_PATH):
-        raise RuntimeError("libsdtree.so is not built; run `python -m tree_verification_amd.build`")
-    L = ctypes.CDLL(LIB_PATH)
+    if not os.path.exists(_LIB_FILE):
+        raise RuntimeError("%s is not built; run `python -m tree_verification_amd.build%s`"
+                           % (os.path.basename(_LIB_FILE), " --debug" if _LIB_FILE == DEBUG_LIB_PATH else ""))
+    L = ctypes.CDLL(_LIB_FILE)
     i32, sz = ctypes.c_int32, ctypes.c_size_t
     sig = {
         "sd_tree_verify_attn": [ctypes.POINTER(SdShape), _P, _P, _P, _P, _P, _P, _P, i32, _P, _P, sz, _P],

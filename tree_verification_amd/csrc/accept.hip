@@ -204,6 +204,7 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
       cbad = SD_ERR_CAPACITY;
     } else {
       const int lo = c_ctx / a.cbs, nblk = (c_ctx + T - 1) / a.cbs - lo + 1;
+      SD_DCHECK(nblk <= kMaxCBlk, a.status);
       const int32_t* ctable = a.ctable + (size_t)b * a.cmax_blocks + lo;
       for (int n = tid; n < nblk; n += kAT) {
         const int blk = ctable[n];
@@ -309,6 +310,10 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
 
   const int sl0 = min(wg * a.SL, V), sl1 = min(sl0 + a.SL, V);
   const int NC = a.NC;
+  // the P slices cover the vocabulary and each slice its chunks; a
+  // register-cached slice has at most kMaxCh chunks
+  SD_DCHECK(P >= 1 && P <= kMaxP && (long long)P * a.SL >= V && NC * kChunk >= a.SL, a.status);
+  SD_DCHECK(!CACHED || NC <= kMaxCh, a.status);
   const bool vec = (V & 7) == 0;
   constexpr bool mss = MODE == kRejection;
   const float c2 = a.tau > 0.f ? 1.4426950408889634f / a.tau : 0.f;
@@ -610,6 +615,9 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
       ku = a.unif[((size_t)b * T + node) * 2 + 0];
     }
     if (!have_row) load_row(row, lc);
+    // the uniform of this node's draw, loaded with the rest so that the draw
+    // does not wait for it
+    const float u_draw = a.unif[((size_t)b * T + cur) * 2 + 1];
     if constexpr (mss) {
       qrow = a.draft + ((size_t)b * T + cur) * V;
       if constexpr (CACHED) {
@@ -821,7 +829,7 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
           w8[e] = v[e] == -INFINITY ? 0.0 : (double)__builtin_amdgcn_exp2f((v[e] - m) * c2);
       };
       if constexpr (!mss) {
-        const float u = a.unif[((size_t)b * T + cur) * 2 + 1];
+        const float u = u_draw;
         const int x = draw(u, ew8);
         exchange((uint32_t)(x + 1), 0u);   // only the drawing workgroup has x >= 0
         int xs = -1;
@@ -954,7 +962,7 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
         }
         if (nxt < 0) {
           if (nrej == 0) init_rr();   // a leaf: the draw is from p itself
-          const float u = a.unif[((size_t)b * T + cur) * 2 + 1];
+          const float u = u_draw;
           const int nr = nrej;
           // weights in the units of mass[]: the residual times `units`
           auto rw8 = [&](int c, double* w8) {
@@ -992,6 +1000,7 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
     lds_sync();
   }
   if (wg == 0 && tid == 0) a.path_len[b] = plen;
+  SD_DCHECK(plen >= 1 && plen <= T, a.status);
   if (commit) {
     if (cerr) {
       if (wg == 0 && tid == 0) set_status(a.status, cerr);

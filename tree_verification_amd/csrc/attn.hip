@@ -86,7 +86,7 @@ __global__ void __launch_bounds__(256) attn_valu_kernel(AttnArgs a) {
   }
   const int bt = a.tree_stride ? b : 0;
   const uint64_t* anc = a.anc + ((size_t)bt * a.T + i) * a.W64;
-  const int32_t* sel = a.sel ? a.sel + row * a.ksel : nullptr;
+  const int32_t* sel = a.sel ? a.sel + (size_t)row * a.ksel : nullptr;
   const int nblk_ctx = (ctx + a.bs - 1) / a.bs;
   const long long n_ctx_keys = sel ? (long long)a.ksel * a.bs : ctx;
   const long long n_keys = n_ctx_keys + a.T;
@@ -318,6 +318,8 @@ __global__ void __launch_bounds__(WQ * WK * 64) attn_mfma_kernel(AttnArgs a) {
   int* s_par = reinterpret_cast<int*>(smem);
   static_assert(2 * (K_BYTES + V_BYTES) >= 4 * kMaxTreeNodes, "parents fit the ring");
   const int nn = i_hi - i_lo + 1;
+  SD_DCHECK(nn <= 0 || (long long)nn * a.W64 <= a.anc_lds_words, a.status);
+  SD_DCHECK(n_tt <= 128, a.status);
   // flag the tree tiles (NK nodes each) that a nonzero ancestor word touches
   auto flag_word = [&](int w, uint64_t acc) {
     if constexpr (NK >= 64) {
@@ -404,6 +406,7 @@ __global__ void __launch_bounds__(WQ * WK * 64) attn_mfma_kernel(AttnArgs a) {
     }
     __syncthreads();
     nU = s_nU;
+    SD_DCHECK(nU <= a.u_max, a.status);
     for (int w = tid; w < BW; w += NT) {
       uint32_t bits = ubits[w];
       int o = upre[w];
@@ -461,6 +464,8 @@ __global__ void __launch_bounds__(WQ * WK * 64) attn_mfma_kernel(AttnArgs a) {
                          ? min((min(t_hi, nct) * NK - 1) >> bsh, (ctx - 1) >> bsh) - cb0 + 1 : 0;
   const int tb0 = ctx >> bsh;
   const int tcount = (cap_ok && t_hi > nct) ? ((ctx + T - 1) >> bsh) - tb0 + 1 : 0;
+  SD_DCHECK(ccount <= a.ct_max && tcount <= a.tt_max, a.status);
+  SD_DCHECK(split < a.n_splits && t_hi - t_lo <= a.tps, a.status);
   const long long blk_elems = (long long)a.Hkv * bs * D;
   const long long head_off = (long long)g * bs * D;   // head g inside a K or a V block
   for (int j = tid; j < ccount + tcount; j += NT) {

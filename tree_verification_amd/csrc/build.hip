@@ -96,6 +96,8 @@ __global__ void __launch_bounds__(kBuildThreads) build_round_kernel(BuildArgs a,
   // candidates after the n - 1 taken ones (fewer than T - n when the n rows
   // have fewer children in all than the budget asks for)
   const int M = min(T - n, kc - (n - 1));
+  // the round's candidates fit the sort and cover the nodes already taken
+  SD_DCHECK(kc <= kBuildSort && n >= 1 && n < T && kc >= n - 1, a.status);
   if (tid == 0) {
     s_m = M;
     s_bad = 0;

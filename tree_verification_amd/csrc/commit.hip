@@ -39,6 +39,8 @@ __global__ void __launch_bounds__(kCommitThreads) commit_kernel(CommitArgs a) {
   const bool shape_ok = err == 0;
   const int lo = shape_ok ? ctx / a.bs : 0;
   const int nblk = shape_ok ? (ctx + a.T - 1) / a.bs - lo + 1 : 0;
+  // the path and the tree slots' block ids fit their LDS copies
+  SD_DCHECK(a.T <= kMaxCommitT && nblk <= kMaxCommitBlocks, a.status);
   if (shape_ok) {
     for (int j = tid; j < L; j += kCommitThreads) s_path[j] = path[j];
     for (int n = tid; n < nblk; n += kCommitThreads) {

@@ -41,6 +41,22 @@ __device__ __forceinline__ void set_status(uint32_t* status, uint32_t bit) {
   atomicOr(status, bit);
 }
 
+// Device-side consistency checks of the debug build (compiled with
+// -DSDTREE_DEBUG into libsdtree_debug.so): invariants that the host's plan and
+// the kernels must agree on, which no argument reaching a kernel can break.
+// A failed check sets SD_ERR_DEBUG in the call's status word and the kernel
+// goes on (no trap); the release build compiles them away.
+#ifdef SDTREE_DEBUG
+#define SD_DCHECK(cond, status)                                       \
+  do {                                                                \
+    if (!(cond)) ::sdtree::set_status((status), SD_ERR_DEBUG);        \
+  } while (0)
+#else
+#define SD_DCHECK(cond, status) \
+  do {                          \
+  } while (0)
+#endif
+
 // Element loads for the two storage types.
 template <typename E> struct Elem;
 template <> struct Elem<float> {

@@ -5,11 +5,13 @@
 
 #include <algorithm>
 
+#include <limits.h>
+
 #include "common.h"
 
 namespace sdtree {
 
-constexpr int kMaxKsel = 64;
+constexpr int kMaxKsel = 1 << 16;   // widest sparse selection (blocks per query row)
 constexpr size_t kLdsLimit = 160 * 1024;
 
 static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -25,8 +27,11 @@ static sd_status check_shape(const sd_shape* s) {
   if (s->D != 64 && s->D != 128) return SD_UNSUPPORTED;
   if (s->bs < 8 || (s->bs & (s->bs - 1)) != 0) return SD_UNSUPPORTED;
   if (s->T > kMaxTreeNodes) return SD_UNSUPPORTED;
+  // query rows, and so every per-row index, fit an int
+  if ((long long)s->B * s->T > INT_MAX || (long long)s->B * s->T * s->Hq > INT_MAX) return SD_UNSUPPORTED;
   if ((long long)s->max_blocks * s->bs > (1ll << 30)) return SD_UNSUPPORTED;
-  if ((long long)s->num_blocks * s->Hkv * s->bs * s->D > (1ll << 40)) return SD_UNSUPPORTED;
+  // (in double: the product of four ints can pass 2^63)
+  if ((double)s->num_blocks * s->Hkv * s->bs * s->D > (double)(1ll << 40)) return SD_UNSUPPORTED;
   if (!(s->scale >= 0.f) || isinf(s->scale)) return SD_INVALID_ARG;
   return SD_OK;
 }
@@ -163,7 +168,7 @@ static sd_status check_build(const sd_build_shape* s) {
   if (s->T < 1 || s->V < 1) return SD_BAD_SHAPE;
   if (s->logit_dtype != SD_F32 && s->logit_dtype != SD_BF16) return SD_BAD_DTYPE;
   if ((long long)s->T * s->V >= 0xFFFFFFFFll) return SD_UNSUPPORTED;
-  if (s->T - 1 + kBuildMargin > kMaxExpandK) return SD_UNSUPPORTED;
+  if ((long long)s->T - 1 + kBuildMargin > kMaxExpandK) return SD_UNSUPPORTED;
   return SD_OK;
 }
 
@@ -223,8 +228,9 @@ using namespace sdtree;
 
 extern "C" {
 
-const char* sd_status_str(sd_status s) {
-  switch (s) {
+const char* sd_status_str(int32_t code) {
+  // (an int, not the enum: any value a caller passes is a defined input)
+  switch (code) {
     case SD_OK: return "ok";
     case SD_INVALID_ARG: return "invalid argument";
     case SD_BAD_SHAPE: return "bad shape";
@@ -284,7 +290,8 @@ sd_status sd_tree_verify_attn(const sd_shape* shape, const void* q, const void* 
   if (!q || !k_pages || !v_pages || !block_table || !ctx_lens || !tree_parent || !out || !ws)
     return SD_INVALID_ARG;
   const bool sparse = sel_blocks != nullptr;
-  if (sparse && (k_sel < 1 || k_sel > kMaxKsel)) return SD_INVALID_ARG;
+  if (sparse && k_sel < 1) return SD_INVALID_ARG;
+  if (sparse && k_sel > kMaxKsel) return SD_UNSUPPORTED;
   if (!sparse && k_sel != 0) return SD_INVALID_ARG;
   const sd_shape& s = *shape;
   const AttnPlan p = plan_attn(&s, k_sel, sparse);

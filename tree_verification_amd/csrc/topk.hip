@@ -156,6 +156,8 @@ __global__ void __launch_bounds__(256) block_score_kernel(TopkArgs a) {
   const int tid = threadIdx.x;
   const int grp = tid >> 4, dl = tid & 15;
   const int R = a.T * a.G;  // query rows of this KV group
+  // the score rows hold every block of the context
+  SD_DCHECK(nblk <= a.nbmax, a.status);
   for (int r0 = 0; r0 < R; r0 += RC) {
     const int rc = min(RC, R - r0);
     __syncthreads();
@@ -279,6 +281,7 @@ __global__ void __launch_bounds__(256) block_select_kernel(TopkArgs a) {
   const bool ok = ctx >= 0 && (long long)ctx <= (long long)a.max_blocks * a.bs;
   const int nb = ok ? (ctx + a.bs - 1) / a.bs : 0;
   const float* sc = a.scores + row * a.nbmax;
+  SD_DCHECK(nb <= a.nbmax, a.status);
   if (nb <= a.topk) {
     for (int e = lane; e < a.topk; e += 64) out[e] = e < nb ? e : -1;
     return;
