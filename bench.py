@@ -141,6 +141,17 @@ def attention_cost(cfg, x, sel=None):
     return bytes_, flops
 
 
+def accept_cost(cfg, plen):
+    """Algorithmic bytes of one acceptance call: every visited node's target
+    logits row, and for rejection sampling its draft probability row (float32),
+    read once.  The visited nodes of a sequence are its accepted path (the
+    last one is where the walk stops); residual passes reread the row from the
+    workgroups' registers, and the test scalars are a few bytes."""
+    e_logit = 2 if cfg.logit_dtype == "bf16" else 4
+    per_row = cfg.V * (e_logit + (4 if cfg.mode == "mss" else 0))
+    return int(np.asarray(plen, dtype=np.int64).sum()) * per_row
+
+
 def roofline_for(cfg, bytes_, flops, seconds):
     ai = flops / bytes_
     ridge = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
@@ -844,6 +855,14 @@ def main():
     if not args.no_secondary:
         secondary = [e for e in secondary_workloads() if e["workload"] != args.workload]
 
+    # the acceptance call: its bytes (the path of the last timed step) over its
+    # own per-call time
+    acc_bytes = accept_cost(cfg, plen)
+    acc_s = calls["accept_us"] * 1e-6
+    accept = {"bytes_per_call": acc_bytes, "accept_us": calls["accept_us"],
+              "achieved_gb_s": round(acc_bytes / acc_s / 1e9, 1),
+              "frac_of_hbm_peak": round(acc_bytes / acc_s / 1e9 / 8000.0, 4),
+              "bound": "latency (a sequential walk: one cross-workgroup exchange per node and per rejection)"}
     cpu = None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_seconds)
     value = cfg.B * cfg.T / step_s
     line = {
@@ -873,6 +892,7 @@ def main():
                          flops_per_call=int(flops)),
         "verified_tree_tokens_per_s_attention": round(cfg.B * cfg.T / attn_s, 1),
         "cpu_baseline": cpu,
+        "accept": accept,
         "accepted_tokens_per_s": round(float(plen.sum()) / step_s, 1),
         "mean_path_len": round(float(plen.mean()), 3),
         "calls_us": calls,
