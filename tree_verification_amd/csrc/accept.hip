@@ -191,6 +191,42 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
   unsigned long long* slots = reinterpret_cast<unsigned long long*>(a.sync + (size_t)b * kAccSeqBytes);
   unsigned* done = reinterpret_cast<unsigned*>(slots + 2 * kMaxP * 2);
 
+  const int sl0 = min(wg * a.SL, V), sl1 = min(sl0 + a.SL, V);
+  const int NC = a.NC;
+  // the P slices cover the vocabulary and each slice its chunks; a
+  // register-cached slice has at most kMaxCh chunks
+  SD_DCHECK(P >= 1 && P <= kMaxP && (long long)P * a.SL >= V && NC * kChunk >= a.SL, a.status);
+  SD_DCHECK(!CACHED || NC <= kMaxCh, a.status);
+  const bool vec = (V & 7) == 0;
+  constexpr bool mss = MODE == kRejection;
+  const float c2 = a.tau > 0.f ? 1.4426950408889634f / a.tau : 0.f;
+  const double invtau_d = a.tau > 0.f ? 1.0 / (double)a.tau : 0.0;
+  auto y0_of = [&](int c) { return sl0 + c * kChunk + tid * 8; };
+  auto row_of = [&](int node) {
+    return reinterpret_cast<const LT*>(a.logits) + ((size_t)b * T + node) * V;
+  };
+
+  // Row caches (CACHED): the current node's logits, the first child's logits
+  // (prefetched in case it is accepted) and, for rejection sampling, the
+  // current node's draft probabilities.
+  uint4 lc[kMaxCh], pfc[kMaxCh];
+  float qc[kMaxCh][8];
+  const LT* row = row_of(0);
+  const float* qrow = nullptr;
+  // CACHED kernels run only when V % 8 == 0, so a chunk starting inside the
+  // slice is whole.  Every cached chunk is loaded unconditionally (a chunk
+  // outside the slice reads the row's first 8 values, which are never used):
+  // a branch around the load would make its merge wait for the data at once.
+  auto cached_y = [&](int c) {
+    const int y0 = y0_of(c);
+    return (c < NC && y0 < sl1) ? y0 : 0;
+  };
+  auto load_row = [&](const LT* r, uint4* dst) {
+    if constexpr (CACHED) {
+#pragma unroll
+      for (int c = 0; c < kMaxCh; ++c) dst[c] = *reinterpret_cast<const uint4*>(r + cached_y(c));
+    }
+  };
   // With a commit: the context length, and the block ids of the tree slots
   // [ctx, ctx + T) staged and validated now, alongside the tree (the commit
   // runs after the walk; see below).
@@ -199,25 +235,32 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
   __shared__ int s_cblk[kMaxCBlk];
   __shared__ int s_cerr;
   uint32_t cbad = 0;
-  if (commit) {
-    if (c_ctx < 0 || (long long)c_ctx + T > (long long)a.cmax_blocks * a.cbs) {
-      cbad = SD_ERR_CAPACITY;
-    } else {
-      const int lo = c_ctx / a.cbs, nblk = (c_ctx + T - 1) / a.cbs - lo + 1;
-      SD_DCHECK(nblk <= kMaxCBlk, a.status);
-      const int32_t* ctable = a.ctable + (size_t)b * a.cmax_blocks + lo;
-      for (int n = tid; n < nblk; n += kAT) {
-        const int blk = ctable[n];
-        if (blk < 0 || blk >= a.cnum_blocks) cbad |= SD_ERR_BLOCK;
-        s_cblk[n] = blk;
-      }
-    }
+  // This thread's first tree entry and first tree-slot block id are loaded
+  // before the root's row, so that waiting for them does not wait for the row
+  // (vector loads complete in order); the walk starts at the root, whose row
+  // is known before the tree is read, and its latency overlaps the set-up.
+  const int32_t* tpar = a.parent + (size_t)bt * T;
+  const int32_t* ttok = a.token + (size_t)bt * T;
+  const int p_first = tid < T ? tpar[tid] : 0;
+  const int t_first = tid < T ? ttok[tid] : 0;
+  const bool c_ok = commit && c_ctx >= 0 && (long long)c_ctx + T <= (long long)a.cmax_blocks * a.cbs;
+  const int c_lo = c_ok ? c_ctx / a.cbs : 0;
+  const int c_nblk = c_ok ? (c_ctx + T - 1) / a.cbs - c_lo + 1 : 0;
+  SD_DCHECK(c_nblk <= kMaxCBlk, a.status);
+  const int32_t* ctable = commit ? a.ctable + (size_t)b * a.cmax_blocks + c_lo : nullptr;
+  const int blk_first = tid < c_nblk ? ctable[tid] : 0;
+  load_row(row_of(0), lc);
+  if (commit && !c_ok) cbad = SD_ERR_CAPACITY;
+  for (int n = tid; n < c_nblk; n += kAT) {
+    const int blk = n == tid ? blk_first : ctable[n];
+    if (blk < 0 || blk >= a.cnum_blocks) cbad |= SD_ERR_BLOCK;
+    s_cblk[n] = blk;
   }
   // The tree (kept in LDS) must be topologically ordered with valid tokens.
   int bad = 0;
   for (int n = tid; n < T; n += kAT) {
-    const int p = a.parent[(size_t)bt * T + n];
-    const int t = a.token[(size_t)bt * T + n];
+    const int p = n == tid ? p_first : tpar[n];
+    const int t = n == tid ? t_first : ttok[n];
     if (n == 0 ? p != -1 : (p < 0 || p >= n)) bad |= SD_ERR_PARENT;
     if (t < 0 || t >= V) bad |= SD_ERR_TOKEN;
     s_par[n] = p;
@@ -308,21 +351,6 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
     return;
   }
 
-  const int sl0 = min(wg * a.SL, V), sl1 = min(sl0 + a.SL, V);
-  const int NC = a.NC;
-  // the P slices cover the vocabulary and each slice its chunks; a
-  // register-cached slice has at most kMaxCh chunks
-  SD_DCHECK(P >= 1 && P <= kMaxP && (long long)P * a.SL >= V && NC * kChunk >= a.SL, a.status);
-  SD_DCHECK(!CACHED || NC <= kMaxCh, a.status);
-  const bool vec = (V & 7) == 0;
-  constexpr bool mss = MODE == kRejection;
-  const float c2 = a.tau > 0.f ? 1.4426950408889634f / a.tau : 0.f;
-  const double invtau_d = a.tau > 0.f ? 1.0 / (double)a.tau : 0.0;
-  auto y0_of = [&](int c) { return sl0 + c * kChunk + tid * 8; };
-  auto row_of = [&](int node) {
-    return reinterpret_cast<const LT*>(a.logits) + ((size_t)b * T + node) * V;
-  };
-
   // ---- cross-workgroup exchange ---------------------------------------------
   // exchange(v0, v1): every workgroup of the sequence publishes two 32-bit
   // values tagged with the barrier number; lanes j < P of wave 0 poll slot j
@@ -408,27 +436,6 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
     return nk;
   };
 
-  // Row caches (CACHED): the current node's logits, the first child's logits
-  // (prefetched in case it is accepted) and, for rejection sampling, the
-  // current node's draft probabilities.
-  uint4 lc[kMaxCh], pfc[kMaxCh];
-  float qc[kMaxCh][8];
-  const LT* row = row_of(0);
-  const float* qrow = nullptr;
-  // CACHED kernels run only when V % 8 == 0, so a chunk starting inside the
-  // slice is whole.  Every cached chunk is loaded unconditionally (a chunk
-  // outside the slice reads the row's first 8 values, which are never used):
-  // a branch around the load would make its merge wait for the data at once.
-  auto cached_y = [&](int c) {
-    const int y0 = y0_of(c);
-    return (c < NC && y0 < sl1) ? y0 : 0;
-  };
-  auto load_row = [&](const LT* r, uint4* dst) {
-    if constexpr (CACHED) {
-#pragma unroll
-      for (int c = 0; c < kMaxCh; ++c) dst[c] = *reinterpret_cast<const uint4*>(r + cached_y(c));
-    }
-  };
   auto logits8 = [&](int c, float* v) {
     const int y0 = y0_of(c);
     if (y0 >= sl1) {
@@ -592,7 +599,7 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
   };
 
   int cur = 0, plen = 1;
-  bool have_row = false;   // lc already holds the current node's row (prefetched)
+  bool have_row = true;    // lc already holds the current node's row (the root's since the start)
   if (wg == 0 && tid == 0) path[0] = 0;
   for (int step = 0; step < T; ++step) {
     const int nk = gather_children(cur);
