@@ -858,9 +858,11 @@ __global__ void __launch_bounds__(WQ * WK * 64) attn_mfma_kernel(AttnArgs a) {
   // DMA sources of K(tk) and V(tk - 1) for a tight step, formed one step
   // ahead so the block-table reads are off the issue path.
   // The 64 / CK K rows one wave-operation copies lie in one page, so that
-  // operation's page base is wave-uniform: it is formed on the scalar unit from
-  // the block table (entries out of range were flagged in the prologue and read
-  // as block 0), and each lane adds a fixed byte offset.
+  // operation's page base is wave-uniform: dense tiles read it from the page
+  // offsets the prologue staged and validated in LDS (those V uses too), so a
+  // step forms it with one LDS read and no block-table load or 64-bit multiply
+  // on the scalar unit, which the CU's wavefronts share; each lane adds a
+  // fixed byte offset.
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   uint32_t koff[K_OPS];
 #pragma unroll
@@ -870,10 +872,6 @@ __global__ void __launch_bounds__(WQ * WK * 64) attn_mfma_kernel(AttnArgs a) {
   }
   const unsigned char* kpage[K_OPS];
   const bf16_bits* vsrc[V_OPS];
-  // the block table read through the constant address space: uniform reads
-  // become scalar loads
-  typedef const __attribute__((address_space(4))) int32_t* const_i32p;
-  const const_i32p table_c = (const_i32p)(table);
   // (sparse tiles index the union of selected blocks: virtual key vi lies in
   // union block vi >> bsh, whose validated physical id is Uphys[vi >> bsh])
   auto tight_sources = [&](auto sp_tag, int tk) __attribute__((always_inline)) {
@@ -881,15 +879,18 @@ __global__ void __launch_bounds__(WQ * WK * 64) attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
     for (int n = 0; n < K_OPS; ++n) {
       const int p0 = tk * NK + (64 * (wave_u + NWAVE * n)) / CK;
-      int phys;
       if constexpr (!SP) {
-        phys = table_c[p0 >> bsh];
-        phys = (phys < 0 || phys >= a.num_blocks) ? 0 : phys;
+        // the page's element offset as staged (and validated) in LDS
+        const long long boff = ctab[(p0 >> bsh) - cb0];
+        const uint64_t bu = (uint64_t)boff;
+        const long long bs_u = (long long)(((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(bu >> 32)) << 32) |
+                                           (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)bu));
+        kpage[n] = reinterpret_cast<const unsigned char*>(Kp + (bs_u + (long long)((p0 & bsm) * D)));
       } else {
-        phys = __builtin_amdgcn_readfirstlane(Uphys[p0 >> bsh]);
+        const int phys = __builtin_amdgcn_readfirstlane(Uphys[p0 >> bsh]);
+        kpage[n] = reinterpret_cast<const unsigned char*>(
+            Kp + (phys * blk_elems + head_off + (long long)((p0 & bsm) * D)));
       }
-      kpage[n] = reinterpret_cast<const unsigned char*>(
-          Kp + (phys * blk_elems + head_off + (long long)((p0 & bsm) * D)));
     }
 #pragma unroll
     for (int n = 0; n < V_OPS; ++n) {
