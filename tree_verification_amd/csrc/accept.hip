@@ -625,21 +625,7 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
     // the uniform of this node's draw, loaded with the rest so that the draw
     // does not wait for it
     const float u_draw = a.unif[((size_t)b * T + cur) * 2 + 1];
-    if constexpr (mss) {
-      qrow = a.draft + ((size_t)b * T + cur) * V;
-      if constexpr (CACHED) {
-        // (chunks outside the slice hold unused draft values; every use
-        // there meets a zero residual)
-#pragma unroll
-        for (int c = 0; c < kMaxCh; ++c) {
-          const int yq = cached_y(c);
-          const float4 u0 = *reinterpret_cast<const float4*>(qrow + yq);
-          const float4 u1 = *reinterpret_cast<const float4*>(qrow + yq + 4);
-          qc[c][0] = u0.x; qc[c][1] = u0.y; qc[c][2] = u0.z; qc[c][3] = u0.w;
-          qc[c][4] = u1.x; qc[c][5] = u1.y; qc[c][6] = u1.z; qc[c][7] = u1.w;
-        }
-      }
-    }
+    if constexpr (mss) qrow = a.draft + ((size_t)b * T + cur) * V;
     // (greedy prefetches the first child's row now; the other rules after
     // the statistics exchange, whose polling loads would otherwise wait for
     // it: vector loads return in order)
@@ -918,7 +904,22 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
           // float64 precision
           double pz = 0.0;
           if constexpr (CACHED) {
-            if (nrej == 0) init_rr();
+            if (nrej == 0) {
+              // The draft row's slice is read only now: a first child accepted
+              // at once never needs it, and it is two thirds of a node's bytes
+              // (float32 against bf16 logits), which all sequences' walks
+              // share the memory for.  (Chunks outside the slice hold unused
+              // draft values; every use there meets a zero residual.)
+#pragma unroll
+              for (int c = 0; c < kMaxCh; ++c) {
+                const int yq = cached_y(c);
+                const float4 u0 = *reinterpret_cast<const float4*>(qrow + yq);
+                const float4 u1 = *reinterpret_cast<const float4*>(qrow + yq + 4);
+                qc[c][0] = u0.x; qc[c][1] = u0.y; qc[c][2] = u0.z; qc[c][3] = u0.w;
+                qc[c][4] = u1.x; qc[c][5] = u1.y; qc[c][6] = u1.z; qc[c][7] = u1.w;
+              }
+              init_rr();
+            }
             FOR_CHUNKS(cc,
               float q8[8];
               q8_of(cc, q8);
