@@ -508,11 +508,18 @@ __global__ void __launch_bounds__(WQ * WK * 64) attn_mfma_kernel(AttnArgs a) {
   const int t_lo = split * tps_here;
   const int t_hi = min(t_lo + tps_here, ntot);
   const int n_ctx_here = max(0, min(t_hi, nct) - t_lo);
-  if (tid == 0) {
+  // the flagged tree tiles of this split, in order (wavefront 0 compacts 64
+  // tiles at a time with a ballot)
+  if (wave == 0) {
     int n = 0;
-    for (int t = max(t_lo, nct); t < t_hi; ++t)
-      if (tflag[t - nct]) tlist[n++] = t;
-    s_ntree = n;
+    for (int t0 = max(t_lo, nct); t0 < t_hi; t0 += 64) {
+      const int t = t0 + lane;
+      const bool f = t < t_hi && tflag[t - nct];
+      const unsigned long long bal = __ballot(f);
+      if (f) tlist[n + __popcll(bal & ((1ull << lane) - 1ull))] = t;
+      n += __popcll(bal);
+    }
+    if (lane == 0) s_ntree = n;
   }
 
   // Physical block ids this split reads, staged once: dense context blocks
