@@ -1080,42 +1080,41 @@ __global__ void __launch_bounds__(WQ * WK * 64) attn_mfma_kernel(AttnArgs a) {
     l_run[qb] += __shfl_xor(l_run[qb], 32);
   }
   if constexpr (WK > 1) {
-    float* xm = reinterpret_cast<float*>(smem);  // [NWAVE][QW]
-    float* xl = xm + NWAVE * QW;                 // [NWAVE][QW]
-    float* xo = xl + NWAVE * QW;                 // [NWAVE][QW][D]
+    // The key-slice partners of a query slice pass (m, l, o) through the
+    // idle ring in the lanes' own layout, so every access is a conflict-free
+    // 16-byte (or 4-byte) one: partner slot sl = (wk - 1) * WQ + wq holds
+    // o[qb][db] of lane l at f32x4 index ((sl * QB + qb) * DB + db) * 64 + l
+    // and m, l of qb at float index (sl * QB + qb) * 64 + l.  (The partner
+    // lane holds the same query column and dims.)
+    constexpr int NSL = (WK - 1) * WQ;
+    f32x4* xo = reinterpret_cast<f32x4*>(smem);                        // [NSL][QB][DB][64]
+    float* xm = reinterpret_cast<float*>(xo + NSL * QB * DB * 64);     // [NSL][QB][64]
+    float* xl = xm + NSL * QB * 64;                                    // [NSL][QB][64]
     if (wk > 0) {
+      const int sl = (wk - 1) * WQ + wq;
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        const int qc = qb * 16 + l16;
-        if (lg == 0) {
-          xm[wave * QW + qc] = m_run[qb];
-          xl[wave * QW + qc] = l_run[qb];
-        }
+        xm[(sl * QB + qb) * 64 + lane] = m_run[qb];
+        xl[(sl * QB + qb) * 64 + lane] = l_run[qb];
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) xo[(wave * QW + qc) * D + db * 16 + 4 * lg + j] = o[qb][db][j];
+        for (int db = 0; db < DB; ++db) xo[((sl * QB + qb) * DB + db) * 64 + lane] = o[qb][db];
       }
     }
     __syncthreads();
     if (wk == 0) {
 #pragma unroll
       for (int kw = 1; kw < WK; ++kw) {
-        const int ow = wq + WQ * kw;
+        const int sl = (kw - 1) * WQ + wq;
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
-          const int qc = qb * 16 + l16;
-          const float mo = xm[ow * QW + qc], lo = xl[ow * QW + qc];
+          const float mo = xm[(sl * QB + qb) * 64 + lane], lo = xl[(sl * QB + qb) * 64 + lane];
           const float mn = fmaxf(m_run[qb], mo);
           const float fs = __builtin_amdgcn_exp2f(m_run[qb] - mn);
           const float fo = __builtin_amdgcn_exp2f(mo - mn);
           m_run[qb] = mn;
           l_run[qb] = l_run[qb] * fs + lo * fo;
 #pragma unroll
-          for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-              o[qb][db][j] = o[qb][db][j] * fs + xo[(ow * QW + qc) * D + db * 16 + 4 * lg + j] * fo;
+          for (int db = 0; db < DB; ++db) o[qb][db] = o[qb][db] * fs + xo[((sl * QB + qb) * DB + db) * 64 + lane] * fo;
         }
       }
     }
