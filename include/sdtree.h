@@ -36,9 +36,8 @@
  *     sd_device_status reads (and clears) it.
  *   - No exceptions, aborts or printing.  One workspace must not be used by two
  *     calls that may run concurrently, and a workspace serves one call kind:
- *     sd_accept keeps barrier counters, and sd_tree_verify_attn split-merge
- *     counters, in their workspaces that must read zero when a call starts
- *     (every call leaves them at zero).
+ *     sd_accept keeps barrier counters in its workspace that must read zero
+ *     when a call starts (every call leaves them at zero).
  *
  * Layouts (row-major, innermost last)
  *   q, out        [B, T, Hq, D]                 element type `dtype`

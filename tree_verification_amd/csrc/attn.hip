@@ -210,64 +210,6 @@ __global__ void __launch_bounds__(256) attn_valu_kernel(AttnArgs a) {
 // formed relative to a running max that may lag the true one by up to this.
 constexpr float kLazy = 8.0f;
 
-// Two floats in one 64-bit word (low, high) and back.
-__device__ __forceinline__ uint64_t pack2(float lo, float hi) {
-  return (uint64_t)__float_as_uint(lo) | ((uint64_t)__float_as_uint(hi) << 32);
-}
-__device__ __forceinline__ float lo_f(uint64_t x) { return __uint_as_float((uint32_t)x); }
-__device__ __forceinline__ float hi_f(uint64_t x) { return __uint_as_float((uint32_t)(x >> 32)); }
-
-// Merge of a split launch's partials, for the 16 * QB query rows of one
-// wavefront starting at rowbase (rows >= M skipped): read back every split's
-// (o, m, l) -- device-scope loads of device-scope stores -- and form
-// sum_s 2^(m_s - m) o_s / sum_s 2^(m_s - m) l_s in split order, as bf16.
-// Kept out of line so the kernel's main loop is register-allocated without it.
-template <int D, int QB>
-__device__ __attribute__((noinline)) void merge_split_rows(const float* part_o, const float* part_ml, bf16_bits* out_base,
-                                                          int NS, int M, int G, int T, int Hq, int b, int g, int rowbase,
-                                                          int l16, int lg) {
-  constexpr int DB = D / 16;
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int r = rowbase + qb * 16 + l16;
-    if (r >= M) continue;
-    const int i = r / G, h = g * G + r % G;
-    const size_t orow = ((size_t)b * T + i) * Hq + h;
-    auto ml_of = [&](int sp) {
-      return __hip_atomic_load(reinterpret_cast<const uint64_t*>(part_ml + (orow * NS + sp) * 2), __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-    };
-    float mx = -1e30f;
-#pragma unroll 4
-    for (int sp = 0; sp < NS; ++sp) mx = fmaxf(mx, lo_f(ml_of(sp)));
-    f32x4 acc[DB];
-#pragma unroll
-    for (int db = 0; db < DB; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float lsum = 0.f;
-#pragma unroll 4
-    for (int sp = 0; sp < NS; ++sp) {
-      const uint64_t mlv = ml_of(sp);
-      const float w = __builtin_amdgcn_exp2f(lo_f(mlv) - mx);
-      lsum += w * hi_f(mlv);
-      const uint64_t* po = reinterpret_cast<const uint64_t*>(part_o + (orow * NS + sp) * D + 4 * lg);
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const uint64_t x0 = __hip_atomic_load(po + db * 8, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const uint64_t x1 = __hip_atomic_load(po + db * 8 + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        acc[db] += w * f32x4{lo_f(x0), hi_f(x0), lo_f(x1), hi_f(x1)};
-      }
-    }
-    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-    bf16_bits* out = out_base + orow * D;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      const uint32_t lo = f32_to_bf16(acc[db][0] * inv) | ((uint32_t)f32_to_bf16(acc[db][1] * inv) << 16);
-      const uint32_t hi = f32_to_bf16(acc[db][2] * inv) | ((uint32_t)f32_to_bf16(acc[db][3] * inv) << 16);
-      *reinterpret_cast<uint2*>(out + db * 16 + 4 * lg) = make_uint2(lo, hi);
-    }
-  }
-}
-
 template <int D, int QW, int WQ, int WK, int KW, int S>
 __global__ void __launch_bounds__(WQ * WK * 64) attn_mfma_kernel(AttnArgs a) {
   constexpr int NWAVE = WQ * WK;
@@ -311,7 +253,7 @@ __global__ void __launch_bounds__(WQ * WK * 64) attn_mfma_kernel(AttnArgs a) {
   long long* ttab = ctab + a.ct_max;
   uint64_t* ancL = reinterpret_cast<uint64_t*>(ttab + a.tt_max);
   uint32_t* ubits = reinterpret_cast<uint32_t*>(ancL + a.anc_lds_words);
-  __shared__ int s_nU, s_err, s_ntree, s_last;
+  __shared__ int s_nU, s_err, s_ntree;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1119,82 +1061,32 @@ __global__ void __launch_bounds__(WQ * WK * 64) attn_mfma_kernel(AttnArgs a) {
       }
     }
   }
-  // Output rows: whole (one split), or this split's partial (o, m, l).  With
-  // a split launch and merge counters, every split publishes its partial and
-  // counts itself in; the split that arrives last (any of them) reads all
-  // the unit's partials back and merges them in split order, so the result
-  // does not depend on which one it is, and resets the counter.
-  const bool writer = wk == 0;
-  const bool fused = a.n_splits > 1 && a.merge_cnt != nullptr;
-  if (writer) {
+  if (wk != 0) return;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const int r = rowbase + qb * 16 + l16;
-      if (r >= M) continue;
-      const int i = r / G, h = g * G + r % G;
-      const size_t orow = ((size_t)b * T + i) * a.Hq + h;
-      if (a.n_splits == 1) {
-        const float inv = l_run[qb] > 0.f ? 1.f / l_run[qb] : 0.f;
-        bf16_bits* out = reinterpret_cast<bf16_bits*>(a.out) + orow * D;
+  for (int qb = 0; qb < QB; ++qb) {
+    const int r = rowbase + qb * 16 + l16;
+    if (r >= M) continue;
+    const int i = r / G, h = g * G + r % G;
+    const size_t orow = ((size_t)b * T + i) * a.Hq + h;
+    if (a.n_splits == 1) {
+      const float inv = l_run[qb] > 0.f ? 1.f / l_run[qb] : 0.f;
+      bf16_bits* out = reinterpret_cast<bf16_bits*>(a.out) + orow * D;
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const uint32_t lo = f32_to_bf16(o[qb][db][0] * inv) | ((uint32_t)f32_to_bf16(o[qb][db][1] * inv) << 16);
-          const uint32_t hi = f32_to_bf16(o[qb][db][2] * inv) | ((uint32_t)f32_to_bf16(o[qb][db][3] * inv) << 16);
-          *reinterpret_cast<uint2*>(out + db * 16 + 4 * lg) = make_uint2(lo, hi);
-        }
-      } else {
-        const size_t pr = orow * a.n_splits + split;
-        float* po = a.part_o + pr * D;
-        if (fused) {
-          // device-scope stores (written through to memory), so the release
-          // below has no dirty cache lines of them to write back
-#pragma unroll
-          for (int db = 0; db < DB; ++db) {
-            uint64_t* d = reinterpret_cast<uint64_t*>(po + db * 16 + 4 * lg);
-            __hip_atomic_store(d, pack2(o[qb][db][0], o[qb][db][1]), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(d + 1, pack2(o[qb][db][2], o[qb][db][3]), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          }
-          if (lg == 0)
-            __hip_atomic_store(reinterpret_cast<uint64_t*>(a.part_ml + pr * 2), pack2(m_run[qb], l_run[qb]),
-                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        } else {
-#pragma unroll
-          for (int db = 0; db < DB; ++db)
-            *reinterpret_cast<f32x4*>(po + db * 16 + 4 * lg) = o[qb][db];
-          if (lg == 0) {
-            a.part_ml[pr * 2 + 0] = m_run[qb];
-            a.part_ml[pr * 2 + 1] = l_run[qb];
-          }
-        }
+      for (int db = 0; db < DB; ++db) {
+        const uint32_t lo = f32_to_bf16(o[qb][db][0] * inv) | ((uint32_t)f32_to_bf16(o[qb][db][1] * inv) << 16);
+        const uint32_t hi = f32_to_bf16(o[qb][db][2] * inv) | ((uint32_t)f32_to_bf16(o[qb][db][3] * inv) << 16);
+        *reinterpret_cast<uint2*>(out + db * 16 + 4 * lg) = make_uint2(lo, hi);
       }
-    }
-  }
-  if (fused) {
-    // Publish, then count in.  The barrier follows this workgroup's partial
-    // stores (each wavefront waits for its own); one release by thread 0
-    // then writes them back to device scope ahead of its count, and only
-    // the last split, which reads the others' partials, acquires.  (A fence
-    // on every wavefront would write back and invalidate the L2 for each.)
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (tid == 0) {
-      uint32_t* cnt = a.merge_cnt + ((size_t)b * a.Hkv + g) * a.n_qtiles + qtile;
-      const uint32_t prev = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-      SD_DCHECK(prev < (uint32_t)a.n_splits, a.status);
-      const bool last = prev == (uint32_t)a.n_splits - 1;
-      if (last) {
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-        __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      const size_t pr = orow * a.n_splits + split;
+      float* po = a.part_o + pr * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        *reinterpret_cast<f32x4*>(po + db * 16 + 4 * lg) = o[qb][db];
+      if (lg == 0) {
+        a.part_ml[pr * 2 + 0] = m_run[qb];
+        a.part_ml[pr * 2 + 1] = l_run[qb];
       }
-      s_last = last;
-    }
-    __syncthreads();
-    if (s_last) {
-      // (the acquire above, by this workgroup's thread 0, was ordered before
-      // these reads by the barrier)
-      if (writer)
-        merge_split_rows<D, QB>(a.part_o, a.part_ml, reinterpret_cast<bf16_bits*>(a.out), a.n_splits, M, G, T,
-                                a.Hq, b, g, rowbase, l16, lg);
     }
   }
   if (tid == 0) {
@@ -1285,7 +1177,7 @@ static hipError_t launch_mfma_d(const AttnArgs& a, const AttnPlan& p, hipStream_
 
 hipError_t launch_attn_mfma(const AttnArgs& a, const AttnPlan& p, hipStream_t st) {
   hipError_t e = a.D == 64 ? launch_mfma_d<64>(a, p, st) : launch_mfma_d<128>(a, p, st);
-  if (e != hipSuccess || a.n_splits == 1 || a.merge_cnt) return e;
+  if (e != hipSuccess || a.n_splits == 1) return e;
   const long long nrows = (long long)a.B * a.T * a.Hq;
   dim3 grid((unsigned)((nrows + 3) / 4));
   bf16_bits* out = reinterpret_cast<bf16_bits*>(a.out);

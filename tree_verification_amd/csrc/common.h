@@ -20,13 +20,6 @@ constexpr size_t kWsHeader = 256;
 // 64 bytes inside the header that no kernel writes: a zero source for loads
 // of keys that do not exist.
 constexpr size_t kWsZeros = 128;
-// Attention workspaces: split-merge counters, one per (sequence, KV head,
-// query tile) of a split launch, at a fixed place after the header so that no
-// region of another shape's call ever overlaps them; every call leaves them
-// at zero.  Launches with more units merge in a separate kernel instead.
-constexpr int kMaxMergeUnits = 4096;
-constexpr size_t kWsMergeCnt = kWsHeader;
-constexpr size_t kWsAttnBase = kWsMergeCnt + 4 * (size_t)kMaxMergeUnits;
 
 __device__ __forceinline__ float bf16_to_f32(bf16_bits b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
@@ -181,7 +174,6 @@ struct AttnArgs {
   void* out;
   float* part_o;
   float* part_ml;
-  uint32_t* merge_cnt;  // split launches: the last split of a unit merges (null: separate kernel)
   uint32_t* status;
   int B, T, Hq, Hkv, G, M, D, bs, max_blocks, num_blocks, tree_stride;
   float scale_log2;

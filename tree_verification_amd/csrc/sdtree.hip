@@ -45,7 +45,7 @@ static AttnPlan plan_attn(const sd_shape* s, int ksel, bool sparse) {
   p.D = s->D;
   p.W64 = (s->T + 63) / 64;
   p.T_tree = s->tree_stride ? s->B : 1;
-  p.anc_off = kWsAttnBase;
+  p.anc_off = kWsHeader;
   // precomputed ancestor masks, read by the per-row float32 kernel only
   const size_t anc_bytes = s->dtype == SD_F32 ? (size_t)p.T_tree * s->T * p.W64 * 8 : 0;
   p.part_o_off = align_up(p.anc_off + anc_bytes, 256);
@@ -315,10 +315,6 @@ sd_status sd_tree_verify_attn(const sd_shape* shape, const void* q, const void* 
   a.parent = tree_parent; a.anc = anc; a.sel = sel_blocks; a.ksel = k_sel; a.out = out;
   a.part_o = reinterpret_cast<float*>(w + p.part_o_off);
   a.part_ml = reinterpret_cast<float*>(w + p.part_ml_off);
-  // the last split of each unit merges the partials in the attention kernel
-  // itself when the units fit the counters
-  const long long units = (long long)s.B * s.Hkv * p.n_qtiles;
-  a.merge_cnt = p.n_splits > 1 && units <= kMaxMergeUnits ? reinterpret_cast<uint32_t*>(w + kWsMergeCnt) : nullptr;
   a.status = status;
   a.B = s.B; a.T = s.T; a.Hq = s.Hq; a.Hkv = s.Hkv; a.G = s.Hq / s.Hkv; a.M = s.T * a.G;
   a.D = s.D; a.bs = s.bs; a.max_blocks = s.max_blocks; a.num_blocks = s.num_blocks;
