@@ -257,7 +257,7 @@ __global__ void __launch_bounds__(WQ * WK * 64) attn_mfma_kernel(AttnArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, so indexes built from it stay scalar
   const int wq = wave % WQ;
   const int wk = wave / WQ;
   const int l16 = lane & 15;
@@ -866,10 +866,9 @@ __global__ void __launch_bounds__(WQ * WK * 64) attn_mfma_kernel(AttnArgs a) {
   // ahead so the block-table reads are off the issue path.
   // The 64 / CK K rows one wave-operation copies lie in one page, so that
   // operation's page base is wave-uniform: dense tiles read it from the page
-  // offsets the prologue staged and validated in LDS (those V uses too), so a
-  // step forms it with one LDS read and no block-table load or 64-bit multiply
-  // on the scalar unit, which the CU's wavefronts share; each lane adds a
-  // fixed byte offset.
+  // offsets the prologue staged and validated in LDS, so a step forms it with
+  // one LDS read and no block-table load or 64-bit multiply on the scalar
+  // unit, which the CU's wavefronts share; each lane adds a fixed byte offset.
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   uint32_t koff[K_OPS];
 #pragma unroll
@@ -879,31 +878,51 @@ __global__ void __launch_bounds__(WQ * WK * 64) attn_mfma_kernel(AttnArgs a) {
   }
   const unsigned char* kpage[K_OPS];
   const bf16_bits* vsrc[V_OPS];
+  // A wave-operation's V bytes (slab layout) and its K rows fall in the same
+  // 16-key group of the tile, so with pages of 16 keys or more the V
+  // operation reads the page its K operation read one tile earlier: V's page
+  // base is that K base, kept from the previous step, plus a fixed per-lane
+  // offset, and no per-lane block-table read is needed.
+  const bool v_from_k = bs >= 16;
+  int vlane[V_OPS];
+#pragma unroll
+  for (int n = 0; n < V_OPS; ++n) vlane[n] = (v_key[n] & bsm) * D + v_col[n];
+  long long kb[K_OPS];  // page element offsets of the K operations of the last tile formed
   // (sparse tiles index the union of selected blocks: virtual key vi lies in
   // union block vi >> bsh, whose validated physical id is Uphys[vi >> bsh])
-  auto tight_sources = [&](auto sp_tag, int tk) __attribute__((always_inline)) {
+  auto page_of = [&](auto sp_tag, int p0) __attribute__((always_inline)) -> long long {
+    if constexpr (!decltype(sp_tag)::value) {
+      // the page's element offset as staged (and validated) in LDS
+      const uint64_t bu = (uint64_t)ctab[(p0 >> bsh) - cb0];
+      return (long long)(((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(bu >> 32)) << 32) |
+                         (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)bu));
+    } else {
+      const int phys = __builtin_amdgcn_readfirstlane(Uphys[p0 >> bsh]);
+      return phys * blk_elems + head_off;
+    }
+  };
+  auto tight_sources = [&](auto sp_tag, int tk, bool first) __attribute__((always_inline)) {
     constexpr bool SP = decltype(sp_tag)::value;
+    if (v_from_k) {
+      if (first)
 #pragma unroll
-    for (int n = 0; n < K_OPS; ++n) {
-      const int p0 = tk * NK + (64 * (wave_u + NWAVE * n)) / CK;
-      if constexpr (!SP) {
-        // the page's element offset as staged (and validated) in LDS
-        const long long boff = ctab[(p0 >> bsh) - cb0];
-        const uint64_t bu = (uint64_t)boff;
-        const long long bs_u = (long long)(((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(bu >> 32)) << 32) |
-                                           (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)bu));
-        kpage[n] = reinterpret_cast<const unsigned char*>(Kp + (bs_u + (long long)((p0 & bsm) * D)));
-      } else {
-        const int phys = __builtin_amdgcn_readfirstlane(Uphys[p0 >> bsh]);
-        kpage[n] = reinterpret_cast<const unsigned char*>(
-            Kp + (phys * blk_elems + head_off + (long long)((p0 & bsm) * D)));
+        for (int n = 0; n < K_OPS; ++n) kb[n] = page_of(sp_tag, (tk - 1) * NK + (64 * (wave_u + NWAVE * n)) / CK);
+      const long long u = (long long)((((tk - 1) * NK) & bsm) * D);
+#pragma unroll
+      for (int n = 0; n < V_OPS; ++n) vsrc[n] = Vp + (kb[n] + u) + vlane[n];
+    } else {
+#pragma unroll
+      for (int n = 0; n < V_OPS; ++n) {
+        const int p = (tk - 1) * NK + v_key[n];
+        const long long boff = SP ? (long long)Uphys[p >> bsh] * blk_elems + head_off : ctab[(p >> bsh) - cb0];
+        vsrc[n] = Vp + boff + (long long)((p & bsm) * D + v_col[n]);
       }
     }
 #pragma unroll
-    for (int n = 0; n < V_OPS; ++n) {
-      const int p = (tk - 1) * NK + v_key[n];
-      const long long boff = SP ? (long long)Uphys[p >> bsh] * blk_elems + head_off : ctab[(p >> bsh) - cb0];
-      vsrc[n] = Vp + boff + (long long)((p & bsm) * D + v_col[n]);
+    for (int n = 0; n < K_OPS; ++n) {
+      const int p0 = tk * NK + (64 * (wave_u + NWAVE * n)) / CK;
+      kb[n] = page_of(sp_tag, p0);
+      kpage[n] = reinterpret_cast<const unsigned char*>(Kp + (kb[n] + (long long)((p0 & bsm) * D)));
     }
   };
   // Mask of a whole sparse tile: a row sees an 8-key chunk when it selected
@@ -941,7 +960,7 @@ __global__ void __launch_bounds__(WQ * WK * 64) attn_mfma_kernel(AttnArgs a) {
       const bf16_bits* src = vsrc[n];  // (a named pointer: see issue_k)
       __builtin_amdgcn_global_load_lds(src, vdst + (wave + NWAVE * n) * 1024, 16, 0, 0);
     }
-    if (k + 1 < n_tight) tight_sources(sp_tag, t_lo + k + 1 + S);
+    if (k + 1 < n_tight) tight_sources(sp_tag, t_lo + k + 1 + S, false);
     if constexpr (SP) sparse_mask(t_lo + k, sc);
     softmax_bound(sc);
     // The K fragments of tile k + 1 are read before any MFMA and the V^T
@@ -995,14 +1014,14 @@ __global__ void __launch_bounds__(WQ * WK * 64) attn_mfma_kernel(AttnArgs a) {
   // (two copies of the loop: dense and sparse, each specialised)
   if (!sparse) {
     const std::integral_constant<bool, false> dense_tag;
-    if (n_tight > 0) tight_sources(dense_tag, t_lo + S);
+    if (n_tight > 0) tight_sources(dense_tag, t_lo + S, true);
     for (; k < n_tight; k += 2) {
       tight_step(dense_tag, k, sa, sb);
       tight_step(dense_tag, k + 1, sb, sa);
     }
   } else {
     const std::integral_constant<bool, true> sparse_tag;
-    if (n_tight > 0) tight_sources(sparse_tag, t_lo + S);
+    if (n_tight > 0) tight_sources(sparse_tag, t_lo + S, true);
     for (; k < n_tight; k += 2) {
       tight_step(sparse_tag, k, sa, sb);
       tight_step(sparse_tag, k + 1, sb, sa);
