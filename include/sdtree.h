@@ -226,7 +226,7 @@ sd_status sd_accept_commit(const sd_accept_shape* shape, const sd_shape* kv_shap
  * workspace (code under HIP graph capture, tight serving loops, harnesses
  * that forbid allocation).  Same arguments and results as sd_accept_commit,
  * except that there is no workspace: the acceptance walk's cross-workgroup
- * exchange slots live in a device array of the library (128 KiB, one copy per
+ * exchange slots live in a device array of the library (1 MiB, one copy per
  * GPU, held until the process ends), and the sticky error bits go to
  * `status`, a caller-owned device word (OR-ed into; read and clear it with
  * sd_device_status(status, stream, &bits)).

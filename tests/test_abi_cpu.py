@@ -88,7 +88,7 @@ def test_workspace_sizes():
     assert L.sd_workspace_bytes(4, ctypes.byref(s), 0) == 256 + 256
     a = _lib.SdAcceptShape(16, 64, 128256, 1, 64)
     # 16 workgroups per sequence: barrier state for each of the 16 sequences
-    assert L.sd_workspace_bytes(2, ctypes.byref(a), 0) == 256 + 16 * 1024
+    assert L.sd_workspace_bytes(2, ctypes.byref(a), 0) == 256 + 16 * 8192
     one = _lib.SdAcceptShape(1000000, 5, 8, 0, 5)
     assert L.sd_workspace_bytes(2, ctypes.byref(one), 0) == 256
     assert L.sd_workspace_bytes(9, ctypes.byref(s), 0) == 0

@@ -42,6 +42,10 @@ constexpr int kMaxKid = 64;          // children whose test scalars are prefetch
 constexpr int kCKRegs = 4;           // commit: 16-byte K (and V) chunks per thread per group
 constexpr int kMaxCBlk = kMaxT / 8 + 2;  // commit: blocks of the tree slots (bs >= 8)
 constexpr unsigned kSpinLimit = 1u << 20;
+constexpr int kSeg = 8;              // nodes of a first-child chain whose statistics are formed together
+constexpr int kXW = 2 * kSeg;        // exchanged 32-bit words per workgroup, at most
+static_assert(2 * kMaxP * kXW * 8 + 8 <= (int)kAccSeqBytes, "exchange slots exceed a sequence's sync bytes");
+static_assert(kMaxP * kXW <= kAT, "one polling thread per exchanged word");
 
 // Workgroup barrier for data exchanged through LDS.  __syncthreads() would
 // also wait for every outstanding global load (on this architecture a
@@ -170,6 +174,17 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
   // children, so the history never overflows
   __shared__ double zinv[MODE == kRejection ? kMaxT : 1];
   __shared__ __align__(8) uint32_t xv[kMaxP][2];
+  // First-child chains (cached rows, rejection sampling): the first child of
+  // every node, the chain's nodes, each node's first-child test scalars and
+  // draw uniform, and the P workgroups' statistics of every chain node.
+  constexpr bool kSegOn = CACHED && MODE == kRejection;
+  __shared__ int fk[kSegOn ? kMaxT : 1];
+  __shared__ int s_seg[kSeg];
+  __shared__ int s_seglen;
+  __shared__ float seg_l[kSeg], seg_q[kSeg], seg_u[kSeg], seg_ud[kSeg];
+  __shared__ float sred_f[kSegOn ? kSeg : 1][kAW];
+  __shared__ double sred_d[kSegOn ? kSeg : 1][kAW];
+  __shared__ __align__(8) uint32_t xs[kMaxP][kSegOn ? kXW : 2];
   __shared__ int s_flag, s_to, s_first, s_last, s_x;
 
   const int P = a.P;
@@ -186,10 +201,11 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
   const int T = a.T, V = a.V;
   const int bt = a.tree_stride ? b : 0;
   int32_t* path = a.path + (size_t)b * T;
-  // Exchange slots of this sequence: [2 parities][P workgroups][2 values], each
-  // a 64-bit word (barrier number << 32 | 32-bit value), then the exit counter.
+  // Exchange slots of this sequence: [2 parities][P workgroups][kXW values],
+  // each a 64-bit word (barrier number << 32 | 32-bit value), then the exit
+  // counter.
   unsigned long long* slots = reinterpret_cast<unsigned long long*>(a.sync + (size_t)b * kAccSeqBytes);
-  unsigned* done = reinterpret_cast<unsigned*>(slots + 2 * kMaxP * 2);
+  unsigned* done = reinterpret_cast<unsigned*>(slots + 2 * kMaxP * kXW);
 
   const int sl0 = min(wg * a.SL, V), sl1 = min(sl0 + a.SL, V);
   const int NC = a.NC;
@@ -350,6 +366,13 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
     }
     return;
   }
+  if constexpr (kSegOn) {
+    // the first (lowest-index) child of every node; T where there is none
+    for (int n = tid; n < T; n += kAT) fk[n] = T;
+    lds_sync();
+    for (int n = 1 + tid; n < T; n += kAT) atomicMin(&fk[s_par[n]], n);
+    lds_sync();
+  }
 
   // ---- cross-workgroup exchange ---------------------------------------------
   // exchange(v0, v1): every workgroup of the sequence publishes two 32-bit
@@ -368,18 +391,18 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
         xv[0][1] = v1;
       }
     } else {
-      unsigned long long* sl = slots + (size_t)(nbar & 1) * kMaxP * 2;
+      unsigned long long* sl = slots + (size_t)(nbar & 1) * kMaxP * kXW;
       const unsigned long long tag = (unsigned long long)(unsigned)nbar << 32;
       if (tid == 0) {
-        __hip_atomic_store(sl + wg * 2 + 0, tag | v0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(sl + wg * 2 + 1, tag | v1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(sl + wg * kXW + 0, tag | v0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(sl + wg * kXW + 1, tag | v1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
       if (tid < P) {
         unsigned long long w0, w1;
         unsigned spins = 0;
         for (;;) {
-          w0 = __hip_atomic_load(sl + tid * 2 + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          w1 = __hip_atomic_load(sl + tid * 2 + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          w0 = __hip_atomic_load(sl + tid * kXW + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          w1 = __hip_atomic_load(sl + tid * kXW + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           if ((w0 >> 32) == (unsigned)nbar && (w1 >> 32) == (unsigned)nbar) break;
           if (++spins > kSpinLimit) {
             s_to = 1;
@@ -389,6 +412,36 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
         }
         xv[tid][0] = (uint32_t)w0;
         xv[tid][1] = (uint32_t)w1;
+      }
+    }
+    lds_sync();
+  };
+  // exchange_words(nw, w): as exchange, with nw <= kXW words per workgroup
+  // (thread t < nw publishes word t, w); thread j * nw + k polls word k of
+  // workgroup j, and the P * nw words land in xs[j][k].
+  auto exchange_words = [&](int nw, uint32_t w) {
+    lds_sync();
+    ++nbar;
+    if (P == 1) {
+      if (tid < nw) xs[0][tid] = w;
+    } else {
+      unsigned long long* sl = slots + (size_t)(nbar & 1) * kMaxP * kXW;
+      const unsigned long long tag = (unsigned long long)(unsigned)nbar << 32;
+      if (tid < nw) __hip_atomic_store(sl + wg * kXW + tid, tag | w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (tid < P * nw) {
+        const int j = tid / nw, k = tid - j * nw;
+        unsigned long long x;
+        unsigned spins = 0;
+        for (;;) {
+          x = __hip_atomic_load(sl + j * kXW + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if ((x >> 32) == (unsigned)nbar) break;
+          if (++spins > kSpinLimit) {
+            s_to = 1;
+            break;
+          }
+          __builtin_amdgcn_s_sleep(1);
+        }
+        xs[j][k] = (uint32_t)x;
       }
     }
     lds_sync();
@@ -477,6 +530,134 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
         for (int e = 0; e < 8; ++e) q8[e] = 0.f;
       }
     }
+  };
+
+  // Statistics of this thread's part of a cached row `rw` (its kMaxCh
+  // chunks): the wavefront's max first (a float reduction), then every weight
+  // relative to it at once, so no step of the sum waits on a rescale.  The
+  // wavefront's (max, mass) are left in lane 63.
+  auto row_stats = [&](const uint4* rw, float& mt, double& st) {
+    float v[kMaxCh][8];
+    float cm[kMaxCh];
+#pragma unroll
+    for (int c = 0; c < kMaxCh; ++c) {
+      if (c < NC && y0_of(c) < sl1) {
+        uint4 u = rw[c];
+        asm volatile("" : "+v"(u.x), "+v"(u.y), "+v"(u.z), "+v"(u.w));
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[c][e] = bf16_to_f32((bf16_bits)(w[e >> 1] >> (16 * (e & 1))));
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[c][e] = -INFINITY;
+      }
+      cm[c] = fmaxf(fmaxf(fmaxf(v[c][0], v[c][1]), fmaxf(v[c][2], v[c][3])),
+                    fmaxf(fmaxf(v[c][4], v[c][5]), fmaxf(v[c][6], v[c][7])));
+    }
+    float lm = cm[0];
+#pragma unroll
+    for (int c = 1; c < kMaxCh; ++c) lm = fmaxf(lm, cm[c]);
+    auto mvf = [](auto c, auto r, float old, float x) { return dpp_f<decltype(c)::value, decltype(r)::value>(old, x); };
+    lm = dpp_reduce<true>(lm, -INFINITY, mvf, [](float x, float y) { return fmaxf(x, y); });
+    mt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lm), 63));   // (the reduction ends in lane 63)
+    double ls = 0.0;
+    if (mt > -INFINITY) {
+      double cs[kMaxCh];
+#pragma unroll
+      for (int c = 0; c < kMaxCh; ++c) {
+        double w[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) w[e] = (double)__builtin_amdgcn_exp2f((v[c][e] - mt) * c2);
+        cs[c] = ((w[0] + w[1]) + (w[2] + w[3])) + ((w[4] + w[5]) + (w[6] + w[7]));
+      }
+      ls = cs[0];
+#pragma unroll
+      for (int c = 1; c < kMaxCh; ++c) ls += cs[c];
+    }
+    st = wave_sum_d(ls);
+  };
+  // The workgroup's (max, mass) from its wavefronts' (in wf[], wd[]), as a
+  // two-value exchange carries it.
+  auto wg_stats = [&](const float* wf, const double* wd, float& mw, double& sw) {
+    mw = wf[0];
+    for (int w = 1; w < kAW; ++w) mw = fmaxf(mw, wf[w]);
+    sw = 0.0;
+    if (mw > -INFINITY)
+      for (int w = 0; w < kAW; ++w)
+        if (wf[w] > -INFINITY) sw += wd[w] * (double)__builtin_amdgcn_exp2f((wf[w] - mw) * c2);
+  };
+  // Statistics of a first-child chain (cached rows, rejection sampling).  In
+  // the seeded trees the walk accepts a node's first child nine times in ten,
+  // so the chain from `start` (up to kSeg nodes: start, its first child, that
+  // child's first child, ...) is likely the path ahead.  Its rows are loaded
+  // together, every node's (max, mass) formed as the per-node pass would
+  // form it, and all of them exchanged at once; so is each node's
+  // first-child test scalars and draw uniform.  A node of the chain then
+  // needs no pass and no exchange for its statistics.
+  auto seg_build = [&](int start, bool start_row) {   // start_row: lc holds start's row
+    if (tid == 0) {
+      int n = start, len = 0;
+      for (;;) {
+        s_seg[len++] = n;
+        if (len == kSeg) break;
+        const int f = fk[n];
+        if (f >= T) break;
+        n = f;
+      }
+      s_seglen = len;
+    }
+    lds_sync();
+    const int len = s_seglen;
+    LT gl = LT(0);
+    float gq = 0.f, gu = 0.f, gud = 0.f;
+    if (tid < len) {
+      const int n = s_seg[tid];
+      const int f = fk[n];
+      const int fn = f < T ? f : n;   // (a leaf reads its own values, unused)
+      const int x = s_tok[fn];
+      gl = row_of(n)[x];
+      gq = a.draft[((size_t)b * T + n) * V + x];
+      gu = a.unif[((size_t)b * T + fn) * 2 + 0];
+      gud = a.unif[((size_t)b * T + n) * 2 + 1];
+    }
+    uint4 sr[kSeg][kMaxCh];
+#pragma unroll
+    for (int j = 0; j < kSeg; ++j)
+      if (j < len) {
+        if (j == 0 && start_row) {
+#pragma unroll
+          for (int c = 0; c < kMaxCh; ++c) sr[0][c] = lc[c];
+        } else {
+          load_row(row_of(s_seg[j]), sr[j]);
+        }
+      }
+#pragma unroll
+    for (int j = 0; j < kSeg; ++j)
+      if (j < len) {
+        float mt;
+        double st;
+        row_stats(sr[j], mt, st);
+        if (lane == 63) {
+          sred_f[j][wave] = mt;
+          sred_d[j][wave] = st;
+        }
+      }
+    if (tid < len) {
+      if constexpr (kBF) seg_l[tid] = bf16_to_f32(gl);
+      else seg_l[tid] = gl;
+      seg_q[tid] = gq;
+      seg_u[tid] = gu;
+      seg_ud[tid] = gud;
+    }
+    lds_sync();
+    uint32_t w = 0;
+    if (tid < 2 * len) {
+      float mw;
+      double sw;
+      wg_stats(sred_f[tid >> 1], sred_d[tid >> 1], mw, sw);
+      w = (tid & 1) ? __float_as_uint((float)sw) : __float_as_uint(mw);
+    }
+    exchange_words(2 * len, w);
   };
 
   // Inverse-CDF draw: slices' masses in mass[0..P); threshold u * total.  The
@@ -600,8 +781,16 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
 
   int cur = 0, plen = 1;
   bool have_row = true;    // lc already holds the current node's row (the root's since the start)
+  int seg_len = 0, seg_i = 0;   // the current chain's length and cur's place in it
   if (wg == 0 && tid == 0) path[0] = 0;
   for (int step = 0; step < T; ++step) {
+    if constexpr (kSegOn) {
+      if (seg_i >= seg_len) {
+        seg_build(cur, have_row);
+        seg_len = s_seglen;
+        seg_i = 0;
+      }
+    }
     const int nk = gather_children(cur);
     row = row_of(cur);
     // Issue this node's loads together: the scalars of the child tests, the
@@ -612,8 +801,8 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
     // a branch around the loads would make its merge wait for them)
     LT kl_raw = LT(0);
     float kq = 0.f, ku = 0.f;
-    const bool kid_lane = mss && tid < min(nk, kMaxKid);
-    if constexpr (mss) {
+    const bool kid_lane = mss && !kSegOn && tid < min(nk, kMaxKid);
+    if constexpr (mss && !kSegOn) {
       const int kid = kids[tid < kMaxKid ? tid : 0];
       const int node = kid_lane ? kid : 0;
       const int x = s_tok[node];
@@ -621,10 +810,23 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
       kq = a.draft[((size_t)b * T + cur) * V + x];
       ku = a.unif[((size_t)b * T + node) * 2 + 0];
     }
-    if (!have_row) load_row(row, lc);
+    // (a chain node's row is loaded only when a rejection or a draw needs it)
+    if constexpr (!kSegOn) {
+      if (!have_row) load_row(row, lc);
+    }
     // the uniform of this node's draw, loaded with the rest so that the draw
     // does not wait for it
-    const float u_draw = a.unif[((size_t)b * T + cur) * 2 + 1];
+    float u_draw;
+    if constexpr (kSegOn) u_draw = seg_ud[seg_i];
+    else u_draw = a.unif[((size_t)b * T + cur) * 2 + 1];
+    auto need_row = [&]() {
+      if constexpr (kSegOn) {
+        if (!have_row) {
+          load_row(row, lc);
+          have_row = true;
+        }
+      }
+    };
     if constexpr (mss) qrow = a.draft + ((size_t)b * T + cur) * V;
     // (greedy prefetches the first child's row now; the other rules after
     // the statistics exchange, whose polling loads would otherwise wait for
@@ -700,47 +902,13 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
       }
     } else {
       // statistics of this slice: its max and the mass relative to it,
-      // merged across lanes and waves (in lane 63 of each wave)
+      // merged across lanes and waves (in lane 63 of each wave); a chain
+      // node has them from its chain's exchange
+      if constexpr (!kSegOn) {
       float mt = -INFINITY;
       double st = 0.0;
       if constexpr (CACHED) {
-        // The slice is in registers: the wave's max first (a float
-        // reduction), then every weight relative to it at once, so no step
-        // of the sum waits on a rescale.
-        float v[kMaxCh][8];
-        float cm[kMaxCh];
-#pragma unroll
-        for (int c = 0; c < kMaxCh; ++c) {
-          if (c < NC) {
-            logits8(c, v[c]);
-          } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) v[c][e] = -INFINITY;
-          }
-          cm[c] = fmaxf(fmaxf(fmaxf(v[c][0], v[c][1]), fmaxf(v[c][2], v[c][3])),
-                        fmaxf(fmaxf(v[c][4], v[c][5]), fmaxf(v[c][6], v[c][7])));
-        }
-        float lm = cm[0];
-#pragma unroll
-        for (int c = 1; c < kMaxCh; ++c) lm = fmaxf(lm, cm[c]);
-        auto mvf = [](auto c, auto r, float old, float x) { return dpp_f<decltype(c)::value, decltype(r)::value>(old, x); };
-        lm = dpp_reduce<true>(lm, -INFINITY, mvf, [](float x, float y) { return fmaxf(x, y); });
-        mt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lm), 63));   // (the reduction ends in lane 63)
-        double ls = 0.0;
-        if (mt > -INFINITY) {
-          double cs[kMaxCh];
-#pragma unroll
-          for (int c = 0; c < kMaxCh; ++c) {
-            double w[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) w[e] = (double)__builtin_amdgcn_exp2f((v[c][e] - mt) * c2);
-            cs[c] = ((w[0] + w[1]) + (w[2] + w[3])) + ((w[4] + w[5]) + (w[6] + w[7]));
-          }
-          ls = cs[0];
-#pragma unroll
-          for (int c = 1; c < kMaxCh; ++c) ls += cs[c];
-        }
-        st = wave_sum_d(ls);
+        row_stats(lc, mt, st);   // the slice is in registers
       } else {
       FOR_CHUNKS(c,
         float v[8];
@@ -781,12 +949,9 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
         red_d[wave] = st;
       }
       lds_sync();
-      float mw = red_f[0];
-      for (int w = 1; w < kAW; ++w) mw = fmaxf(mw, red_f[w]);
-      double sw = 0.0;
-      if (mw > -INFINITY)
-        for (int w = 0; w < kAW; ++w)
-          if (red_f[w] > -INFINITY) sw += red_d[w] * (double)__builtin_amdgcn_exp2f((red_f[w] - mw) * c2);
+      float mw;
+      double sw;
+      wg_stats(red_f, red_d, mw, sw);
       // the children's test scalars reach LDS only now: their loads were in
       // flight during the statistics pass and the exchange's wait
       if (kid_lane) {
@@ -797,6 +962,7 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
       }
       exchange(__float_as_uint(mw), __float_as_uint((float)sw));
       if (nk > 0) load_row(row_of(kids[0]), pfc);
+      }
       // Slice j's (max, mass) sits in lane j % 16 of every wavefront; the
       // global max and the masses' sum are formed by butterflies over those
       // 16 lanes, which leave the same value in every lane (each step adds a
@@ -805,8 +971,16 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
       double z0;
       {
         const int j = lane & 15;
-        const float mj = j < P ? xf(j, 0) : -INFINITY;
-        const float sj = j < P ? xf(j, 1) : 0.f;
+        float mj = -INFINITY, sj = 0.f;
+        if (j < P) {
+          if constexpr (kSegOn) {
+            mj = __uint_as_float(xs[j][2 * seg_i + 0]);
+            sj = __uint_as_float(xs[j][2 * seg_i + 1]);
+          } else {
+            mj = xf(j, 0);
+            sj = xf(j, 1);
+          }
+        }
         auto mvf = [](auto c, auto r, float old, float x) { return dpp_f<decltype(c)::value, decltype(r)::value>(old, x); };
         auto mvd = [](auto c, auto r, double old, double x) { return dpp_d<decltype(c)::value, decltype(r)::value>(old, x); };
         m = dpp_reduce<false>(mj, -INFINITY, mvf, [](float x, float y) { return fmaxf(x, y); });
@@ -877,11 +1051,12 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
           }
         };
         for (int c = 0; c < nk; ++c) {
-          if (c > 0 && c % kMaxKid == 0) {
-            // the next batch of children's test scalars (wide nodes only);
-            // these loads are waited for here, off the common path
+          if ((c > 0 && c % kMaxKid == 0) || (kSegOn && c == 1)) {
+            // the next batch of children's test scalars (wide nodes, and a
+            // chain node once its first child is rejected); these loads are
+            // waited for here, off the common path
             lds_sync();
-            const int cc = c + tid;
+            const int cc = c - c % kMaxKid + tid;
             if (tid < kMaxKid && cc < nk) {
               const int node = kids[cc];
               const int x = s_tok[node];
@@ -892,9 +1067,17 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
             lds_sync();
           }
           const int ci = c % kMaxKid;
-          const float lx = kid_l[ci];
-          const double qx = (double)kid_q[ci];
-          const double u = (double)kid_u[ci];
+          float lx;
+          double qx, u;
+          if (kSegOn && c == 0) {
+            lx = seg_l[seg_i];
+            qx = (double)seg_q[seg_i];
+            u = (double)seg_u[seg_i];
+          } else {
+            lx = kid_l[ci];
+            qx = (double)kid_q[ci];
+            u = (double)kid_u[ci];
+          }
           const double rx = resid(p_of(lx), qx, nrej);
           if (u * qx < rx) {
             nxt = c;
@@ -905,6 +1088,7 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
           double pz = 0.0;
           if constexpr (CACHED) {
             if (nrej == 0) {
+              need_row();
               // The draft row's slice is read only now: a first child accepted
               // at once never needs it, and it is two thirds of a node's bytes
               // (float32 against bf16 logits), which all sequences' walks
@@ -969,7 +1153,10 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
           ++nrej;
         }
         if (nxt < 0) {
-          if (nrej == 0) init_rr();   // a leaf: the draw is from p itself
+          if (nrej == 0) {
+            need_row();
+            init_rr();   // a leaf: the draw is from p itself
+          }
           const float u = u_draw;
           const int nr = nrej;
           // weights in the units of mass[]: the residual times `units`
@@ -998,7 +1185,11 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
     ++plen;
     cur = nnode;
     have_row = false;
-    if constexpr (CACHED) {
+    if constexpr (kSegOn) {
+      // the first child is the chain's next node; any other starts a chain
+      if (nxt == 0 && seg_i + 1 < seg_len) ++seg_i;
+      else seg_len = 0;
+    } else if constexpr (CACHED) {
       if (nxt == 0) {
 #pragma unroll
         for (int c = 0; c < kMaxCh; ++c) lc[c] = pfc[c];
@@ -1034,7 +1225,7 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
     if (tid == 0) s_flag = atomicAdd(done, 1u) == (unsigned)P - 1;
     lds_sync();
     if (s_flag) {
-      for (int j = tid; j < 2 * kMaxP * 2; j += kAT)
+      for (int j = tid; j < 2 * kMaxP * kXW; j += kAT)
         __hip_atomic_store(slots + j, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (tid == 0) {
         if (commit && !cerr) a.cctx[b] = c_ctx + plen;

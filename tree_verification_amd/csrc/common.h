@@ -186,7 +186,7 @@ struct AttnArgs {
 
 // Per-sequence synchronisation scratch of the acceptance walk: barrier
 // counter, exit counter, a broadcast slot, then [2][P][2] float64 partials.
-constexpr size_t kAccSeqBytes = 1024;
+constexpr size_t kAccSeqBytes = 8192;
 
 struct AcceptArgs {
   const void* logits;
