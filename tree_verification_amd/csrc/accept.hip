@@ -24,7 +24,10 @@
 // the first child's logits (the likeliest next node).  An inverse-CDF draw
 // picks the slice holding the crossing point from the per-slice masses and
 // only that workgroup rescans its slice.  Sums are float64; the probability a
-// test is taken on is recomputed in float64.
+// test is taken on is recomputed in float64.  With rejection sampling over
+// register-cached rows, the statistics of a whole first-child chain (the
+// likely path) are formed and exchanged in one round, so a chain node whose
+// first child is accepted takes no pass and no exchange.
 #include <mutex>
 #include <type_traits>
 
@@ -42,7 +45,7 @@ constexpr int kMaxKid = 64;          // children whose test scalars are prefetch
 constexpr int kCKRegs = 4;           // commit: 16-byte K (and V) chunks per thread per group
 constexpr int kMaxCBlk = kMaxT / 8 + 2;  // commit: blocks of the tree slots (bs >= 8)
 constexpr unsigned kSpinLimit = 1u << 20;
-constexpr int kSeg = 8;              // nodes of a first-child chain whose statistics are formed together
+constexpr int kSeg = 6;              // nodes of a first-child chain whose statistics are formed together
 constexpr int kXW = 2 * kSeg;        // exchanged 32-bit words per workgroup, at most
 static_assert(2 * kMaxP * kXW * 8 + 8 <= (int)kAccSeqBytes, "exchange slots exceed a sequence's sync bytes");
 static_assert(kMaxP * kXW <= kAT, "one polling thread per exchanged word");
@@ -782,16 +785,20 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
   int cur = 0, plen = 1;
   bool have_row = true;    // lc already holds the current node's row (the root's since the start)
   int seg_len = 0, seg_i = 0;   // the current chain's length and cur's place in it
+  int lc_node = 0;              // (chains) the node whose row lc holds
   if (wg == 0 && tid == 0) path[0] = 0;
   for (int step = 0; step < T; ++step) {
     if constexpr (kSegOn) {
       if (seg_i >= seg_len) {
-        seg_build(cur, have_row);
+        seg_build(cur, lc_node == cur);
         seg_len = s_seglen;
         seg_i = 0;
       }
     }
-    const int nk = gather_children(cur);
+    // (a chain node lists its children only once its first child is rejected)
+    int nk;
+    if constexpr (kSegOn) nk = fk[cur] < T ? 1 : 0;
+    else nk = gather_children(cur);
     row = row_of(cur);
     // Issue this node's loads together: the scalars of the child tests, the
     // row (unless prefetched), the draft row, and the first child's row.
@@ -821,9 +828,9 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
     else u_draw = a.unif[((size_t)b * T + cur) * 2 + 1];
     auto need_row = [&]() {
       if constexpr (kSegOn) {
-        if (!have_row) {
+        if (lc_node != cur) {
           load_row(row, lc);
-          have_row = true;
+          lc_node = cur;
         }
       }
     };
@@ -1151,6 +1158,7 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
           }
           lds_sync();
           ++nrej;
+          if (kSegOn && c == 0) nk = gather_children(cur);
         }
         if (nxt < 0) {
           if (nrej == 0) {
@@ -1180,7 +1188,7 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
       }
     }
     if (stop) break;
-    const int nnode = kids[nxt];
+    const int nnode = (kSegOn && nxt == 0) ? fk[cur] : kids[nxt];
     if (wg == 0 && tid == 0) path[plen] = nnode;
     ++plen;
     cur = nnode;
