@@ -24,10 +24,11 @@
 // the first child's logits (the likeliest next node).  An inverse-CDF draw
 // picks the slice holding the crossing point from the per-slice masses and
 // only that workgroup rescans its slice.  Sums are float64; the probability a
-// test is taken on is recomputed in float64.  With rejection sampling over
-// register-cached rows, the statistics of a whole first-child chain (the
-// likely path) are formed and exchanged in one round, so a chain node whose
-// first child is accepted takes no pass and no exchange.
+// test is taken on is recomputed in float64.  With rejection sampling or
+// greedy acceptance over register-cached rows, the statistics (or argmaxes)
+// of a whole first-child chain (the likely path) are formed and exchanged in
+// one round, so a chain node whose first child is accepted takes no pass and
+// no exchange.
 #include <mutex>
 #include <type_traits>
 
@@ -177,16 +178,18 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
   // children, so the history never overflows
   __shared__ double zinv[MODE == kRejection ? kMaxT : 1];
   __shared__ __align__(8) uint32_t xv[kMaxP][2];
-  // First-child chains (cached rows, rejection sampling): the first child of
-  // every node, the chain's nodes, each node's first-child test scalars and
-  // draw uniform, and the P workgroups' statistics of every chain node.
-  constexpr bool kSegOn = CACHED && MODE == kRejection;
+  // First-child chains (cached rows; rejection sampling or greedy): the first
+  // child of every node, the chain's nodes, each node's first-child test
+  // scalars and draw uniform (rejection sampling), and the P workgroups'
+  // statistics (or argmax) of every chain node.
+  constexpr bool kSegOn = CACHED && (MODE == kRejection || MODE == kGreedy);
   __shared__ int fk[kSegOn ? kMaxT : 1];
   __shared__ int s_seg[kSeg];
   __shared__ int s_seglen;
   __shared__ float seg_l[kSeg], seg_q[kSeg], seg_u[kSeg], seg_ud[kSeg];
   __shared__ float sred_f[kSegOn ? kSeg : 1][kAW];
   __shared__ double sred_d[kSegOn ? kSeg : 1][kAW];
+  __shared__ int sred_i[kSegOn ? kSeg : 1][kAW];
   __shared__ __align__(8) uint32_t xs[kMaxP][kSegOn ? kXW : 2];
   __shared__ int s_flag, s_to, s_first, s_last, s_x;
 
@@ -579,6 +582,37 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
     }
     st = wave_sum_d(ls);
   };
+  // Argmax (lowest id among equal maxima) of this thread's part of a cached
+  // row, reduced over the wavefront into lane 63.
+  auto row_argmax = [&](const uint4* rw, float& bv, int& bi) {
+    bv = -INFINITY;
+    bi = V;
+#pragma unroll
+    for (int c = 0; c < kMaxCh; ++c) {
+      const int y0 = y0_of(c);
+      if (c < NC && y0 < sl1) {
+        const uint4 u = rw[c];
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float v = bf16_to_f32((bf16_bits)(w[e >> 1] >> (16 * (e & 1))));
+          if (v > bv) {
+            bv = v;
+            bi = y0 + e;
+          }
+        }
+      }
+    }
+    struct VI { float v; int i; };
+    auto mv = [&](auto c, auto r, VI old, VI x) {
+      return VI{dpp_f<decltype(c)::value, decltype(r)::value>(old.v, x.v),
+                dpp_i<decltype(c)::value, decltype(r)::value>(old.i, x.i)};
+    };
+    auto comb = [](VI x, VI y) { return (y.v > x.v || (y.v == x.v && y.i < x.i)) ? y : x; };
+    const VI t = dpp_reduce<true>(VI{bv, bi}, VI{-INFINITY, V}, mv, comb);
+    bv = t.v;
+    bi = t.i;
+  };
   // The workgroup's (max, mass) from its wavefronts' (in wf[], wd[]), as a
   // two-value exchange carries it.
   auto wg_stats = [&](const float* wf, const double* wd, float& mw, double& sw) {
@@ -613,7 +647,7 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
     const int len = s_seglen;
     LT gl = LT(0);
     float gq = 0.f, gu = 0.f, gud = 0.f;
-    if (tid < len) {
+    if (mss && tid < len) {
       const int n = s_seg[tid];
       const int f = fk[n];
       const int fn = f < T ? f : n;   // (a leaf reads its own values, unused)
@@ -637,15 +671,25 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
 #pragma unroll
     for (int j = 0; j < kSeg; ++j)
       if (j < len) {
-        float mt;
-        double st;
-        row_stats(sr[j], mt, st);
-        if (lane == 63) {
-          sred_f[j][wave] = mt;
-          sred_d[j][wave] = st;
+        if constexpr (MODE == kGreedy) {
+          float bv;
+          int bi;
+          row_argmax(sr[j], bv, bi);
+          if (lane == 63) {
+            sred_f[j][wave] = bv;
+            sred_i[j][wave] = bi;
+          }
+        } else {
+          float mt;
+          double st;
+          row_stats(sr[j], mt, st);
+          if (lane == 63) {
+            sred_f[j][wave] = mt;
+            sred_d[j][wave] = st;
+          }
         }
       }
-    if (tid < len) {
+    if (mss && tid < len) {
       if constexpr (kBF) seg_l[tid] = bf16_to_f32(gl);
       else seg_l[tid] = gl;
       seg_q[tid] = gq;
@@ -655,10 +699,23 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
     lds_sync();
     uint32_t w = 0;
     if (tid < 2 * len) {
-      float mw;
-      double sw;
-      wg_stats(sred_f[tid >> 1], sred_d[tid >> 1], mw, sw);
-      w = (tid & 1) ? __float_as_uint((float)sw) : __float_as_uint(mw);
+      const int j = tid >> 1;
+      if constexpr (MODE == kGreedy) {
+        // the workgroup's argmax, combined over its wavefronts in order
+        float bv = sred_f[j][0];
+        int bi = sred_i[j][0];
+        for (int w2 = 1; w2 < kAW; ++w2)
+          if (sred_f[j][w2] > bv || (sred_f[j][w2] == bv && sred_i[j][w2] < bi)) {
+            bv = sred_f[j][w2];
+            bi = sred_i[j][w2];
+          }
+        w = (tid & 1) ? (uint32_t)bi : __float_as_uint(bv);
+      } else {
+        float mw;
+        double sw;
+        wg_stats(sred_f[j], sred_d[j], mw, sw);
+        w = (tid & 1) ? __float_as_uint((float)sw) : __float_as_uint(mw);
+      }
     }
     exchange_words(2 * len, w);
   };
@@ -824,7 +881,7 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
     // the uniform of this node's draw, loaded with the rest so that the draw
     // does not wait for it
     float u_draw;
-    if constexpr (kSegOn) u_draw = seg_ud[seg_i];
+    if constexpr (kSegOn && mss) u_draw = seg_ud[seg_i];
     else u_draw = a.unif[((size_t)b * T + cur) * 2 + 1];
     auto need_row = [&]() {
       if constexpr (kSegOn) {
@@ -838,71 +895,98 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
     // (greedy prefetches the first child's row now; the other rules after
     // the statistics exchange, whose polling loads would otherwise wait for
     // it: vector loads return in order)
-    if constexpr (MODE == kGreedy) {
+    if constexpr (MODE == kGreedy && !kSegOn) {
       if (nk > 0) load_row(row_of(kids[0]), pfc);
     }
     int nxt = -1;
     bool stop = false;
     if constexpr (MODE == kGreedy) {
-      // argmax, lowest id among equal maxima
-      float bv = -INFINITY;
-      int bi = V;
-      FOR_CHUNKS(c,
-        float v[8];
-        logits8(c, v);
-        const int y0 = y0_of(c);
-        _Pragma("unroll")
-        for (int e = 0; e < 8; ++e)
-          if (v[e] > bv) {
-            bv = v[e];
-            bi = y0 + e;
-          }
-      )
-      {
-        struct VI { float v; int i; };
-        auto mv = [&](auto c, auto r, VI old, VI x) {
-          return VI{dpp_f<decltype(c)::value, decltype(r)::value>(old.v, x.v),
-                    dpp_i<decltype(c)::value, decltype(r)::value>(old.i, x.i)};
-        };
-        auto comb = [](VI x, VI y) { return (y.v > x.v || (y.v == x.v && y.i < x.i)) ? y : x; };
-        const VI t = dpp_reduce<true>(VI{bv, bi}, VI{-INFINITY, V}, mv, comb);
-        bv = t.v;
-        bi = t.i;
-      }
-      lds_sync();
-      if (lane == 63) {
-        red_f[wave] = bv;
-        red_i[wave] = bi;
-      }
-      lds_sync();
-      bv = red_f[0];
-      bi = red_i[0];
-      for (int w = 1; w < kAW; ++w)
-        if (red_f[w] > bv || (red_f[w] == bv && red_i[w] < bi)) {
-          bv = red_f[w];
-          bi = red_i[w];
-        }
-      exchange(__float_as_uint(bv), (uint32_t)bi);
+      // argmax, lowest id among equal maxima (a chain node has its slices'
+      // argmaxes from its chain's exchange)
       float gv = -INFINITY;
       int gi = V;
-      {
-        uint32_t x0[kMaxP], x1[kMaxP];
-        read_pairs(x0, x1, __float_as_uint(-INFINITY), (uint32_t)V);
+      if constexpr (kSegOn) {
 #pragma unroll
         for (int j = 0; j < kMaxP; ++j) {
-          const float v = __uint_as_float(x0[j]);
-          const int i = (int)x1[j];
+          const float v = j < P ? __uint_as_float(xs[j][2 * seg_i + 0]) : -INFINITY;
+          const int i = j < P ? (int)xs[j][2 * seg_i + 1] : V;
           if (v > gv || (v == gv && i < gi)) {
             gv = v;
             gi = i;
           }
         }
-      }
-      for (int c = 0; c < nk; ++c)
-        if (s_tok[kids[c]] == gi) {
-          nxt = c;
-          break;
+      } else {
+        float bv = -INFINITY;
+        int bi = V;
+        FOR_CHUNKS(c,
+          float v[8];
+          logits8(c, v);
+          const int y0 = y0_of(c);
+          _Pragma("unroll")
+          for (int e = 0; e < 8; ++e)
+            if (v[e] > bv) {
+              bv = v[e];
+              bi = y0 + e;
+            }
+        )
+        {
+          struct VI { float v; int i; };
+          auto mv = [&](auto c, auto r, VI old, VI x) {
+            return VI{dpp_f<decltype(c)::value, decltype(r)::value>(old.v, x.v),
+                      dpp_i<decltype(c)::value, decltype(r)::value>(old.i, x.i)};
+          };
+          auto comb = [](VI x, VI y) { return (y.v > x.v || (y.v == x.v && y.i < x.i)) ? y : x; };
+          const VI t = dpp_reduce<true>(VI{bv, bi}, VI{-INFINITY, V}, mv, comb);
+          bv = t.v;
+          bi = t.i;
         }
+        lds_sync();
+        if (lane == 63) {
+          red_f[wave] = bv;
+          red_i[wave] = bi;
+        }
+        lds_sync();
+        bv = red_f[0];
+        bi = red_i[0];
+        for (int w = 1; w < kAW; ++w)
+          if (red_f[w] > bv || (red_f[w] == bv && red_i[w] < bi)) {
+            bv = red_f[w];
+            bi = red_i[w];
+          }
+        exchange(__float_as_uint(bv), (uint32_t)bi);
+        {
+          uint32_t x0[kMaxP], x1[kMaxP];
+          read_pairs(x0, x1, __float_as_uint(-INFINITY), (uint32_t)V);
+  #pragma unroll
+          for (int j = 0; j < kMaxP; ++j) {
+            const float v = __uint_as_float(x0[j]);
+            const int i = (int)x1[j];
+            if (v > gv || (v == gv && i < gi)) {
+              gv = v;
+              gi = i;
+            }
+          }
+        }
+      }
+      if constexpr (kSegOn) {
+        // the first child first; the others are listed only when it misses
+        if (nk > 0 && s_tok[fk[cur]] == gi) {
+          nxt = 0;
+        } else if (nk > 0) {
+          nk = gather_children(cur);
+          for (int c = 1; c < nk; ++c)
+            if (s_tok[kids[c]] == gi) {
+              nxt = c;
+              break;
+            }
+        }
+      } else {
+        for (int c = 0; c < nk; ++c)
+          if (s_tok[kids[c]] == gi) {
+            nxt = c;
+            break;
+          }
+      }
       if (nxt < 0) {
         if (wg == 0 && tid == 0) a.bonus[b] = gi;
         stop = true;
