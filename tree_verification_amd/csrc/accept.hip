@@ -24,11 +24,10 @@
 // the first child's logits (the likeliest next node).  An inverse-CDF draw
 // picks the slice holding the crossing point from the per-slice masses and
 // only that workgroup rescans its slice.  Sums are float64; the probability a
-// test is taken on is recomputed in float64.  With rejection sampling or
-// greedy acceptance over register-cached rows, the statistics (or argmaxes)
-// of a whole first-child chain (the likely path) are formed and exchanged in
-// one round, so a chain node whose first child is accepted takes no pass and
-// no exchange.
+// test is taken on is recomputed in float64.  Over register-cached rows, the
+// statistics (argmaxes; drawn tokens) of a whole first-child chain (the
+// likely path) are formed and exchanged in one round, so a chain node whose
+// first child is accepted takes no pass and no exchange.
 #include <mutex>
 #include <type_traits>
 
@@ -178,11 +177,11 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
   // children, so the history never overflows
   __shared__ double zinv[MODE == kRejection ? kMaxT : 1];
   __shared__ __align__(8) uint32_t xv[kMaxP][2];
-  // First-child chains (cached rows; rejection sampling or greedy): the first
-  // child of every node, the chain's nodes, each node's first-child test
-  // scalars and draw uniform (rejection sampling), and the P workgroups'
-  // statistics (or argmax) of every chain node.
-  constexpr bool kSegOn = CACHED && (MODE == kRejection || MODE == kGreedy);
+  // First-child chains (cached rows, every rule): the first child of every
+  // node, the chain's nodes, each node's first-child test scalars (rejection
+  // sampling) and draw uniform, and the P workgroups' statistics (argmax,
+  // or drawn token) of every chain node.
+  constexpr bool kSegOn = CACHED;
   __shared__ int fk[kSegOn ? kMaxT : 1];
   __shared__ int s_seg[kSeg];
   __shared__ int s_seglen;
@@ -190,6 +189,7 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
   __shared__ float sred_f[kSegOn ? kSeg : 1][kAW];
   __shared__ double sred_d[kSegOn ? kSeg : 1][kAW];
   __shared__ int sred_i[kSegOn ? kSeg : 1][kAW];
+  __shared__ int seg_x[kSeg];
   __shared__ __align__(8) uint32_t xs[kMaxP][kSegOn ? kXW : 2];
   __shared__ int s_flag, s_to, s_first, s_last, s_x;
 
@@ -623,103 +623,6 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
       for (int w = 0; w < kAW; ++w)
         if (wf[w] > -INFINITY) sw += wd[w] * (double)__builtin_amdgcn_exp2f((wf[w] - mw) * c2);
   };
-  // Statistics of a first-child chain (cached rows, rejection sampling).  In
-  // the seeded trees the walk accepts a node's first child nine times in ten,
-  // so the chain from `start` (up to kSeg nodes: start, its first child, that
-  // child's first child, ...) is likely the path ahead.  Its rows are loaded
-  // together, every node's (max, mass) formed as the per-node pass would
-  // form it, and all of them exchanged at once; so is each node's
-  // first-child test scalars and draw uniform.  A node of the chain then
-  // needs no pass and no exchange for its statistics.
-  auto seg_build = [&](int start, bool start_row) {   // start_row: lc holds start's row
-    if (tid == 0) {
-      int n = start, len = 0;
-      for (;;) {
-        s_seg[len++] = n;
-        if (len == kSeg) break;
-        const int f = fk[n];
-        if (f >= T) break;
-        n = f;
-      }
-      s_seglen = len;
-    }
-    lds_sync();
-    const int len = s_seglen;
-    LT gl = LT(0);
-    float gq = 0.f, gu = 0.f, gud = 0.f;
-    if (mss && tid < len) {
-      const int n = s_seg[tid];
-      const int f = fk[n];
-      const int fn = f < T ? f : n;   // (a leaf reads its own values, unused)
-      const int x = s_tok[fn];
-      gl = row_of(n)[x];
-      gq = a.draft[((size_t)b * T + n) * V + x];
-      gu = a.unif[((size_t)b * T + fn) * 2 + 0];
-      gud = a.unif[((size_t)b * T + n) * 2 + 1];
-    }
-    uint4 sr[kSeg][kMaxCh];
-#pragma unroll
-    for (int j = 0; j < kSeg; ++j)
-      if (j < len) {
-        if (j == 0 && start_row) {
-#pragma unroll
-          for (int c = 0; c < kMaxCh; ++c) sr[0][c] = lc[c];
-        } else {
-          load_row(row_of(s_seg[j]), sr[j]);
-        }
-      }
-#pragma unroll
-    for (int j = 0; j < kSeg; ++j)
-      if (j < len) {
-        if constexpr (MODE == kGreedy) {
-          float bv;
-          int bi;
-          row_argmax(sr[j], bv, bi);
-          if (lane == 63) {
-            sred_f[j][wave] = bv;
-            sred_i[j][wave] = bi;
-          }
-        } else {
-          float mt;
-          double st;
-          row_stats(sr[j], mt, st);
-          if (lane == 63) {
-            sred_f[j][wave] = mt;
-            sred_d[j][wave] = st;
-          }
-        }
-      }
-    if (mss && tid < len) {
-      if constexpr (kBF) seg_l[tid] = bf16_to_f32(gl);
-      else seg_l[tid] = gl;
-      seg_q[tid] = gq;
-      seg_u[tid] = gu;
-      seg_ud[tid] = gud;
-    }
-    lds_sync();
-    uint32_t w = 0;
-    if (tid < 2 * len) {
-      const int j = tid >> 1;
-      if constexpr (MODE == kGreedy) {
-        // the workgroup's argmax, combined over its wavefronts in order
-        float bv = sred_f[j][0];
-        int bi = sred_i[j][0];
-        for (int w2 = 1; w2 < kAW; ++w2)
-          if (sred_f[j][w2] > bv || (sred_f[j][w2] == bv && sred_i[j][w2] < bi)) {
-            bv = sred_f[j][w2];
-            bi = sred_i[j][w2];
-          }
-        w = (tid & 1) ? (uint32_t)bi : __float_as_uint(bv);
-      } else {
-        float mw;
-        double sw;
-        wg_stats(sred_f[j], sred_d[j], mw, sw);
-        w = (tid & 1) ? __float_as_uint((float)sw) : __float_as_uint(mw);
-      }
-    }
-    exchange_words(2 * len, w);
-  };
-
   // Inverse-CDF draw: slices' masses in mass[0..P); threshold u * total.  The
   // workgroup owning the crossing finds it in its slice, four chunks at a
   // time: each thread sums its 8 weights `wf(c, w8)` of each chunk, a scan over
@@ -837,6 +740,155 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
     }
     lds_sync();
     return s_last;
+  };
+
+  // Slice j's (max, mass) sits in lane j % 16 of every wavefront (mj, sj);
+  // the global max m and the masses' sum z0 are formed by butterflies over
+  // those 16 lanes, which leave the same value in every lane (each step adds
+  // a pair of values in either order).  mass_j: this lane's slice's mass
+  // relative to m.
+  auto slice_bfly = [&](float mj, float sj, float& m, double& z0, double& mass_j) {
+    auto mvf = [](auto c, auto r, float old, float x) { return dpp_f<decltype(c)::value, decltype(r)::value>(old, x); };
+    auto mvd = [](auto c, auto r, double old, double x) { return dpp_d<decltype(c)::value, decltype(r)::value>(old, x); };
+    m = dpp_reduce<false>(mj, -INFINITY, mvf, [](float x, float y) { return fmaxf(x, y); });
+    mass_j = mj == -INFINITY ? 0.0 : (double)sj * (double)__builtin_amdgcn_exp2f((mj - m) * c2);
+    z0 = dpp_reduce<false>(mass_j, 0.0, mvd, [](double x, double y) { return x + y; });
+  };
+  // Statistics of a first-child chain (cached rows).  In the seeded trees
+  // the walk accepts a node's first child nine times in ten, so the chain
+  // from `start` (up to kSeg nodes: start, its first child, that child's
+  // first child, ...) is likely the path ahead.  Its rows are loaded
+  // together, every node's (max, mass) -- or argmax -- formed as the
+  // per-node pass would form it, and all of them exchanged at once; so is
+  // each node's first-child test scalars and draw uniform.  With target
+  // sampling every chain node's draw is then made from its row (the draw
+  // depends only on the node) and the drawn tokens exchanged in a second
+  // round.  A node of the chain needs no pass and no exchange of its own.
+  auto seg_build = [&](int start, bool start_row) {   // start_row: lc holds start's row
+    if (tid == 0) {
+      int n = start, len = 0;
+      for (;;) {
+        s_seg[len++] = n;
+        if (len == kSeg) break;
+        const int f = fk[n];
+        if (f >= T) break;
+        n = f;
+      }
+      s_seglen = len;
+    }
+    lds_sync();
+    const int len = s_seglen;
+    LT gl = LT(0);
+    float gq = 0.f, gu = 0.f, gud = 0.f;
+    if (tid < len) {
+      const int n = s_seg[tid];
+      if constexpr (mss) {
+        const int f = fk[n];
+        const int fn = f < T ? f : n;   // (a leaf reads its own values, unused)
+        const int x = s_tok[fn];
+        gl = row_of(n)[x];
+        gq = a.draft[((size_t)b * T + n) * V + x];
+        gu = a.unif[((size_t)b * T + fn) * 2 + 0];
+      }
+      if constexpr (MODE != kGreedy) gud = a.unif[((size_t)b * T + n) * 2 + 1];
+    }
+    uint4 sr[kSeg][kMaxCh];
+#pragma unroll
+    for (int j = 0; j < kSeg; ++j)
+      if (j < len) {
+        if (j == 0 && start_row) {
+#pragma unroll
+          for (int c = 0; c < kMaxCh; ++c) sr[0][c] = lc[c];
+        } else {
+          load_row(row_of(s_seg[j]), sr[j]);
+        }
+      }
+#pragma unroll
+    for (int j = 0; j < kSeg; ++j)
+      if (j < len) {
+        if constexpr (MODE == kGreedy) {
+          float bv;
+          int bi;
+          row_argmax(sr[j], bv, bi);
+          if (lane == 63) {
+            sred_f[j][wave] = bv;
+            sred_i[j][wave] = bi;
+          }
+        } else {
+          float mt;
+          double st;
+          row_stats(sr[j], mt, st);
+          if (lane == 63) {
+            sred_f[j][wave] = mt;
+            sred_d[j][wave] = st;
+          }
+        }
+      }
+    if (tid < len) {
+      if constexpr (mss) {
+        seg_l[tid] = bf16_to_f32(gl);
+        seg_q[tid] = gq;
+        seg_u[tid] = gu;
+      }
+      if constexpr (MODE != kGreedy) seg_ud[tid] = gud;
+    }
+    lds_sync();
+    uint32_t w = 0;
+    if (tid < 2 * len) {
+      const int j = tid >> 1;
+      if constexpr (MODE == kGreedy) {
+        // the workgroup's argmax, combined over its wavefronts in order
+        float bv = sred_f[j][0];
+        int bi = sred_i[j][0];
+        for (int w2 = 1; w2 < kAW; ++w2)
+          if (sred_f[j][w2] > bv || (sred_f[j][w2] == bv && sred_i[j][w2] < bi)) {
+            bv = sred_f[j][w2];
+            bi = sred_i[j][w2];
+          }
+        w = (tid & 1) ? (uint32_t)bi : __float_as_uint(bv);
+      } else {
+        float mw;
+        double sw;
+        wg_stats(sred_f[j], sred_d[j], mw, sw);
+        w = (tid & 1) ? __float_as_uint((float)sw) : __float_as_uint(mw);
+      }
+    }
+    exchange_words(2 * len, w);
+    if constexpr (MODE == kTarget) {
+      // each chain node's draw, as the per-node step would make it; only the
+      // workgroup holding the crossing point gets the token
+#pragma unroll
+      for (int j = 0; j < kSeg; ++j)
+        if (j < len) {
+          float m;
+          double z0, mass_j;
+          {
+            const int jj = lane & 15;
+            const float mj = jj < P ? __uint_as_float(xs[jj][2 * j + 0]) : -INFINITY;
+            const float sj = jj < P ? __uint_as_float(xs[jj][2 * j + 1]) : 0.f;
+            slice_bfly(mj, sj, m, z0, mass_j);
+          }
+          if (tid < P) mass[tid] = mass_j;
+          auto ewj = [&](int c, double* w8) {
+            if (y0_of(c) >= sl1) {
+#pragma unroll
+              for (int e = 0; e < 8; ++e) w8[e] = 0.0;
+              return;
+            }
+            const uint4 u = sr[j][c];
+            const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const float v = bf16_to_f32((bf16_bits)(wd[e >> 1] >> (16 * (e & 1))));
+              w8[e] = v == -INFINITY ? 0.0 : (double)__builtin_amdgcn_exp2f((v - m) * c2);
+            }
+          };
+          const int x = draw(seg_ud[j], ewj);
+          if (tid == 0) seg_x[j] = x;
+        }
+      lds_sync();
+      exchange_words(len, tid < len ? (uint32_t)(seg_x[tid] + 1) : 0u);   // xs[j][k]: token + 1 of chain node k from slice j, or 0
+    }
   };
 
   int cur = 0, plen = 1;
@@ -991,6 +1043,26 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
         if (wg == 0 && tid == 0) a.bonus[b] = gi;
         stop = true;
       }
+    } else if constexpr (kSegOn && !mss) {
+      // target sampling on a chain: the node's token was drawn with its chain
+      int xd = -1;
+#pragma unroll
+      for (int j = 0; j < kMaxP; ++j)
+        if (j < P) xd = max(xd, (int)xs[j][seg_i] - 1);
+      if (nk > 0 && s_tok[fk[cur]] == xd) {
+        nxt = 0;
+      } else if (nk > 0) {
+        nk = gather_children(cur);
+        for (int c = 1; c < nk; ++c)
+          if (s_tok[kids[c]] == xd) {
+            nxt = c;
+            break;
+          }
+      }
+      if (nxt < 0) {
+        if (wg == 0 && tid == 0) a.bonus[b] = xd;
+        stop = true;
+      }
     } else {
       // statistics of this slice: its max and the mass relative to it,
       // merged across lanes and waves (in lane 63 of each wave); a chain
@@ -1054,10 +1126,8 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
       exchange(__float_as_uint(mw), __float_as_uint((float)sw));
       if (nk > 0) load_row(row_of(kids[0]), pfc);
       }
-      // Slice j's (max, mass) sits in lane j % 16 of every wavefront; the
-      // global max and the masses' sum are formed by butterflies over those
-      // 16 lanes, which leave the same value in every lane (each step adds a
-      // pair of values in either order).  mass[] is read only by the draw.
+      // the P slices' (max, mass) combined (slice_bfly); mass[] is read only
+      // by the draw
       float m;
       double z0;
       {
@@ -1072,11 +1142,8 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
             sj = xf(j, 1);
           }
         }
-        auto mvf = [](auto c, auto r, float old, float x) { return dpp_f<decltype(c)::value, decltype(r)::value>(old, x); };
-        auto mvd = [](auto c, auto r, double old, double x) { return dpp_d<decltype(c)::value, decltype(r)::value>(old, x); };
-        m = dpp_reduce<false>(mj, -INFINITY, mvf, [](float x, float y) { return fmaxf(x, y); });
-        const double mass_j = mj == -INFINITY ? 0.0 : (double)sj * (double)__builtin_amdgcn_exp2f((mj - m) * c2);
-        z0 = dpp_reduce<false>(mass_j, 0.0, mvd, [](double x, double y) { return x + y; });
+        double mass_j;
+        slice_bfly(mj, sj, m, z0, mass_j);
         if (tid < P) mass[tid] = mass_j;
       }
       auto ew8 = [&](int c, double* w8) {
