@@ -868,6 +868,10 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
             const float sj = jj < P ? __uint_as_float(xs[jj][2 * j + 1]) : 0.f;
             slice_bfly(mj, sj, m, z0, mass_j);
           }
+          // (a workgroup not holding the last crossing returns from the draw
+          // right after reading mass[]: every wavefront is past those reads
+          // before mass[] changes)
+          lds_sync();
           if (tid < P) mass[tid] = mass_j;
           auto ewj = [&](int c, double* w8) {
             if (y0_of(c) >= sl1) {
