@@ -22,9 +22,10 @@ steps, the attention call against the HBM or MFMA roofline (algorithmic
 bytes or FLOPs per call / event-timed call duration), and the CPU oracle
 timed on a bounded sample of the same workload.  The attention call of every
 10th timed step (--event-every; more often when fewer than 200 steps are
-timed, so that at least 20 calls are) is bracketed by HIP events: an event
-record leaves the GPU idle for a few microseconds, so bracketing every call
-would add that idle time to every step.  Before the warmup steps, untimed
+timed, so that at least 20 calls are) is timed with HIP events that its
+first kernel records at its start and its last kernel at its end
+(sd_attn_timing_events, hipExtLaunchKernelGGL): the kernels' own device time,
+without the idle gap of event markers recorded on the stream around the call.  Before the warmup steps, untimed
 steps run for --settle-ms so the GPU has left its idle clocks.
 
 `secondary` lists the other workloads, each with its attention call against
@@ -62,8 +63,8 @@ def parse():
                          "GPU leaves its idle clocks (a step is ~0.15 ms; without this the "
                          "first tens of milliseconds of steps run up to 10%% slower)")
     ap.add_argument("--event-every", type=int, default=10,
-                    help="bracket the attention call of every N-th timed step with HIP events "
-                         "(each event record adds a few microseconds of idle GPU time to its step)")
+                    help="time the attention call of every N-th timed step with HIP events that "
+                         "its kernels record at their start and end")
     ap.add_argument("--kv-copies", type=int, default=2,
                     help="K/V page copies, used by consecutive steps in turn")
     ap.add_argument("--workload", default="llama3_8b_tree64")
@@ -338,10 +339,10 @@ class HipEvent:
             cls._rt = rt
         return cls._rt
 
-    def __init__(self):
+    def __init__(self, flags=0x20000000):
         import ctypes
         self.h = ctypes.c_void_p()
-        assert self.runtime().hipEventCreateWithFlags(ctypes.byref(self.h), 0x20000000) == 0
+        assert self.runtime().hipEventCreateWithFlags(ctypes.byref(self.h), flags) == 0
 
     def record(self):
         import torch
@@ -437,10 +438,9 @@ class Workload:
         self.n_steps += 1
         self.select(ctx)
         if ev is not None:
-            ev[0].record()
+            # the attention kernels themselves record the two events
+            tva.attn_timing_events(ev[0].h.value, ev[1].h.value)
         self.attention(ctx)
-        if ev is not None:
-            ev[1].record()
         # the acceptance walk and the commit of its paths, in one launch
         tva.accept_commit(self.logits, self.draft, self.parent, self.token, self.unif, self.tau,
                           self.k, self.v, self.table, ctx,
@@ -826,7 +826,7 @@ def main():
     torch.cuda.synchronize()
     # at least 20 bracketed calls (all of them for fewer than 20 steps)
     every = max(1, min(args.event_every, args.steps // 20))
-    evs = {k: (HipEvent(), HipEvent()) for k in range(0, args.steps, every)}
+    evs = {k: (HipEvent(0), HipEvent(0)) for k in range(0, args.steps, every)}
     # each timed step gets its own copy of the context lengths (its commit
     # advances them), so no restore runs inside the timed region
     ctxs = [w.ctx0.clone() for _ in range(args.steps)]

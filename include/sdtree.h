@@ -377,6 +377,18 @@ size_t sd_workspace_bytes(int32_t call_id, const void* shape, int32_t extra);
  * them, and returns SD_DEVICE_DATA_ERROR if any was set. */
 sd_status sd_device_status(void* ws, void* stream, uint32_t* bits);
 
+/* Kernel timing for profilers and benchmarks (not part of the method): the
+ * next sd_tree_verify_attn call made on this host thread launches its first
+ * kernel so that it records `start_event` when that kernel begins, and its
+ * last kernel so that it records `stop_event` when that kernel ends
+ * (hipExtLaunchKernelGGL).  hipEventElapsedTime(start, stop) is then the
+ * call's own device time, without the idle gap that an event recorded on the
+ * stream around the call adds.  Both are hipEvent_t handles created with
+ * timing enabled (either may be NULL: not recorded).  The setting is used by
+ * that one call, also when it fails, and then cleared; NULL, NULL clears it.
+ * Returns SD_OK. */
+sd_status sd_attn_timing_events(void* start_event, void* stop_event);
+
 /* Static description of a status code. */
 const char* sd_status_str(int32_t code);
 

@@ -7,7 +7,7 @@ verification -- as hand-written HIP kernels behind a small C ABI
 (csrc/), the in-tree build (build.py) and a ctypes binding (_lib.py).
 """
 from ._lib import (  # noqa: F401
-    SdError, accept, accept_commit, accept_commit_noalloc, block_sums, block_sums_append, device_status, kv_commit, lib,
+    SdError, accept, accept_commit, attn_timing_events, accept_commit_noalloc, block_sums, block_sums_append, device_status, kv_commit, lib,
     topk_blocks, topk_blocks_cached, topk_blocks_shared, tree_build, tree_expand, tree_verify_attn,
     workspace_bytes,
 )

@@ -103,6 +103,7 @@ def lib():
         "sd_tree_build": [ctypes.POINTER(SdBuildShape), _P, ctypes.c_float, i32, _P, _P, _P,
                           ctypes.POINTER(ctypes.c_int32), _P, sz, _P],
         "sd_device_status": [_P, _P, ctypes.POINTER(ctypes.c_uint32)],
+        "sd_attn_timing_events": [_P, _P],
         "sd_workspace_bytes": [i32, _P, i32],
         "sd_status_str": [i32],
     }
@@ -179,6 +180,13 @@ _WS = Workspace()
 
 def workspace_bytes(call, shape, extra=0):
     return lib().sd_workspace_bytes(call, ctypes.byref(shape), extra)
+
+
+def attn_timing_events(start_event, stop_event):
+    """The next tree_verify_attn call on this thread records the two hipEvent_t
+    handles (ints; 0 = none) at its first kernel's start and its last kernel's
+    end."""
+    _check("sd_attn_timing_events", lib().sd_attn_timing_events(start_event or None, stop_event or None))
 
 
 def tree_verify_attn(q, k_pages, v_pages, block_table, ctx_lens, tree_parent, out=None,

@@ -15,6 +15,8 @@
 //   attn_combine_kernel merges split partials into the normalised output
 #include <type_traits>
 
+#include <hip/hip_ext.h>
+
 #include "common.h"
 
 namespace sdtree {
@@ -1141,71 +1143,82 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(const float* __restri
 }
 
 // ---------------------------------------------------------------------------
-// Host-side launchers.
+// Host-side launchers.  A kernel given a start or stop event is launched with
+// hipExtLaunchKernelGGL, which records the events at the kernel's own start
+// and end.
+
+template <typename F, typename... Args>
+static void launch_ev(F fn, dim3 grid, dim3 block, size_t lds, hipStream_t st, hipEvent_t e0,
+                      hipEvent_t e1, Args... args) {
+  if (e0 || e1) hipExtLaunchKernelGGL(fn, grid, block, (uint32_t)lds, st, e0, e1, 0u, args...);
+  else hipLaunchKernelGGL(fn, grid, block, lds, st, args...);
+}
 
 hipError_t launch_anc_mask(const int32_t* parent, int T, int W64, int n_trees, uint64_t* anc,
-                           uint32_t* status, hipStream_t st) {
+                           uint32_t* status, hipStream_t st, hipEvent_t start) {
   dim3 grid((T + 255) / 256, n_trees);
-  hipLaunchKernelGGL(anc_mask_kernel, grid, dim3(256), 0, st, parent, T, W64, anc, status);
+  launch_ev(anc_mask_kernel, grid, dim3(256), 0, st, start, nullptr, parent, T, W64, anc, status);
   return hipGetLastError();
 }
 
 template <int D>
-static hipError_t launch_valu_d(const AttnArgs& a, bool f32, hipStream_t st) {
+static hipError_t launch_valu_d(const AttnArgs& a, bool f32, hipStream_t st, CallEvents ev) {
   const long long nrows = (long long)a.B * a.T * a.Hq;
   dim3 grid((unsigned)nrows);
   if (f32)
-    hipLaunchKernelGGL((attn_valu_kernel<float, D>), grid, dim3(256), 0, st, a);
+    launch_ev(attn_valu_kernel<float, D>, grid, dim3(256), 0, st, ev.start, ev.stop, a);
   else
-    hipLaunchKernelGGL((attn_valu_kernel<bf16_bits, D>), grid, dim3(256), 0, st, a);
+    launch_ev(attn_valu_kernel<bf16_bits, D>, grid, dim3(256), 0, st, ev.start, ev.stop, a);
   return hipGetLastError();
 }
 
-hipError_t launch_attn_valu(const AttnArgs& a, bool f32, hipStream_t st) {
-  return a.D == 64 ? launch_valu_d<64>(a, f32, st) : launch_valu_d<128>(a, f32, st);
+hipError_t launch_attn_valu(const AttnArgs& a, bool f32, hipStream_t st, CallEvents ev) {
+  return a.D == 64 ? launch_valu_d<64>(a, f32, st, ev) : launch_valu_d<128>(a, f32, st, ev);
 }
 
 template <int D, int QW, int WQ, int WK, int KW, int S>
-static hipError_t launch_mfma_cfg(const AttnArgs& a, size_t lds, hipStream_t st) {
+static hipError_t launch_mfma_cfg(const AttnArgs& a, size_t lds, hipStream_t st, CallEvents ev) {
   auto fn = attn_mfma_kernel<D, QW, WQ, WK, KW, S>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   const unsigned nwg = (unsigned)a.B * a.Hkv * a.n_qtiles * a.n_splits;
-  hipLaunchKernelGGL(fn, dim3(nwg), dim3(WQ * WK * 64), lds, st, a);
+  launch_ev(fn, dim3(nwg), dim3(WQ * WK * 64), lds, st, ev.start, ev.stop, a);
   return hipGetLastError();
 }
 
 template <int D>
-static hipError_t launch_mfma_d(const AttnArgs& a, const AttnPlan& p, hipStream_t st) {
+static hipError_t launch_mfma_d(const AttnArgs& a, const AttnPlan& p, hipStream_t st, CallEvents ev) {
   if constexpr (D == 128) {
     if (p.WQ == 8) {
-      if (p.stages == 8) return launch_mfma_cfg<D, 32, 8, 1, 32, 8>(a, p.lds_bytes, st);
-      return launch_mfma_cfg<D, 32, 8, 1, 32, 4>(a, p.lds_bytes, st);
+      if (p.stages == 8) return launch_mfma_cfg<D, 32, 8, 1, 32, 8>(a, p.lds_bytes, st, ev);
+      return launch_mfma_cfg<D, 32, 8, 1, 32, 4>(a, p.lds_bytes, st, ev);
     }
   }
-  if (p.WQ == 1) return launch_mfma_cfg<D, 32, 1, 4, 32, 2>(a, p.lds_bytes, st);
+  if (p.WQ == 1) return launch_mfma_cfg<D, 32, 1, 4, 32, 2>(a, p.lds_bytes, st, ev);
   if (p.WQ == 2) {
-    if (p.stages == 4) return launch_mfma_cfg<D, 32, 2, 2, 32, 4>(a, p.lds_bytes, st);
-    return launch_mfma_cfg<D, 32, 2, 2, 32, 2>(a, p.lds_bytes, st);
+    if (p.stages == 4) return launch_mfma_cfg<D, 32, 2, 2, 32, 4>(a, p.lds_bytes, st, ev);
+    return launch_mfma_cfg<D, 32, 2, 2, 32, 2>(a, p.lds_bytes, st, ev);
   }
-  if (p.stages == 4) return launch_mfma_cfg<D, 32, 4, 2, 32, 4>(a, p.lds_bytes, st);
-  if (p.stages == 3) return launch_mfma_cfg<D, 32, 4, 2, 32, 3>(a, p.lds_bytes, st);
-  return launch_mfma_cfg<D, 32, 4, 2, 32, 2>(a, p.lds_bytes, st);
+  if (p.stages == 4) return launch_mfma_cfg<D, 32, 4, 2, 32, 4>(a, p.lds_bytes, st, ev);
+  if (p.stages == 3) return launch_mfma_cfg<D, 32, 4, 2, 32, 3>(a, p.lds_bytes, st, ev);
+  return launch_mfma_cfg<D, 32, 4, 2, 32, 2>(a, p.lds_bytes, st, ev);
 }
 
-hipError_t launch_attn_mfma(const AttnArgs& a, const AttnPlan& p, hipStream_t st) {
-  hipError_t e = a.D == 64 ? launch_mfma_d<64>(a, p, st) : launch_mfma_d<128>(a, p, st);
+hipError_t launch_attn_mfma(const AttnArgs& a, const AttnPlan& p, hipStream_t st, CallEvents ev) {
+  // with a split context the merge kernel is the call's last
+  const CallEvents main_ev{ev.start, a.n_splits == 1 ? ev.stop : nullptr};
+  hipError_t e = a.D == 64 ? launch_mfma_d<64>(a, p, st, main_ev) : launch_mfma_d<128>(a, p, st, main_ev);
   if (e != hipSuccess || a.n_splits == 1) return e;
   const long long nrows = (long long)a.B * a.T * a.Hq;
   dim3 grid((unsigned)((nrows + 3) / 4));
   bf16_bits* out = reinterpret_cast<bf16_bits*>(a.out);
   if (a.D == 64)
-    hipLaunchKernelGGL(attn_combine_kernel<64>, grid, dim3(256), 0, st, a.part_o, a.part_ml, out, nrows,
-                       a.n_splits);
+    launch_ev(attn_combine_kernel<64>, grid, dim3(256), 0, st, nullptr, ev.stop, (const float*)a.part_o,
+              (const float*)a.part_ml, out, nrows, a.n_splits);
   else
-    hipLaunchKernelGGL(attn_combine_kernel<128>, grid, dim3(256), 0, st, a.part_o, a.part_ml, out, nrows,
-                       a.n_splits);
+    launch_ev(attn_combine_kernel<128>, grid, dim3(256), 0, st, nullptr, ev.stop, (const float*)a.part_o,
+              (const float*)a.part_ml, out, nrows, a.n_splits);
   return hipGetLastError();
 }
 

@@ -280,14 +280,20 @@ struct BuildArgs {
   uint32_t* status;
 };
 
+// Events a call's first kernel records at its start and its last kernel at
+// its end (either may be null).
+struct CallEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+
 // Launchers (one per kernel family).
 hipError_t launch_expand(const ExpandArgs& a, bool f32, hipStream_t st);
 hipError_t run_tree_build(const BuildArgs& a, const ExpandArgs& ex0, bool f32, hipStream_t st,
                           int* rounds);
 hipError_t launch_anc_mask(const int32_t* parent, int T, int W64, int n_trees, uint64_t* anc,
-                           uint32_t* status, hipStream_t st);
-hipError_t launch_attn_valu(const AttnArgs& a, bool f32, hipStream_t st);
-hipError_t launch_attn_mfma(const AttnArgs& a, const AttnPlan& p, hipStream_t st);
+                           uint32_t* status, hipStream_t st, hipEvent_t start = nullptr);
+hipError_t launch_attn_valu(const AttnArgs& a, bool f32, hipStream_t st, CallEvents ev = {});
+hipError_t launch_attn_mfma(const AttnArgs& a, const AttnPlan& p, hipStream_t st, CallEvents ev = {});
 hipError_t launch_accept(const AcceptArgs& a, hipStream_t st);
 // The acceptance walk with its exchange slots in the library's own device
 // array (no workspace argument): at most kNoAllocMaxSeqs sequences when a

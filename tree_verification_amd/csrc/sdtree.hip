@@ -280,11 +280,22 @@ size_t sd_workspace_bytes(int32_t call_id, const void* shape, int32_t extra) {
   return 0;
 }
 
+// Timing events for this host thread's next attention call.
+static thread_local CallEvents t_attn_events;
+
+sd_status sd_attn_timing_events(void* start_event, void* stop_event) {
+  t_attn_events.start = static_cast<hipEvent_t>(start_event);
+  t_attn_events.stop = static_cast<hipEvent_t>(stop_event);
+  return SD_OK;
+}
+
 sd_status sd_tree_verify_attn(const sd_shape* shape, const void* q, const void* k_pages,
                               const void* v_pages, const int32_t* block_table,
                               const int32_t* ctx_lens, const int32_t* tree_parent,
                               const int32_t* sel_blocks, int32_t k_sel, void* out, void* ws,
                               size_t ws_bytes, void* stream) {
+  const CallEvents ev = t_attn_events;
+  t_attn_events = CallEvents{};
   sd_status st = check_shape(shape);
   if (st != SD_OK) return st;
   if (!q || !k_pages || !v_pages || !block_table || !ctx_lens || !tree_parent || !out || !ws)
@@ -305,7 +316,7 @@ sd_status sd_tree_verify_attn(const sd_shape* shape, const void* q, const void* 
   if (p.variant == 0) {
     // the per-row kernel reads precomputed ancestor masks; the MFMA kernel
     // walks the tree itself
-    hipError_t e = launch_anc_mask(tree_parent, s.T, p.W64, p.T_tree, anc, status, hs);
+    hipError_t e = launch_anc_mask(tree_parent, s.T, p.W64, p.T_tree, anc, status, hs, ev.start);
     if (e != hipSuccess) return SD_HIP_ERROR;
   }
 
@@ -326,8 +337,8 @@ sd_status sd_tree_verify_attn(const sd_shape* shape, const void* q, const void* 
   a.ct_max = p.ct_max; a.tt_max = p.tt_max;
   a.anc_lds_words = p.anc_lds_words;
   a.zeros = w + kWsZeros;
-  if (p.variant == 0) return hip_status(launch_attn_valu(a, s.dtype == SD_F32, hs));
-  return hip_status(launch_attn_mfma(a, p, hs));
+  if (p.variant == 0) return hip_status(launch_attn_valu(a, s.dtype == SD_F32, hs, CallEvents{nullptr, ev.stop}));
+  return hip_status(launch_attn_mfma(a, p, hs, ev));
 }
 
 // Checks the arguments of an acceptance call and fills its kernel arguments
