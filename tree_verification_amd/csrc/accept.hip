@@ -280,13 +280,28 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
   }
   // The tree (kept in LDS) must be topologically ordered with valid tokens.
   int bad = 0;
-  for (int n = tid; n < T; n += kAT) {
-    const int p = n == tid ? p_first : tpar[n];
-    const int t = n == tid ? t_first : ttok[n];
+  auto check_node = [&](int n, int p, int t) {
     if (n == 0 ? p != -1 : (p < 0 || p >= n)) bad |= SD_ERR_PARENT;
     if (t < 0 || t >= V) bad |= SD_ERR_TOKEN;
     s_par[n] = p;
     s_tok[n] = t;
+  };
+  if (tid < T) check_node(tid, p_first, t_first);
+  // the rest of a larger tree, four nodes per thread with their loads in
+  // flight together (a plain loop would wait for each node's loads in turn)
+  for (int n0 = kAT; n0 < T; n0 += 4 * kAT) {
+    int pv[4], tv[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int n = n0 + u * kAT + tid;
+      pv[u] = n < T ? tpar[n] : 0;
+      tv[u] = n < T ? ttok[n] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int n = n0 + u * kAT + tid;
+      if (n < T) check_node(n, pv[u], tv[u]);
+    }
   }
   if (tid == 0) {
     s_flag = 0;

@@ -334,7 +334,22 @@ __global__ void __launch_bounds__(WQ * WK * 64) attn_mfma_kernel(AttnArgs a) {
   };
   if (tid < 128) tflag[tid] = 0;
   if (tid == 0) s_err = 0;
-  for (int j = tid; j <= i_hi; j += NT) s_par[j] = a.parent[(size_t)bt * T + j];
+  // (loads batched so that a thread's loads are in flight together: a plain
+  // loop waits for each load before the next iteration's)
+  constexpr int LB = 4;
+  for (int j0 = 0; j0 <= i_hi; j0 += LB * NT) {
+    int pv[LB];
+#pragma unroll
+    for (int u = 0; u < LB; ++u) {
+      const int j = j0 + u * NT + tid;
+      pv[u] = j <= i_hi ? a.parent[(size_t)bt * T + j] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < LB; ++u) {
+      const int j = j0 + u * NT + tid;
+      if (j <= i_hi) s_par[j] = pv[u];
+    }
+  }
   for (int idx = tid; idx < nn * a.W64; idx += NT) ancL[idx] = 0ull;
   __syncthreads();
   int err = 0;
@@ -374,18 +389,38 @@ __global__ void __launch_bounds__(WQ * WK * 64) attn_mfma_kernel(AttnArgs a) {
     for (int w = tid; w < ROWS * UW; w += NT) rowbits[w] = 0;
     __syncthreads();
     const int nsel = max(r_hi - row0, 0) * a.ksel;
-    if (cap_ok) {
-      for (int idx = tid; idx < nsel; idx += NT) {
-        const int r = row0 + idx / a.ksel, e = idx % a.ksel;
-        const int i = r / G, h = g * G + r % G;
-        const int32_t* sr = a.sel + (((size_t)b * T + i) * a.Hq + h) * a.ksel;
-        const int n = sr[e];
-        if (n < 0) continue;
-        if (n >= nblk_ctx || (e > 0 && sr[e - 1] >= n)) {
-          err |= SD_ERR_SELECTION;
-          continue;
+    // Selection entries idx = base + u * NT + tid (u < LB) of this
+    // workgroup's rows: the entry n[u] and its row predecessor np[u] (-1 for
+    // a row's first entry), all loads in flight together.
+    auto sel_batch = [&](int base, int (&n)[LB], int (&np)[LB]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int u = 0; u < LB; ++u) {
+        const int idx = base + u * NT + tid;
+        n[u] = -1;
+        np[u] = -1;
+        if (idx < nsel) {
+          const int rl = idx / a.ksel, e = idx - rl * a.ksel;
+          const int r = row0 + rl;
+          const int i = r / G, h = g * G + r % G;
+          const int32_t* sr = a.sel + (((size_t)b * T + i) * a.Hq + h) * a.ksel;
+          n[u] = sr[e];
+          if (e > 0) np[u] = sr[e - 1];
         }
-        atomicOr(&ubits[n >> 5], 1u << (n & 31));
+      }
+    };
+    if (cap_ok) {
+      for (int base = 0; base < nsel; base += LB * NT) {
+        int n[LB], np[LB];
+        sel_batch(base, n, np);
+#pragma unroll
+        for (int u = 0; u < LB; ++u) {
+          if (n[u] < 0) continue;
+          if (n[u] >= nblk_ctx || np[u] >= n[u]) {
+            err |= SD_ERR_SELECTION;
+            continue;
+          }
+          atomicOr(&ubits[n[u] >> 5], 1u << (n[u] & 31));
+        }
       }
     }
     __syncthreads();
@@ -420,24 +455,35 @@ __global__ void __launch_bounds__(WQ * WK * 64) attn_mfma_kernel(AttnArgs a) {
     }
     __syncthreads();
     // physical ids of the union's blocks, all loads in flight together
-    for (int o = tid; o < nU; o += NT) {
-      int phys = table[U[o]];
-      if (phys < 0 || phys >= a.num_blocks) {
-        err |= SD_ERR_BLOCK;
-        phys = 0;
+    for (int o0 = 0; o0 < nU; o0 += LB * NT) {
+      int phys[LB];
+#pragma unroll
+      for (int u = 0; u < LB; ++u) {
+        const int o = o0 + u * NT + tid;
+        phys[u] = o < nU ? table[U[o]] : 0;
       }
-      Uphys[o] = phys;
+#pragma unroll
+      for (int u = 0; u < LB; ++u) {
+        const int o = o0 + u * NT + tid;
+        if (o >= nU) continue;
+        if (phys[u] < 0 || phys[u] >= a.num_blocks) {
+          err |= SD_ERR_BLOCK;
+          phys[u] = 0;
+        }
+        Uphys[o] = phys[u];
+      }
     }
     if (cap_ok) {
-      for (int idx = tid; idx < nsel; idx += NT) {
-        const int rl = idx / a.ksel, e = idx % a.ksel;
-        const int r = row0 + rl;
-        const int i = r / G, h = g * G + r % G;
-        const int32_t* sr = a.sel + (((size_t)b * T + i) * a.Hq + h) * a.ksel;
-        const int n = sr[e];
-        if (n < 0 || n >= nblk_ctx || (e > 0 && sr[e - 1] >= n)) continue;
-        const int u = upre[n >> 5] + __popc(ubits[n >> 5] & ((1u << (n & 31)) - 1u));
-        atomicOr(&rowbits[rl * UW + (u >> 5)], 1u << (u & 31));
+      for (int base = 0; base < nsel; base += LB * NT) {
+        int n[LB], np[LB];
+        sel_batch(base, n, np);
+#pragma unroll
+        for (int u = 0; u < LB; ++u) {
+          if (n[u] < 0 || n[u] >= nblk_ctx || np[u] >= n[u]) continue;
+          const int rl = (base + u * NT + tid) / a.ksel;
+          const int uu = upre[n[u] >> 5] + __popc(ubits[n[u] >> 5] & ((1u << (n[u] & 31)) - 1u));
+          atomicOr(&rowbits[rl * UW + (uu >> 5)], 1u << (uu & 31));
+        }
       }
     }
   }
