@@ -29,8 +29,10 @@ without the idle gap of event markers recorded on the stream around the call.  B
 steps run for --settle-ms so the GPU has left its idle clocks.
 
 `secondary` lists the other workloads, each with its attention call against
-its roofline (the mean of 3 x 40 back-to-back calls alternating between two
-K/V copies), its whole step, and the selection call of the sparse modes; the
+its roofline (the call inside 40 whole steps, timed by its own kernels'
+events as above; the mean of back-to-back calls alternating between two K/V
+copies is `attention_loop_us`), its whole step, and the selection call of
+the sparse modes; the
 2048-node tree also reports the MFMA FLOPs its kernel executes against the
 algorithmic ones.
 """
@@ -523,19 +525,45 @@ def step_loop_us(w, n=40):
     return e0.elapsed_time(e1) / n * 1e3
 
 
+def step_attention_us(w, n=40):
+    """Mean duration of the attention call inside n whole steps (each on its
+    own copy of the starting context lengths), timed with HIP events that
+    the call's own kernels record at their start and end, after 200 ms of
+    untimed steps."""
+    torch = w.torch
+    # untimed steps for 200 ms first: after the workload's set-up on the host
+    # the GPU is back at its idle clocks
+    t_end = time.perf_counter() + 0.2
+    while time.perf_counter() < t_end:
+        for _ in range(10):
+            w.step()
+        torch.cuda.synchronize()
+    ctxs = [w.ctx0.clone() for _ in range(n)]
+    evs = [(HipEvent(), HipEvent()) for _ in range(n)]
+    torch.cuda.synchronize()
+    for j in range(n):
+        w.step(evs[j], ctxs[j])
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
+
+
 def measure_workload(w, label, n_calls=40):
-    """One workload's attention against its roofline (n_calls back-to-back
-    calls alternating between the K/V copies), its whole step, and, for the
-    sparse modes, the selection call."""
+    """One workload's attention against its roofline (the call inside n_calls
+    whole steps, timed by its own kernels' events, as the headline workload's
+    is), the mean of back-to-back calls alternating between the K/V copies
+    (`attention_loop_us`), its whole step, and, for the sparse modes, the
+    selection call."""
     torch, cfg = w.torch, w.cfg
     sel = w.sel
+    t_us = step_attention_us(w, n=n_calls)
     calls = [bound_attention(w, sel, kv) for kv in range(len(w.kvs))]
-    t_us = loop_us(torch, calls, n=n_calls)
+    loop = loop_us(torch, calls, n=n_calls)
     sel_np = None if sel is None else sel.cpu().numpy()
     bytes_, flops = attention_cost(cfg, w.x, sel_np)
     roof = roofline_for(cfg, bytes_, flops, t_us * 1e-6)
     e = {"workload": cfg.name, "call": label, "attention_us": round(t_us, 2),
-         "timed_calls": 3 * n_calls, "bytes_per_call": int(bytes_), "flops_per_call": int(flops),
+         "timed_calls": n_calls, "attention_loop_us": round(loop, 2),
+         "bytes_per_call": int(bytes_), "flops_per_call": int(flops),
          "roofline": roof, "verified_tree_tokens_per_s": round(cfg.B * cfg.T / (t_us * 1e-6), 1)}
     if sel is not None:
         f = (lambda: w.tva.topk_blocks_shared(w.q, w.k, w.table, w.ctx, cfg.topk, sums=w.sums, sel=w.sel)) \
@@ -826,7 +854,7 @@ def main():
     torch.cuda.synchronize()
     # at least 20 bracketed calls (all of them for fewer than 20 steps)
     every = max(1, min(args.event_every, args.steps // 20))
-    evs = {k: (HipEvent(0), HipEvent(0)) for k in range(0, args.steps, every)}
+    evs = {k: (HipEvent(), HipEvent()) for k in range(0, args.steps, every)}
     # each timed step gets its own copy of the context lengths (its commit
     # advances them), so no restore runs inside the timed region
     ctxs = [w.ctx0.clone() for _ in range(args.steps)]
