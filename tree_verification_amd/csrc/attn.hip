@@ -14,6 +14,7 @@
 //                       softmax in registers, split context with partials
 //   attn_combine_kernel merges split partials into the normalised output
 #include <type_traits>
+#include <utility>
 
 #include <hip/hip_ext.h>
 
@@ -211,6 +212,16 @@ __global__ void __launch_bounds__(256) attn_valu_kernel(AttnArgs a) {
 // Reference-max slack of the online softmax, in log2 units: probabilities are
 // formed relative to a running max that may lag the true one by up to this.
 constexpr float kLazy = 8.0f;
+
+// Calls f(std::integral_constant<int, 0>) ... f(std::integral_constant<int, N - 1>).
+template <int N, typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl<N>(f, std::make_integer_sequence<int, N>{});
+}
 
 template <int D, int QW, int WQ, int WK, int KW, int S>
 __global__ void __launch_bounds__(WQ * WK * 64) attn_mfma_kernel(AttnArgs a) {
@@ -909,7 +920,15 @@ __global__ void __launch_bounds__(WQ * WK * 64) attn_mfma_kernel(AttnArgs a) {
     const int n_whole = nU - ((nU > 0 && U[nU - 1] == nblk_ctx - 1 && (ctx & bsm) != 0) ? 1 : 0);
     n_full = max(0, min(t_hi, (int)(((long long)n_whole << bsh) / NK)) - t_lo);
   }
-  const int n_tight = max(0, n_full - S) & ~1;
+  // (a multiple of TU, the tight loop's unroll.  With the 8-stage ring it is
+  // a whole ring turn, so every step's ring slots are constants and its
+  // fragment reads and DMA destinations fixed offsets from loop-invariant
+  // addresses; the other configurations unroll by a pair of score tiles and
+  // form the slots at run time, since the invariant addresses would not fit
+  // their registers.)
+  constexpr bool kConstSlots = S == 8;
+  constexpr int TU = kConstSlots ? S : 2;
+  const int n_tight = max(0, n_full - S) / TU * TU;
   // DMA sources of K(tk) and V(tk - 1) for a tight step, formed one step
   // ahead so the block-table reads are off the issue path.
   // The 64 / CK K rows one wave-operation copies lie in one page, so that
@@ -1036,10 +1055,24 @@ __global__ void __launch_bounds__(WQ * WK * 64) attn_mfma_kernel(AttnArgs a) {
     exp_tile(sc, pf);
     pv_regs(vf, pf);
   };
-  auto tight_step = [&](auto sp_tag, int k, STile& sc, STile& sn) __attribute__((always_inline)) {
+  // Step k = k0 + J of the tight loop (k0 a multiple of TU).
+  auto tight_step = [&](auto sp_tag, auto j_tag, int k, STile& sc, STile& sn) __attribute__((always_inline)) {
     sync_tiles(true);
-    tight_body(sp_tag, k, sc, sn, Kst + (k % S) * K_BYTES, Vst + ((k + S - 1) % S) * V_BYTES,
-               Kst + ((k + 1) % S) * K_BYTES, Vst + (k % S) * V_BYTES);
+    if constexpr (kConstSlots) {
+      constexpr int J = decltype(j_tag)::value;
+      tight_body(sp_tag, k, sc, sn, Kst + (J % S) * K_BYTES, Vst + ((J + S - 1) % S) * V_BYTES,
+                 Kst + ((J + 1) % S) * K_BYTES, Vst + (J % S) * V_BYTES);
+    } else {
+      tight_body(sp_tag, k, sc, sn, Kst + (k % S) * K_BYTES, Vst + ((k + S - 1) % S) * V_BYTES,
+                 Kst + ((k + 1) % S) * K_BYTES, Vst + (k % S) * V_BYTES);
+    }
+  };
+  auto tight_turn = [&](auto sp_tag, int k0) __attribute__((always_inline)) {
+    static_for<TU>([&](auto j_tag) __attribute__((always_inline)) {
+      constexpr int J = decltype(j_tag)::value;
+      if constexpr (J % 2 == 0) tight_step(sp_tag, j_tag, k0 + J, sa, sb);
+      else tight_step(sp_tag, j_tag, k0 + J, sb, sa);
+    });
   };
   auto general_body = [&](int k, STile& sc, STile& sn, unsigned char* __restrict__ kdst,
                           unsigned char* __restrict__ vdst, const unsigned char* __restrict__ krd,
@@ -1063,17 +1096,11 @@ __global__ void __launch_bounds__(WQ * WK * 64) attn_mfma_kernel(AttnArgs a) {
   if (!sparse) {
     const std::integral_constant<bool, false> dense_tag;
     if (n_tight > 0) tight_sources(dense_tag, t_lo + S, true);
-    for (; k < n_tight; k += 2) {
-      tight_step(dense_tag, k, sa, sb);
-      tight_step(dense_tag, k + 1, sb, sa);
-    }
+    for (; k < n_tight; k += TU) tight_turn(dense_tag, k);
   } else {
     const std::integral_constant<bool, true> sparse_tag;
     if (n_tight > 0) tight_sources(sparse_tag, t_lo + S, true);
-    for (; k < n_tight; k += 2) {
-      tight_step(sparse_tag, k, sa, sb);
-      tight_step(sparse_tag, k + 1, sb, sa);
-    }
+    for (; k < n_tight; k += TU) tight_turn(sparse_tag, k);
   }
   for (; k < nuse; k += 2) {
     general_step(k, sa, sb);
