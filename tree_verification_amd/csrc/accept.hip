@@ -391,7 +391,14 @@ __global__ void __launch_bounds__(kAT) accept_kernel(AcceptArgs a) {
     // the first (lowest-index) child of every node; T where there is none
     for (int n = tid; n < T; n += kAT) fk[n] = T;
     lds_sync();
-    for (int n = 1 + tid; n < T; n += kAT) atomicMin(&fk[s_par[n]], n);
+    // (fk only decreases, so a node that reads a smaller value already is not
+    // its parent's first child and skips the atomic: a node with many
+    // children, such as the root of a best-first tree, then takes one
+    // contended atomic per child of the first 256 nodes only)
+    for (int n = 1 + tid; n < T; n += kAT) {
+      const int p = s_par[n];
+      if (fk[p] > n) atomicMin(&fk[p], n);
+    }
     lds_sync();
   }
 
